@@ -1,0 +1,282 @@
+"""Plain fp64 CPU oracle of one Focus-dLLM sparse denoising step.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check of the entry module and
+the CPU-baseline leg of the benchmark may import or run this file.  It shares
+no code with the HIP library: the two meet only in the arrays drawn by
+``workloads.synth``.  It is deliberately slow and literal: each function is
+the definition written out in fp64 NumPy (plain Python where the definition is
+a selection), with no blocking, fusion or reordering beyond it.
+
+Citations.  "Summary" is the structured summary of the paper "Focus-dLLM:
+Accelerating Long-Context Diffusion LLM Inference via Confidence-Guided
+Context Focusing" at paper.rainbus.top/paper/2602.02159.  Its sections used
+here: "Prerequisites" (前置知识, with the sub-sections on dLLMs, attention
+sinks, the approximate KV cache and semi-autoregressive remasking), "Core
+method" (核心方法), "Method steps" (方法步骤详情, numbered (1)-(5)) and
+"Reproducibility" (复现评估).  "Abstract" is the paper's abstract at
+paperdance.org/p/2602.02159.
+
+Numeric model.  Inputs arrive as the exact fp64 upcast of the fp32 or bf16
+arrays the GPU receives.  Confidences are compared as the fp32 values given.
+Selections order by value, larger first, then by lower index.
+
+Readings (the pages leave these open; each is fixed here and listed with its
+reason in the design notes):
+  R1 window: exactly w positions [p - floor(w/2), p - floor(w/2) + w), clipped
+     to [0, L).
+  R2 attention: scale 1/sqrt(d), no mask (bidirectional), query head h reads
+     KV head floor(h * Hkv / Hq); inputs are already rotary-embedded.
+  R3 sinks: score_j = sum over heads and active queries of the normalised
+     attention probability of key j at layer l_dense; the n_sinks largest win.
+  R4 relevance: R_b = scale * sum over heads h and active queries i of
+     q_{h,i} . kbar_{g(h),b}; one block set per sequence and layer, shared by
+     all heads.
+  R5 key set: I_p = I_sink U (selected prompt blocks) U [P, L), each key once.
+     Without the generation region, attention with every block kept and a
+     window covering the sequence could not equal dense attention.
+
+Pins (tests marked "not gpu"): brute-force dominance and exhaustive subset
+checks for every selection, exact rational block means, closed-form and
+hand-worked attention fixtures, a library softmax/attention routine on small
+inputs, the sparse == dense reduction, and recovery of injected sinks.  The
+pages print no worked example, so no pin holds a value printed on a page.
+Parity of the readings R1, R3, R4, R5 against the authors' own code is
+unpinned: the pins fix the oracle to these readings, not the readings to the
+paper.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ selections
+
+def focus_count(n_t: int, rho: float) -> int:
+    """k = floor(rho * n(t)), in double precision.
+
+    Summary, "Core method": the indicator keeps the top-k masked positions,
+    k = floor(rho * n(t)), rho a preset expansion factor and n(t) the number
+    of tokens decoded at step t.
+    """
+    return int(math.floor(float(rho) * int(n_t)))
+
+
+def rank_select(values, candidates, count: int) -> np.ndarray:
+    """The `count` candidates with the largest value, lower index first on equal
+    values, returned in ascending index order.  Fewer candidates: all of them."""
+    ranked = sorted((int(i) for i in candidates), key=lambda i: (-float(values[i]), i))
+    return np.array(sorted(ranked[: max(count, 0)]), dtype=np.int64)
+
+
+def pcgi_focus(conf, mask, k: int) -> np.ndarray:
+    """I_focus: the k still-masked positions with the highest previous confidence.
+
+    Summary, "Core method" and "Method steps" (1): among all positions still
+    [MASK], take the top-k by the previous step's confidence c_{t-1}.
+    """
+    conf = np.asarray(conf, dtype=np.float32)
+    candidates = [i for i in range(len(mask)) if mask[i]]
+    return rank_select(conf, candidates, k)
+
+
+def window_active(focus, w: int, L: int) -> np.ndarray:
+    """I_active: the union of a window of w positions around each focus position.
+
+    Summary, "Method steps" (2): each candidate is widened to a local window of
+    size w.  Reading R1 places floor(w/2) positions before p.
+    """
+    half = w // 2
+    members = set()
+    for p in focus:
+        start = int(p) - half
+        for j in range(start, start + w):
+            if 0 <= j < L:
+                members.add(j)
+    return np.array(sorted(members), dtype=np.int64)
+
+
+# ------------------------------------------------------------------ attention
+
+def kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head h (grouped-query attention, reading R2)."""
+    return (h * Hkv) // Hq
+
+
+def attention(Q, K, V, scale: float):
+    """softmax(Q K^T * scale) V per head, with its log-sum-exp.
+
+    Q [Hq, n, d], K and V [Hkv, m, d] (fp64) -> O [Hq, n, d], lse [Hq, n].
+    No mask: dLLM attention is bidirectional (Summary, "Prerequisites", dLLMs).
+    An empty key set gives O = 0 and lse = -inf.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    Hq, n, d = Q.shape
+    Hkv, m = K.shape[0], K.shape[1]
+    O = np.zeros((Hq, n, V.shape[2]))
+    lse = np.full((Hq, n), -np.inf)
+    if m == 0 or n == 0:
+        return O, lse
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        S = (Q[h] @ K[g].T) * scale
+        top = S.max(axis=1, keepdims=True)
+        E = np.exp(S - top)
+        Z = E.sum(axis=1, keepdims=True)
+        O[h] = (E / Z) @ V[g]
+        lse[h] = (top + np.log(Z))[:, 0]
+    return O, lse
+
+
+def dense_attention(Q_rows, K, V, scale: float):
+    """Full attention of the given query rows over all L keys.
+
+    Summary, "Method steps": at a block-entry step the whole sequence attends
+    densely (use_sparse = False); in the other steps the first l_dense layers
+    run full attention (step (3)), here for the active query rows.
+    """
+    return attention(Q_rows, K, V, scale)
+
+
+# ------------------------------------------------------------------ sinks
+
+def sink_scores(Q_rows, K, lse, scale: float) -> np.ndarray:
+    """Attention mass each key receives at layer l_dense, summed over heads and rows.
+
+    Summary, "Prerequisites" (attention sinks draw a disproportionate share of
+    attention) and "Method steps" (3) (layer l_dense's attention distribution
+    identifies the sinks).  Reading R3: score_j = sum_h sum_i
+    exp(q_{h,i} . k_{g(h),j} * scale - lse_{h,i}).
+    """
+    Q_rows = np.asarray(Q_rows, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    Hq, Hkv = Q_rows.shape[0], K.shape[0]
+    score = np.zeros(K.shape[1])
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        S = (Q_rows[h] @ K[g].T) * scale
+        score += np.exp(S - np.asarray(lse[h], dtype=np.float64)[:, None]).sum(axis=0)
+    return score
+
+
+def sink_select(scores, n_sinks: int) -> np.ndarray:
+    """I_sink: the n_sinks keys with the largest score, ascending."""
+    return rank_select(scores, range(len(scores)), n_sinks)
+
+
+# ------------------------------------------------------------------ block pruning
+
+def block_means(K, P: int, bs: int) -> np.ndarray:
+    """Representative key of each prompt block: the mean of its keys.
+
+    Summary, "Method steps" (4): prompt tokens are split into contiguous
+    blocks, each represented by the mean of its keys.  K [Hkv, L, d] ->
+    kbar [Hkv, nb, d], nb = ceil(P / bs); a shorter last block is averaged over
+    its own keys.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    nb = -(-P // bs)
+    kbar = np.zeros((K.shape[0], nb, K.shape[2]))
+    for b in range(nb):
+        lo, hi = b * bs, min((b + 1) * bs, P)
+        kbar[:, b] = K[:, lo:hi].sum(axis=1) / (hi - lo)
+    return kbar
+
+
+def block_relevance(Q_rows, kbar, scale: float) -> np.ndarray:
+    """R_b between the active queries and each block's mean key (reading R4).
+
+    Summary, "Method steps" (4): relevance scores between the candidate queries
+    and every block are computed and the top-C blocks kept.
+    """
+    Q_rows = np.asarray(Q_rows, dtype=np.float64)
+    Hq, Hkv = Q_rows.shape[0], kbar.shape[0]
+    R = np.zeros(kbar.shape[1])
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        R += (Q_rows[h] @ kbar[g].T).sum(axis=0)
+    return R * scale
+
+
+def top_blocks(R, C: int) -> np.ndarray:
+    """The C blocks of highest relevance, ascending (all blocks when C >= nb)."""
+    return rank_select(R, range(len(R)), C)
+
+
+def key_set(sinks, blocks, bs: int, P: int, L: int) -> np.ndarray:
+    """I_p: sinks, the keys of the selected prompt blocks and the generation region.
+
+    Summary, "Method steps" (5): the sink set and the selected prompt blocks
+    form I_p; the generation region [P, L) is added by reading R5.  Each key
+    appears once, ascending.
+    """
+    keys = set(int(j) for j in sinks if j >= 0)
+    for b in blocks:
+        if b >= 0:
+            keys.update(range(int(b) * bs, min((int(b) + 1) * bs, P)))
+    keys.update(range(P, L))
+    return np.array(sorted(keys), dtype=np.int64)
+
+
+def sparse_attention(Q_rows, K, V, I_p, scale: float):
+    """Attention of the active queries over the key/value pairs in I_p only.
+
+    Summary, "Method steps" (5): sparse attention is computed only over the
+    key-value pairs of I_p.
+    """
+    I_p = np.asarray(I_p, dtype=np.int64)
+    return attention(Q_rows, np.asarray(K)[:, I_p], np.asarray(V)[:, I_p], scale)
+
+
+# ------------------------------------------------------------------ one step
+
+@dataclass
+class SparseStep:
+    focus: np.ndarray
+    active: np.ndarray
+    sinks: np.ndarray = None
+    sink_scores: np.ndarray = None
+    blocks: dict = field(default_factory=dict)     # layer -> selected blocks
+    relevance: dict = field(default_factory=dict)  # layer -> R
+    out: dict = field(default_factory=dict)        # layer -> O [Hq, n_active, d]
+    lse: dict = field(default_factory=dict)        # layer -> lse [Hq, n_active]
+
+
+def sparse_step(conf, mask, layer_inputs, *, layers: int, l_dense: int, n_t: int,
+                rho: float, w: int, P: int, bs: int, C: int, n_sinks: int,
+                scale: float, layer_subset=None) -> SparseStep:
+    """One non-block-entry denoising step of one sequence, in the pages' order.
+
+    Summary, "Method steps" (1)-(5): PCGI focus, window expansion, dense
+    layers 1..l_dense (sinks from layer l_dense), then per deeper layer block
+    means, top-C relevance, the key set and sparse attention.
+    `layer_inputs(l)` returns (Q [Hq, L, d], K [Hkv, L, d], V [Hkv, L, d]) of
+    layer l (0-based).  `layer_subset` limits which layers are evaluated; the
+    layer l_dense - 1 is always evaluated because the sinks come from it.
+    A one-layer step (layers == l_dense == 1) uses that layer both ways.
+    """
+    L = len(mask)
+    st = SparseStep(focus=pcgi_focus(conf, mask, focus_count(n_t, rho)), active=None)
+    st.active = window_active(st.focus, w, L)
+    wanted = set(range(layers)) if layer_subset is None else set(layer_subset)
+    wanted.add(l_dense - 1)
+    for l in sorted(wanted):
+        Q, K, V = layer_inputs(l)
+        Qa = np.asarray(Q, dtype=np.float64)[:, st.active]
+        if l < l_dense:
+            st.out[l], st.lse[l] = dense_attention(Qa, K, V, scale)
+            if l == l_dense - 1:
+                st.sink_scores = sink_scores(Qa, K, st.lse[l], scale)
+                st.sinks = sink_select(st.sink_scores, n_sinks)
+        if l >= l_dense or layers == l_dense == 1:
+            R = block_relevance(Qa, block_means(K, P, bs), scale)
+            st.relevance[l] = R
+            st.blocks[l] = top_blocks(R, C)
+            I_p = key_set(st.sinks, st.blocks[l], bs, P, L)
+            key = l if l >= l_dense else ("sparse", l)
+            st.out[key], st.lse[key] = sparse_attention(Qa, K, V, I_p, scale)
+    return st

@@ -1,0 +1,414 @@
+"""Pins of the fp64 oracle: checks against things other than the oracle itself.
+
+Every check reads the oracle through the module object ``O`` at call time, so
+a test can plant a mistake in the oracle (monkeypatching one of its functions)
+and confirm that some check fails.  Each check raises AssertionError on a
+mismatch.  Sources of truth, per check:
+  * hand-worked fixtures in tests/golden (values derived by hand from the
+    definitions on the Focus-dLLM summary page; the pages print no example);
+  * brute force: dominance of a selection over every non-selected candidate,
+    and exhaustive enumeration of all subsets on tiny inputs;
+  * exact rational arithmetic (fractions.Fraction) for block means and
+    relevance;
+  * a library routine: torch's scaled_dot_product_attention and scipy's
+    softmax / logsumexp in fp64 on the CPU;
+  * closed forms and invariants: total sink mass = heads x rows, constant V,
+    single key, key permutation, sparse == dense when nothing is pruned.
+"""
+from __future__ import annotations
+
+import dataclasses
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import scipy.special
+import torch
+
+from oracle import focus_oracle as O
+from workloads import configs, synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ------------------------------------------------------------------ selections
+
+def dominance_ok(values, candidates, chosen, k) -> bool:
+    """True iff `chosen` is the top-k of `candidates` (larger value, then lower index)."""
+    cand = set(int(c) for c in candidates)
+    ch = [int(c) for c in chosen]
+    if len(ch) != len(set(ch)) or list(ch) != sorted(ch):
+        return False
+    if not set(ch) <= cand or len(ch) != min(max(k, 0), len(cand)):
+        return False
+    for i in ch:
+        for j in cand - set(ch):
+            vi, vj = float(values[i]), float(values[j])
+            if not (vi > vj or (vi == vj and i < j)):
+                return False
+    return True
+
+
+def check_focus_count():
+    for n_t, rho, k in [(4, 2.0, 8), (8, 2.0, 16), (3, 2.5, 7), (3, 0.5, 1), (16, 4.0, 64),
+                        (0, 4.0, 0), (5, 0.1, 0), (10, 0.3, 3)]:
+        assert O.focus_count(n_t, rho) == k, (n_t, rho)
+
+
+def check_pcgi_dominance(trials=300, seed=0):
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        L = int(rng.integers(1, 48))
+        mask = rng.random(L) < rng.random()
+        conf = (rng.integers(0, 9, size=L) / 8.0).astype(np.float32)   # forced ties
+        k = int(rng.integers(0, L + 3))
+        got = O.pcgi_focus(conf, mask, k)
+        assert dominance_ok(conf, np.flatnonzero(mask), got, k), (L, k, got)
+
+
+def check_pcgi_exhaustive(trials=150, seed=1):
+    """On tiny inputs exactly one subset of the candidates dominates the rest."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        L = int(rng.integers(1, 10))
+        mask = rng.random(L) < 0.7
+        conf = (rng.integers(0, 4, size=L) / 4.0).astype(np.float32)
+        k = int(rng.integers(0, L + 2))
+        cand = np.flatnonzero(mask)
+        size = min(k, len(cand))
+        winners = [c for c in itertools.combinations(cand, size)
+                   if dominance_ok(conf, cand, c, k)]
+        assert len(winners) == 1
+        assert list(O.pcgi_focus(conf, mask, k)) == list(winners[0])
+
+
+def check_pcgi_window_fixture():
+    for case in _golden("pcgi_window_hand.json")["cases"]:
+        L = case["L"]
+        mask = np.zeros(L, dtype=bool)
+        mask[case["mask"]] = True
+        conf = np.zeros(L, dtype=np.float32)
+        for i, c in case["conf"].items():
+            conf[int(i)] = c
+        k = O.focus_count(case["n_t"], case["rho"])
+        assert k == case["k"], case["why"]
+        focus = O.pcgi_focus(conf, mask, k)
+        assert list(focus) == case["focus"], case["why"]
+        for w, expect in case["windows"].items():
+            assert list(O.window_active(focus, int(w), L)) == expect, (w, case["why"])
+
+
+def check_window_closed_forms(seed=2):
+    rng = np.random.default_rng(seed)
+    for _ in range(100):
+        L = int(rng.integers(4, 300))
+        focus = np.sort(rng.choice(L, size=int(rng.integers(1, min(L, 6) + 1)), replace=False))
+        assert list(O.window_active(focus, 2 * L + int(rng.integers(0, 3)), L)) == list(range(L))
+        assert list(O.window_active(focus, 1, L)) == list(focus)
+    for w in range(1, 12):
+        L = 50
+        left = O.window_active([0], w, L)
+        right = O.window_active([L - 1], w, L)
+        assert len(left) == w - w // 2 and left[0] == 0
+        assert len(right) == w // 2 + 1 and right[-1] == L - 1
+        mid = O.window_active([25], w, L)
+        assert len(mid) == w and 25 in mid and np.all(np.diff(mid) == 1)
+        assert mid[0] == 25 - w // 2
+    # disjoint interior windows: k*w positions
+    focus = [20, 60, 100, 140]
+    for w in (3, 8, 16, 33):
+        assert len(O.window_active(focus, w, 400)) == len(focus) * w
+
+
+# ------------------------------------------------------------------ attention
+
+def check_attention_closed_form():
+    for case in _golden("attention_closed_form.json")["cases"]:
+        Q, K, V = (np.array(case[x], dtype=np.float64) for x in ("q", "k", "v"))
+        d = Q.shape[-1]
+        out, lse = O.attention(Q, K, V, 1.0 / math.sqrt(d))
+        for h in range(case["Hq"]):
+            for i, row in enumerate(case["o"][h]):
+                if row is None:
+                    continue
+                _close(out[h, i], row, 1e-12, case["name"])
+                _close(lse[h, i], case["lse"][h][i], 1e-12, case["name"] + " lse")
+
+
+def _sdpa(Q, K, V, scale):
+    Hq, Hkv = Q.shape[0], K.shape[0]
+    q = torch.from_numpy(Q)[None]
+    k = torch.from_numpy(K)[None]
+    v = torch.from_numpy(V)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, scale=scale, enable_gqa=(Hq != Hkv))
+    return o[0].numpy()
+
+
+def check_attention_vs_library(seed=3):
+    rng = np.random.default_rng(seed)
+    for Hq, Hkv, n, m, d in [(1, 1, 5, 9, 8), (4, 4, 7, 13, 16), (6, 2, 3, 17, 8),
+                             (28, 4, 2, 40, 4), (2, 1, 1, 1, 64)]:
+        Q = rng.normal(size=(Hq, n, d))
+        K = rng.normal(size=(Hkv, m, d))
+        V = rng.normal(size=(Hkv, m, d))
+        scale = 1.0 / math.sqrt(d)
+        out, lse = O.attention(Q, K, V, scale)
+        _close(out, _sdpa(Q, K, V, scale), 1e-12, f"sdpa {Hq}/{Hkv}")
+        G = Hq // Hkv
+        for h in range(Hq):
+            S = Q[h] @ K[h // G].T * scale
+            _close(lse[h], scipy.special.logsumexp(S, axis=1), 1e-12, "lse")
+
+
+def check_attention_invariants(seed=4):
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, n, m, d = 4, 2, 6, 11, 8
+    Q = rng.normal(size=(Hq, n, d))
+    K = rng.normal(size=(Hkv, m, d))
+    V = rng.normal(size=(Hkv, m, d))
+    s = 0.3
+    out, lse = O.attention(Q, K, V, s)
+    # constant V rows -> O equals that row
+    Vc = np.broadcast_to(rng.normal(size=(Hkv, 1, d)), (Hkv, m, d)).copy()
+    oc, _ = O.attention(Q, K, Vc, s)
+    for h in range(Hq):
+        _close(oc[h], np.broadcast_to(Vc[h // 2, 0], (n, d)), 1e-12, "constant V")
+    # one key -> O = v and lse = q.k*s
+    o1, l1 = O.attention(Q, K[:, :1], V[:, :1], s)
+    for h in range(Hq):
+        _close(o1[h], np.broadcast_to(V[h // 2, 0], (n, d)), 1e-12, "single key")
+        _close(l1[h], Q[h] @ K[h // 2, 0] * s, 1e-12, "single key lse")
+    # permuting keys and values together leaves O and lse unchanged
+    perm = rng.permutation(m)
+    op, lp = O.attention(Q, K[:, perm], V[:, perm], s)
+    _close(op, out, 1e-12, "key permutation")
+    _close(lp, lse, 1e-12, "key permutation lse")
+    # permuting query rows permutes the output rows
+    qp = rng.permutation(n)
+    oq, _ = O.attention(Q[:, qp], K, V, s)
+    _close(oq, out[:, qp], 1e-12, "query permutation")
+    # no keys: zero output, lse = -inf
+    oe, le = O.attention(Q, K[:, :0], V[:, :0], s)
+    assert np.all(oe == 0) and np.all(np.isneginf(le))
+
+
+# ------------------------------------------------------------------ sinks
+
+def check_sink_scores_vs_library(seed=5):
+    rng = np.random.default_rng(seed)
+    for Hq, Hkv, n, L, d in [(4, 4, 5, 30, 8), (6, 2, 3, 41, 4), (2, 1, 1, 7, 16)]:
+        Q = rng.normal(size=(Hq, n, d))
+        K = rng.normal(size=(Hkv, L, d))
+        s = 1.0 / math.sqrt(d)
+        _, lse = O.attention(Q, K, K, s)
+        got = O.sink_scores(Q, K, lse, s)
+        expect = np.zeros(L)
+        G = Hq // Hkv
+        for h in range(Hq):
+            expect += scipy.special.softmax(Q[h] @ K[h // G].T * s, axis=1).sum(axis=0)
+        _close(got, expect, 1e-12, "sink scores")
+        # every query row spreads unit mass over the keys
+        _close(got.sum(), Hq * n, 1e-9, "total attention mass")
+
+
+def check_sink_select_dominance(seed=6):
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        L = int(rng.integers(1, 60))
+        scores = rng.integers(0, 6, size=L) / 5.0
+        n = int(rng.integers(0, L + 2))
+        assert dominance_ok(scores, range(L), O.sink_select(scores, n), n)
+        R = rng.integers(-3, 4, size=L).astype(np.float64)
+        assert dominance_ok(R, range(L), O.top_blocks(R, n), n)
+
+
+def check_sink_recovery(seeds=(0, 1, 2)):
+    """Sinks injected by the generator are the ones the oracle identifies."""
+    base = configs.TINY_2K_F32
+    for seed in seeds:
+        wl = base if seed == 0 else dataclasses.replace(base, seed=seed, sinks_fixed=())
+        conf, mask = synth.step_inputs(wl)
+        K, V = (synth.to_f64(t)[0] for t in synth.make_kv(wl, 0))
+        Q = synth.to_f64(synth.make_q(wl, 0))[0]
+        focus = O.pcgi_focus(conf[0], mask[0], wl.k)
+        active = O.window_active(focus, wl.w, wl.L)
+        _, lse = O.dense_attention(Q[:, active], K, V, wl.scale)
+        sinks = O.sink_select(O.sink_scores(Q[:, active], K, lse, wl.scale), wl.n_sinks)
+        assert list(sinks) == list(synth.sink_positions(wl, 0)), (seed, sinks)
+
+
+# ------------------------------------------------------------------ block pruning
+
+def _bf16_grid(rng, shape):
+    """Random values exactly representable in bf16 (8 significant bits)."""
+    mant = rng.integers(-255, 256, size=shape)
+    expo = rng.integers(-12, 2, size=shape)
+    return np.ldexp(mant.astype(np.float64), expo)
+
+
+def check_block_means_exact(seed=7):
+    rng = np.random.default_rng(seed)
+    for Hkv, P, extra, bs, d in [(2, 13, 3, 4, 3), (1, 16, 0, 4, 2), (3, 7, 2, 8, 2), (1, 1, 1, 1, 1)]:
+        K = _bf16_grid(rng, (Hkv, P + extra, d))
+        kbar = O.block_means(K, P, bs)
+        nb = -(-P // bs)
+        assert kbar.shape == (Hkv, nb, d)
+        for g in range(Hkv):
+            for b in range(nb):
+                lo, hi = b * bs, min(b * bs + bs, P)
+                for e in range(d):
+                    exact = sum(Fraction(float(K[g, j, e])) for j in range(lo, hi)) / (hi - lo)
+                    # the sum is exact in fp64; the one division rounds correctly
+                    assert float(kbar[g, b, e]) == float(exact), (g, b, e)
+    wl = configs.TINY_2K_F32
+    K = synth.to_f64(synth.make_kv(wl, 0)[0])[0]
+    kbar = O.block_means(K, wl.P, wl.bs)
+    for g, b, e in [(0, 0, 0), (1, 10, 5), (3, 30, 63), (2, 23, 17)]:
+        lo, hi = b * wl.bs, min(b * wl.bs + wl.bs, wl.P)
+        exact = sum(Fraction(float(K[g, j, e])) for j in range(lo, hi)) / (hi - lo)
+        assert float(kbar[g, b, e]) == float(exact)
+
+
+def check_relevance_bruteforce(seed=8):
+    rng = np.random.default_rng(seed)
+    for Hq, Hkv, n, P, bs, d in [(2, 2, 3, 10, 4, 3), (4, 2, 2, 9, 3, 2), (3, 1, 1, 5, 5, 2)]:
+        Q = _bf16_grid(rng, (Hq, n, d))
+        K = _bf16_grid(rng, (Hkv, P + 2, d))
+        scale = 0.25
+        R = O.block_relevance(Q, O.block_means(K, P, bs), scale)
+        nb = -(-P // bs)
+        G = Hq // Hkv
+        for b in range(nb):
+            lo, hi = b * bs, min(b * bs + bs, P)
+            total = Fraction(0)
+            for h in range(Hq):
+                for i in range(n):
+                    for e in range(d):
+                        mean = sum(Fraction(float(K[h // G, j, e])) for j in range(lo, hi)) / (hi - lo)
+                        total += Fraction(float(Q[h, i, e])) * mean
+            assert abs(float(R[b]) - float(total) * scale) <= 1e-12 * (1 + abs(float(total))), b
+    # one head, one query row: R_b = scale * q . kbar_b
+    q = rng.normal(size=(1, 1, 4))
+    K = rng.normal(size=(1, 12, 4))
+    kbar = O.block_means(K, 12, 4)
+    _close(O.block_relevance(q, kbar, 0.5), 0.5 * kbar[0] @ q[0, 0], 1e-12, "single row")
+
+
+def check_block_fixture():
+    for case in _golden("block_keyset_hand.json")["cases"]:
+        K = np.array(case["k"], dtype=np.float64)
+        Q = np.array(case["q"], dtype=np.float64)
+        kbar = O.block_means(K, case["P"], case["bs"])
+        _close(kbar, case["kbar"], 0.0, "kbar")
+        R = O.block_relevance(Q, kbar, case["scale"])
+        _close(R, case["R"], 1e-15, "R")
+        for C, sel in case["C"].items():
+            blocks = O.top_blocks(R, int(C))
+            assert list(blocks) == sel["blocks"], (C, case["why"])
+            I_p = O.key_set(sel["sinks"], blocks, case["bs"], case["P"], case["L"])
+            assert list(I_p) == sel["I_p"], (C, case["why"])
+
+
+def check_key_set(seed=9):
+    rng = np.random.default_rng(seed)
+    for _ in range(100):
+        bs = int(rng.integers(1, 9))
+        P = int(rng.integers(1, 60))
+        L = P + int(rng.integers(0, 20))
+        nb = -(-P // bs)
+        blocks = np.sort(rng.choice(nb, size=int(rng.integers(0, nb + 1)), replace=False))
+        sinks = np.sort(rng.choice(L, size=int(rng.integers(0, min(L, 6) + 1)), replace=False))
+        I_p = O.key_set(sinks, blocks, bs, P, L)
+        members = [j for j in range(L)
+                   if j >= P or j in set(sinks.tolist()) or (j // bs) in set(blocks.tolist())]
+        assert list(I_p) == members
+    # every block kept: the whole sequence; nothing kept: the generation region
+    assert list(O.key_set([], range(8), 4, 30, 37)) == list(range(37))
+    assert list(O.key_set([], [], 4, 30, 37)) == list(range(30, 37))
+    assert list(O.key_set([1, 2, 33], [0], 4, 30, 37)) == [0, 1, 2, 3] + list(range(30, 37))
+
+
+# ------------------------------------------------------------------ sparse step
+
+def _tiny_inputs(wl=configs.TINY_2K_F32):
+    conf, mask = synth.step_inputs(wl)
+    K, V = (synth.to_f64(t)[0] for t in synth.make_kv(wl, 0))
+    Q = synth.to_f64(synth.make_q(wl, 0))[0]
+    return conf[0], mask[0], Q, K, V
+
+
+def check_sparse_equals_dense():
+    """Every block kept and a window over the whole sequence: sparse == dense."""
+    wl = configs.TINY_2K_F32
+    conf, mask, Q, K, V = _tiny_inputs(wl)
+    focus = O.pcgi_focus(conf, mask, wl.k)
+    active = O.window_active(focus, 2 * wl.L, wl.L)
+    assert list(active) == list(range(wl.L))
+    Qa = Q[:, active[::17]]
+    dense, dlse = O.dense_attention(Qa, K, V, wl.scale)
+    R = O.block_relevance(Qa, O.block_means(K, wl.P, wl.bs), wl.scale)
+    blocks = O.top_blocks(R, wl.nb)
+    I_p = O.key_set([], blocks, wl.bs, wl.P, wl.L)
+    sparse, slse = O.sparse_attention(Qa, K, V, I_p, wl.scale)
+    _close(sparse, dense, 1e-13, "sparse == dense")
+    _close(slse, dlse, 1e-12, "sparse == dense lse")
+
+
+def check_sparse_vs_library(seed=10):
+    wl = configs.TINY_2K_F32
+    conf, mask, Q, K, V = _tiny_inputs(wl)
+    rng = np.random.default_rng(seed)
+    active = np.sort(rng.choice(wl.L, 24, replace=False))
+    sinks = [3, 700, 2040]
+    blocks = np.sort(rng.choice(wl.nb, 5, replace=False))
+    I_p = O.key_set(sinks, blocks, wl.bs, wl.P, wl.L)
+    out, _ = O.sparse_attention(Q[:, active], K, V, I_p, wl.scale)
+    ref = _sdpa(Q[:, active].copy(), K[:, I_p].copy(), V[:, I_p].copy(), wl.scale)
+    _close(out, ref, 1e-12, "sparse vs library on the gathered keys")
+    # no sinks, no blocks: attention over the generation region only
+    I_gen = O.key_set([], [], wl.bs, wl.P, wl.L)
+    out, _ = O.sparse_attention(Q[:, active], K, V, I_gen, wl.scale)
+    ref = _sdpa(Q[:, active].copy(), K[:, wl.P:].copy(), V[:, wl.P:].copy(), wl.scale)
+    _close(out, ref, 1e-12, "generation region only")
+
+
+def check_step_composition():
+    """The one-layer driver reproduces its parts and keeps the sink blocks."""
+    wl = configs.TINY_2K_F32
+    conf, mask, Q, K, V = _tiny_inputs(wl)
+    st = O.sparse_step(conf, mask, lambda l: (Q, K, V), layers=1, l_dense=1, n_t=wl.n_t,
+                       rho=wl.rho, w=wl.w, P=wl.P, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
+                       scale=wl.scale)
+    assert len(st.focus) == wl.k
+    assert list(st.sinks) == list(wl.sinks_fixed)
+    assert {s // wl.bs for s in wl.sinks_fixed} <= set(st.blocks[0].tolist())
+    out, _ = O.sparse_attention(Q[:, st.active], K, V,
+                                O.key_set(st.sinks, st.blocks[0], wl.bs, wl.P, wl.L), wl.scale)
+    _close(st.out[("sparse", 0)], out, 0.0, "driver sparse output")
+
+
+ALL_CHECKS = [
+    check_focus_count, check_pcgi_dominance, check_pcgi_exhaustive, check_pcgi_window_fixture,
+    check_window_closed_forms, check_attention_closed_form, check_attention_vs_library,
+    check_attention_invariants, check_sink_scores_vs_library, check_sink_select_dominance,
+    check_sink_recovery, check_block_means_exact, check_relevance_bruteforce,
+    check_block_fixture, check_key_set, check_sparse_equals_dense, check_sparse_vs_library,
+    check_step_composition,
+]

@@ -1,0 +1,101 @@
+"""Mistakes planted in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutation replaces one oracle function with a plausible wrong version (a
+dropped term, a wrong index or sign, a transposed operand, a wrong tie-break)
+and runs the pins; the test passes only if some pin raises.
+"""
+import numpy as np
+import pytest
+
+import oracle_checks
+from oracle import focus_oracle as O
+
+_orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
+
+
+def _rank_highest_index(values, candidates, count):
+    ranked = sorted((int(i) for i in candidates), key=lambda i: (-float(values[i]), -i))
+    return np.array(sorted(ranked[: max(count, 0)]), dtype=np.int64)
+
+
+def _rank_smallest(values, candidates, count):
+    ranked = sorted((int(i) for i in candidates), key=lambda i: (float(values[i]), i))
+    return np.array(sorted(ranked[: max(count, 0)]), dtype=np.int64)
+
+
+def _window_shifted(focus, w, L):
+    return _orig["window_active"]([p + 1 for p in focus], w, L)
+
+
+def _window_centered(focus, w, L):
+    members = set()
+    for p in focus:
+        for j in range(int(p) - w // 2, int(p) + w // 2 + 1):
+            if 0 <= j < L:
+                members.add(j)
+    return np.array(sorted(members), dtype=np.int64)
+
+
+def _block_means_by_bs(K, P, bs):
+    K = np.asarray(K, dtype=np.float64)
+    nb = -(-P // bs)
+    out = np.zeros((K.shape[0], nb, K.shape[2]))
+    for b in range(nb):
+        out[:, b] = K[:, b * bs:min((b + 1) * bs, P)].sum(axis=1) / bs
+    return out
+
+
+def _relevance_first_head(Q, kbar, scale):
+    return _orig["block_relevance"](np.asarray(Q)[:1], kbar[:1], scale)
+
+
+def _key_set_no_gen(sinks, blocks, bs, P, L):
+    return _orig["key_set"](sinks, blocks, bs, P, P)
+
+
+def _key_set_block_shift(sinks, blocks, bs, P, L):
+    return _orig["key_set"](sinks, [b + 1 for b in blocks if b + 1 < -(-P // bs)], bs, P, L)
+
+
+MUTATIONS = {
+    "tie_break_highest_index": ("rank_select", _rank_highest_index),
+    "select_smallest": ("rank_select", _rank_smallest),
+    "pcgi_ignores_mask": ("pcgi_focus",
+                          lambda conf, mask, k: _orig["rank_select"](
+                              np.asarray(conf, np.float32), range(len(mask)), k)),
+    "focus_count_round": ("focus_count", lambda n_t, rho: int(round(rho * n_t))),
+    "window_shifted": ("window_active", _window_shifted),
+    "window_centered_2h_plus_1": ("window_active", _window_centered),
+    "gqa_modulo_mapping": ("kv_head", lambda h, Hq, Hkv: h % Hkv),
+    "attention_no_scale": ("attention", lambda Q, K, V, s: _orig["attention"](Q, K, V, 1.0)),
+    "attention_k_v_swapped": ("attention", lambda Q, K, V, s: _orig["attention"](Q, V, K, s)),
+    "sink_scores_unnormalised": ("sink_scores",
+                                 lambda Q, K, lse, s: _orig["sink_scores"](
+                                     Q, K, np.zeros_like(np.asarray(lse)), s)),
+    "sink_scores_dropped_head": ("sink_scores",
+                                 lambda Q, K, lse, s: _orig["sink_scores"](
+                                     np.asarray(Q)[1:], K[1:] if len(K) > 1 else K,
+                                     np.asarray(lse)[1:], s)),
+    "block_means_divide_by_bs": ("block_means", _block_means_by_bs),
+    "relevance_first_head_only": ("block_relevance", _relevance_first_head),
+    "relevance_sign_flipped": ("block_relevance",
+                               lambda Q, kbar, s: -_orig["block_relevance"](Q, kbar, s)),
+    "key_set_without_generation_region": ("key_set", _key_set_no_gen),
+    "key_set_block_off_by_one": ("key_set", _key_set_block_shift),
+    "sparse_ignores_key_set": ("sparse_attention",
+                               lambda Q, K, V, I_p, s: _orig["attention"](Q, K, V, s)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, bad)
+    caught = []
+    for check in oracle_checks.ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"
