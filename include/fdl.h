@@ -1,0 +1,192 @@
+/*
+ * fdl.h - C ABI of the Focus-dLLM sparse attention step on AMD Instinct MI355X (gfx950).
+ *
+ * One non-block-entry denoising step of a long-context diffusion LLM, as the
+ * structured summary of "Focus-dLLM: Accelerating Long-Context Diffusion LLM
+ * Inference via Confidence-Guided Context Focusing" (paper.rainbus.top/paper/
+ * 2602.02159) describes it in its sections "Core method" and "Method steps"
+ * (1)-(5):
+ *   fdl_pcgi_select       (1) top-k masked positions by previous confidence, (2) windows
+ *   fdl_dense_attention   (3) dense layers 1..l_dense, and the block-entry full refresh
+ *   fdl_sink_identify     (3) attention sinks from layer l_dense's attention distribution
+ *   fdl_block_score_topc  (4) mean key per prompt block, relevance R_b, top-C blocks
+ *   fdl_sparse_attention  (5) attention of the active queries over I_p only
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates device memory, never frees, never synchronises the stream
+ *     and never throws or aborts: it validates what the host can see, enqueues
+ *     its kernels on `stream` (NULL = the default stream) and returns a status.
+ *     Kernels read device-side counts (n_focus, n_active) themselves, so a whole
+ *     step runs without a host round trip.
+ *   - Entry points that need temporary device memory take a caller-owned
+ *     workspace (`ws`, `ws_bytes`); the matching *_workspace_bytes function
+ *     returns the size needed.  The workspace holds no state between calls.
+ *   - dtype (fdl_dtype) is shared by Q, K, V and O: FDL_F32, or FDL_BF16 with fp32
+ *     accumulation.  Head dim d is 64 or 128 and is contiguous in memory.
+ *     Q, K, V and O are addressed as base + b*s.b + h*s.h + row*s.r (element
+ *     strides, fdl_strides); each row must start on a 16-byte boundary.
+ *   - Query rows: the logical query row r of sequence b reads the physical row
+ *     q_idx[b*nq_max + r] of Q when q_idx is non-NULL (e.g. the active_idx output
+ *     of fdl_pcgi_select), else row r.  Rows r >= n_q[b] are padding (n_q NULL:
+ *     all nq_max rows are valid); padding rows of O are written as 0 and their
+ *     log-sum-exp as -inf.  Physical rows and indices must lie in [0, L); the
+ *     host cannot check device-resident indices, and out-of-range values there
+ *     give undefined results.
+ *   - Grouped-query attention: query head h reads KV head floor(h*Hkv/Hq);
+ *     Hq % Hkv == 0.  Scale: `scale` <= 0 selects 1/sqrt(d).  Attention has no
+ *     mask (dLLM attention is bidirectional).
+ *   - Index outputs are ascending and padded with -1.  Selections order by value,
+ *     larger first, and take the lower index among equal values.
+ *   - Calls are stream-ordered and reentrant; there is no global state.  Two
+ *     calls that share a workspace must be ordered on one stream.
+ */
+#ifndef FDL_H
+#define FDL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fdl_status {
+    FDL_OK = 0,
+    FDL_ERR_NULL = 1,        /* a required pointer is NULL */
+    FDL_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or inconsistent */
+    FDL_ERR_DTYPE = 3,       /* dtype is not FDL_F32 or FDL_BF16 */
+    FDL_ERR_ALIGN = 4,       /* a pointer or a row stride breaks the 16-byte row alignment */
+    FDL_ERR_WORKSPACE = 5,   /* ws is NULL or ws_bytes is below the *_workspace_bytes size */
+    FDL_ERR_HIP = 6,         /* a kernel launch failed; the HIP error is left for hipGetLastError */
+    FDL_ERR_UNSUPPORTED = 7  /* a valid but unsupported configuration (head dim other than 64/128) */
+} fdl_status;
+
+typedef enum fdl_dtype { FDL_F32 = 0, FDL_BF16 = 1 } fdl_dtype;
+
+/* Element strides of the batch, head and row axes; the head-dim axis is contiguous. */
+typedef struct fdl_strides { int64_t b, h, r; } fdl_strides;
+
+/* Static text for a status code (never NULL). */
+const char* fdl_status_string(fdl_status status);
+
+/* k = floor(rho * n_t), evaluated in double precision (negative results clamp to 0). */
+int fdl_focus_count(int n_t, double rho);
+
+/*
+ * fdl_pcgi_select - past-confidence-guided focus selection and window expansion.
+ * Summary page, "Core method" and "Method steps" (1)-(2): among the positions
+ * still [MASK], keep the k = floor(rho*n_t) with the highest previous-step
+ * confidence c_{t-1} (I_focus), then widen each focus position p to the window
+ * [p - floor(w/2), p - floor(w/2) + w) clipped to [0, L); the union is I_active.
+ *   conf       [B, L] fp32, previous-step confidence (compared exactly; NaN unsupported,
+ *              -0.0 equals +0.0)
+ *   mask       [B, L] uint8, non-zero where the slot is still [MASK]
+ *   focus_idx  [B, k_cap] out, I_focus ascending, -1 padded; k_cap >= k
+ *   n_focus    [B] out, min(k, #masked)
+ *   active_idx [B, nq_max] out, I_active ascending, -1 padded; nq_max >= min(k*w, L)
+ *   n_active   [B] out, |I_active|
+ * Fewer masked slots than k: all of them are kept.  Errors: FDL_ERR_NULL,
+ * FDL_ERR_SHAPE (B, L, w < 1, n_t < 0, rho < 0 or NaN, k_cap or nq_max too small).
+ */
+fdl_status fdl_pcgi_select(const float* conf, const uint8_t* mask, int B, int L,
+                           int n_t, double rho, int w,
+                           int32_t* focus_idx, int32_t* n_focus, int k_cap,
+                           int32_t* active_idx, int32_t* n_active, int nq_max,
+                           hipStream_t stream);
+
+/*
+ * fdl_dense_attention - full bidirectional attention of the given query rows over all L keys.
+ * Summary page, "Method steps": the block-entry full refresh (use_sparse = False,
+ * every row attends to every key) and the dense layers 1..l_dense of a sparse step
+ * (step (3)), there for the active rows only (q_idx = active_idx, n_q = n_active).
+ *   q       [B, Hq, *, d] with strides qs; q_idx [B, nq_max] or NULL; n_q [B] or NULL
+ *   k, v    [B, Hkv, L, d] with strides ks, vs
+ *   o       [B, Hq, nq_max, d] out with strides os, in the input dtype
+ *   lse     [B, Hq, nq_max] fp32 out (natural log of the softmax denominator) or NULL
+ * Workspace: fdl_dense_attention_workspace_bytes (partial results of the key split).
+ */
+size_t fdl_dense_attention_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int L,
+                                           int d, int nq_max);
+fdl_status fdl_dense_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int d,
+                               const void* q, fdl_strides qs, const int32_t* q_idx,
+                               const int32_t* n_q, int nq_max,
+                               const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                               float scale, void* o, fdl_strides os, float* lse,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fdl_sink_identify - attention-sink positions from layer l_dense.
+ * Summary page, "Prerequisites" (attention sinks) and "Method steps" (3): layer
+ * l_dense's attention distribution identifies the sinks, which every deeper layer
+ * of the step reuses.  score_j = sum over query heads h and valid query rows i of
+ * exp(q_{h,i} . k_{g(h),j} * scale - lse_{h,i}), for every key j in [0, L); the
+ * n_sinks keys of highest score form I_sink.
+ *   q, q_idx, n_q, nq_max, k, ks, scale   as in fdl_dense_attention (same layer)
+ *   lse        [B, Hq, nq_max] fp32, the lse output of fdl_dense_attention for these rows
+ *   sink_idx   [B, n_sinks] out, ascending
+ *   scores     [B, L] fp32 out, or NULL
+ * Errors as fdl_dense_attention; n_sinks must lie in [0, L].
+ */
+size_t fdl_sink_identify_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int L,
+                                         int d, int nq_max);
+fdl_status fdl_sink_identify(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int d,
+                             const void* q, fdl_strides qs, const int32_t* q_idx,
+                             const int32_t* n_q, int nq_max,
+                             const void* k, fdl_strides ks, float scale, const float* lse,
+                             int n_sinks, int32_t* sink_idx, float* scores,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fdl_block_score_topc - prompt-block pruning.
+ * Summary page, "Method steps" (4): split the P prompt keys into nb = ceil(P/bs)
+ * contiguous blocks, represent each by the mean of its keys kbar_b, score every
+ * block by its relevance to the candidate queries and keep the C best.
+ * R_b = scale * sum over query heads h and valid query rows i of q_{h,i} . kbar_{g(h),b}
+ * (one block set per sequence, shared by all heads).  The kernels accumulate R_b
+ * in fp64.
+ *   q, q_idx, n_q, nq_max, k, ks, scale   as in fdl_dense_attention
+ *   P, bs, C   prompt length (P <= L), block size (>= 1), blocks kept (>= 0)
+ *   block_idx  [B, C] out, ascending, -1 padded when C > nb
+ *   R          [B, nb] fp64 out, or NULL
+ *   kbar       [B, Hkv, nb, d] fp32 out (block means, rounded once from fp64), or NULL
+ */
+size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int P,
+                                            int d, int bs);
+fdl_status fdl_block_score_topc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int P, int d,
+                                const void* q, fdl_strides qs, const int32_t* q_idx,
+                                const int32_t* n_q, int nq_max,
+                                const void* k, fdl_strides ks, float scale, int bs, int C,
+                                int32_t* block_idx, double* R, float* kbar,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fdl_sparse_attention - attention of the active queries over I_p only.
+ * Summary page, "Method steps" (5): I_p is the union of the sinks and the
+ * selected prompt blocks; this library also adds the generation region [P, L)
+ * (without it, keeping every block could not reproduce dense attention).  Each
+ * key of I_p is attended once, however many of the three sets hold it.
+ *   q, q_idx, n_q, nq_max, k, ks, v, vs, scale, o, os, lse   as in fdl_dense_attention
+ *   sink_idx   [B, n_sinks] ascending, -1 entries ignored (fdl_sink_identify output)
+ *   block_idx  [B, C] ascending, -1 entries ignored (fdl_block_score_topc output)
+ *   P, bs      prompt length and block size used to select block_idx
+ */
+size_t fdl_sparse_attention_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int L,
+                                            int P, int d, int nq_max, int n_sinks, int C,
+                                            int bs);
+fdl_status fdl_sparse_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int P, int d,
+                                const void* q, fdl_strides qs, const int32_t* q_idx,
+                                const int32_t* n_q, int nq_max,
+                                const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                const int32_t* sink_idx, int n_sinks,
+                                const int32_t* block_idx, int C, int bs,
+                                float scale, void* o, fdl_strides os, float* lse,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDL_H */

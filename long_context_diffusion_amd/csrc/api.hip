@@ -1,0 +1,239 @@
+// Host side of the C ABI declared in include/fdl.h: argument validation,
+// workspace sizing and kernel launches.  No allocation, no synchronisation.
+
+#include <cmath>
+#include <cstdint>
+
+#include "ops.cuh"
+
+using namespace fdl;
+
+namespace {
+
+constexpr int kMaxSparseSinks = 4096;  // LDS bitmask of the sparse attention kernel
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t elem_size(fdl_dtype dt) { return dt == FDL_BF16 ? 2 : 4; }
+
+fdl_status check_dtype_dims(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d) {
+    if (dt != FDL_F32 && dt != FDL_BF16) return FDL_ERR_DTYPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1) return FDL_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FDL_ERR_SHAPE;
+    if (d != 64 && d != 128) return FDL_ERR_UNSUPPORTED;
+    return FDL_OK;
+}
+
+// Row starts base + b*s.b + h*s.h + r*s.r must be 16-byte aligned, and d contiguous elements
+// must fit between rows (|s.r| >= d) unless there is a single row.
+fdl_status check_tensor(const void* p, fdl_strides s, fdl_dtype dt, int d) {
+    if (!p) return FDL_ERR_NULL;
+    if (!aligned16(p)) return FDL_ERR_ALIGN;
+    const int64_t e = static_cast<int64_t>(elem_size(dt));
+    if ((s.b * e) % 16 || (s.h * e) % 16 || (s.r * e) % 16) return FDL_ERR_ALIGN;
+    if (s.r < d && s.r > -d) return FDL_ERR_SHAPE;
+    return FDL_OK;
+}
+
+fdl_status check_rows(int nq_max, int Gq) {
+    if (nq_max < 0) return FDL_ERR_SHAPE;
+    if (static_cast<int64_t>(nq_max) * Gq > (1ll << 30)) return FDL_ERR_SHAPE;
+    return FDL_OK;
+}
+
+fdl_status check_ws(const void* ws, size_t have, size_t need) {
+    if (need == 0) return FDL_OK;
+    if (!ws || have < need) return FDL_ERR_WORKSPACE;
+    if (!aligned16(ws)) return FDL_ERR_ALIGN;
+    return FDL_OK;
+}
+
+inline float resolve_scale(float scale, int d) {
+    return scale > 0.0f ? scale : static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+}
+
+inline fdl_status hip_status(hipError_t e) { return e == hipSuccess ? FDL_OK : FDL_ERR_HIP; }
+
+constexpr float kLog2eF = 1.44269504088896340736f;
+
+AttnArgs attn_args(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, const void* q, fdl_strides qs,
+                   const int32_t* q_idx, const int32_t* n_q, int nq_max, const void* k, fdl_strides ks,
+                   const void* v, fdl_strides vs, float scale, int d, void* o, fdl_strides os, float* lse,
+                   void* ws) {
+    AttnArgs a{};
+    a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
+    a.q_idx = q_idx; a.n_q = n_q; a.nq_max = nq_max;
+    a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
+    a.v = v; a.vsb = vs.b; a.vsh = vs.h; a.vsr = vs.r;
+    a.o = o; a.osb = os.b; a.osh = os.h; a.osr = os.r;
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.P = P; a.Gq = Hq / Hkv;
+    a.sl2 = resolve_scale(scale, d) * kLog2eF;
+    a.part_o = static_cast<float*>(ws);
+    (void)dt;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fdl_status_string(fdl_status s) {
+    switch (s) {
+        case FDL_OK: return "ok";
+        case FDL_ERR_NULL: return "a required pointer is NULL";
+        case FDL_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case FDL_ERR_DTYPE: return "unsupported dtype";
+        case FDL_ERR_ALIGN: return "a pointer or row stride is not 16-byte aligned";
+        case FDL_ERR_WORKSPACE: return "workspace missing or too small";
+        case FDL_ERR_HIP: return "a HIP kernel launch failed";
+        case FDL_ERR_UNSUPPORTED: return "unsupported configuration";
+    }
+    return "unknown status";
+}
+
+int fdl_focus_count(int n_t, double rho) {
+    if (!(rho >= 0.0) || n_t < 0) return 0;
+    const double k = std::floor(rho * static_cast<double>(n_t));
+    return k > 2147483647.0 ? 2147483647 : static_cast<int>(k);
+}
+
+fdl_status fdl_pcgi_select(const float* conf, const uint8_t* mask, int B, int L, int n_t, double rho,
+                           int w, int32_t* focus_idx, int32_t* n_focus, int k_cap, int32_t* active_idx,
+                           int32_t* n_active, int nq_max, hipStream_t stream) {
+    if (!conf || !mask || !focus_idx || !n_focus || !active_idx || !n_active) return FDL_ERR_NULL;
+    if (B < 1 || L < 1 || w < 1 || n_t < 0 || !(rho >= 0.0) || !std::isfinite(rho)) return FDL_ERR_SHAPE;
+    const int k = fdl_focus_count(n_t, rho);
+    if (k_cap < k || k_cap < 0) return FDL_ERR_SHAPE;
+    const int64_t need = static_cast<int64_t>(k) * w < L ? static_cast<int64_t>(k) * w : L;
+    if (nq_max < need) return FDL_ERR_SHAPE;
+    return hip_status(launch_pcgi_select(conf, mask, B, L, k, w, focus_idx, n_focus, k_cap, active_idx,
+                                         n_active, nq_max, stream));
+}
+
+size_t fdl_dense_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d,
+                                           int nq_max) {
+    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 1) return 0;
+    return plan_attention(dt, B, Hq, Hkv, d, nq_max, L).ws_bytes;
+}
+
+fdl_status fdl_dense_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, const void* q,
+                               fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                               const void* k, fdl_strides ks, const void* v, fdl_strides vs, float scale,
+                               void* o, fdl_strides os, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
+    if (st != FDL_OK) return st;
+    if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
+    if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(v, vs, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
+    if (nq_max == 0) return FDL_OK;
+    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, L);
+    if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
+    AttnArgs a = attn_args(dt, B, Hq, Hkv, L, L, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, scale, d, o, os,
+                           lse, ws);
+    a.sparse = 0;
+    return hip_status(launch_attention(dt, d, a, pl, stream));
+}
+
+size_t fdl_sink_identify_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, int nq_max) {
+    (void)nq_max;
+    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK) return 0;
+    return sink_workspace_bytes(B, Hkv, L);
+}
+
+fdl_status fdl_sink_identify(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, const void* q,
+                             fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                             const void* k, fdl_strides ks, float scale, const float* lse, int n_sinks,
+                             int32_t* sink_idx, float* scores, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
+    if (st != FDL_OK) return st;
+    if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
+    if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if (!lse || !sink_idx) return FDL_ERR_NULL;
+    if (n_sinks < 0 || n_sinks > L) return FDL_ERR_SHAPE;
+    if ((st = check_ws(ws, ws_bytes, sink_workspace_bytes(B, Hkv, L))) != FDL_OK) return st;
+    SinkArgs a{};
+    a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
+    a.q_idx = q_idx; a.n_q = n_q; a.nq_max = nq_max;
+    a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.Gq = Hq / Hkv;
+    a.sl2 = resolve_scale(scale, d) * kLog2eF;
+    return hip_status(launch_sink_identify(dt, d, a, n_sinks, sink_idx, scores, ws, stream));
+}
+
+size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int P, int d, int bs) {
+    if (check_dtype_dims(dt, B, Hq, Hkv, P < 1 ? 1 : P, d) != FDL_OK || P < 1 || bs < 1) return 0;
+    return block_workspace_bytes(B, Hkv, P, d, bs);
+}
+
+fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
+                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                                const void* k, fdl_strides ks, float scale, int bs, int C,
+                                int32_t* block_idx, double* R, float* kbar, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
+    if (st != FDL_OK) return st;
+    if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
+    if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if (!block_idx) return FDL_ERR_NULL;
+    if (P < 1 || P > L || bs < 1 || C < 0) return FDL_ERR_SHAPE;
+    if ((st = check_ws(ws, ws_bytes, block_workspace_bytes(B, Hkv, P, d, bs))) != FDL_OK) return st;
+    BlockArgs a{};
+    a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
+    a.q_idx = q_idx; a.n_q = n_q; a.nq_max = nq_max;
+    a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.P = P; a.Gq = Hq / Hkv; a.bs = bs;
+    a.nb = static_cast<int>((static_cast<int64_t>(P) + bs - 1) / bs);
+    a.scale = resolve_scale(scale, d);
+    a.kbar = kbar;
+    return hip_status(launch_block_score_topc(dt, d, a, C, block_idx, R, ws, stream));
+}
+
+size_t fdl_sparse_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d,
+                                            int nq_max, int n_sinks, int C, int bs) {
+    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 1 || bs < 1 || P < 0 || P > L ||
+        C < 0 || n_sinks < 0)
+        return 0;
+    return plan_attention(dt, B, Hq, Hkv, d, nq_max, sparse_key_bound(L, P, n_sinks, C, bs)).ws_bytes;
+}
+
+fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
+                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                                const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                const int32_t* sink_idx, int n_sinks, const int32_t* block_idx, int C,
+                                int bs, float scale, void* o, fdl_strides os, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
+    if (st != FDL_OK) return st;
+    if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
+    if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(v, vs, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
+    if (P < 0 || P > L || bs < 1 || C < 0 || n_sinks < 0) return FDL_ERR_SHAPE;
+    if ((n_sinks > 0 && !sink_idx) || (C > 0 && !block_idx)) return FDL_ERR_NULL;
+    if (n_sinks > kMaxSparseSinks) return FDL_ERR_UNSUPPORTED;
+    if (nq_max == 0) return FDL_OK;
+    const int64_t bound = sparse_key_bound(L, P, n_sinks, C, bs);
+    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, bound);
+    if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
+    AttnArgs a = attn_args(dt, B, Hq, Hkv, L, P, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, scale, d, o, os,
+                           lse, ws);
+    a.sparse = 1;
+    a.sink_idx = sink_idx;
+    a.n_sinks = n_sinks;
+    a.block_idx = block_idx;
+    a.C = C;
+    a.bs = bs;
+    a.nb = static_cast<int>((static_cast<int64_t>(P) + bs - 1) / bs);
+    return hip_status(launch_attention(dt, d, a, pl, stream));
+}
+
+}  // extern "C"

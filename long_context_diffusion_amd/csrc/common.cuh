@@ -1,0 +1,217 @@
+// Device helpers shared by the Focus-dLLM kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fdl.h"
+
+namespace fdl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16 helpers
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element loads/stores for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
+    static __device__ __forceinline__ float load(const uint16_t* p) {
+        return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, float x) {
+        *p = static_cast<uint16_t>(f32_to_bf16_bits(x));
+    }
+};
+
+// ------------------------------------------------------------------ ordered keys
+
+// Monotone map of a float to uint32: a < b  <=>  okey(a) < okey(b); -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t okey32(float f) {
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t okey64(double f) {
+    uint64_t u = static_cast<uint64_t>(__double_as_longlong(f == 0.0 ? 0.0 : f));
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// ------------------------------------------------------------------ wave / block scans
+
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
+// `s_tmp` holds >= 17 ints.  Returns the exclusive prefix; *total gets the block sum.
+__device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    int inc = wave_inclusive_sum(x);
+    if (lane == kWave - 1) s_tmp[wv] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < nw; ++i) {
+            int t = s_tmp[i];
+            s_tmp[i] = run;
+            run += t;
+        }
+        s_tmp[16] = run;
+    }
+    __syncthreads();
+    int excl = s_tmp[wv] + inc - x;
+    *total = s_tmp[16];
+    __syncthreads();
+    return excl;
+}
+
+// ------------------------------------------------------------------ top-k selection
+
+// Shared scratch for block_kth_largest / block_emit_topk.
+struct SelectSmem {
+    int hist[256];
+    int tmp[17];
+    int digit;
+    int remaining;
+};
+
+// Per-thread contiguous chunk [lo, hi) of [0, n).
+__device__ __forceinline__ void thread_chunk(int n, int* lo, int* hi) {
+    const int chunk = (n + blockDim.x - 1) / blockDim.x;
+    *lo = min(n, static_cast<int>(threadIdx.x) * chunk);
+    *hi = min(n, *lo + chunk);
+}
+
+// Radix select: the k-th largest ordered key among the valid entries of [0, n)
+// (1 <= k <= number of valid entries).  KeyFn(j, &key) returns whether entry j
+// takes part.  Every thread of the block must call it; all get the same result.
+template <typename U, typename KeyFn>
+__device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
+    constexpr int kBits = 8 * sizeof(U);
+    U prefix = 0, prefix_mask = 0;
+    int remaining = k;
+    int lo, hi;
+    thread_chunk(n, &lo, &hi);
+    for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) sm->hist[i] = 0;
+        __syncthreads();
+        for (int j = lo; j < hi; ++j) {
+            U kj;
+            if (key_of(j, &kj) && (kj & prefix_mask) == prefix)
+                atomicAdd(&sm->hist[static_cast<int>((kj >> shift) & 0xff)], 1);
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            // lane l owns bins 4l..4l+3; find the bin holding the remaining-th largest
+            const int l = threadIdx.x;
+            int h[4];
+            for (int q = 0; q < 4; ++q) h[q] = sm->hist[4 * l + q];
+            int mine = h[0] + h[1] + h[2] + h[3];
+            // sum over lanes above l (bins above 4l+3)
+            int suffix = mine;
+            for (int off = 1; off < kWave; off <<= 1) {
+                int y = __shfl_down(suffix, off, kWave);
+                if (l + off < kWave) suffix += y;
+            }
+            int above = suffix - mine;
+            for (int q = 3; q >= 0; --q) {
+                if (above < remaining && remaining <= above + h[q]) {
+                    sm->digit = 4 * l + q;
+                    sm->remaining = remaining - above;
+                }
+                above += h[q];
+            }
+        }
+        __syncthreads();
+        const int dgt = sm->digit;
+        remaining = sm->remaining;
+        prefix |= static_cast<U>(dgt) << shift;
+        prefix_mask |= static_cast<U>(0xff) << shift;
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// Writes, in ascending index order, the k valid entries with the largest keys
+// (lower index first among equal keys) to out[0..), pads out[..cap) with -1 and
+// returns the number written (min(k, valid)).  Every thread must call it.
+template <typename U, typename KeyFn>
+__device__ int block_emit_topk(int n, int k, KeyFn key_of, int32_t* out, int cap,
+                               SelectSmem* sm) {
+    int lo, hi;
+    thread_chunk(n, &lo, &hi);
+    int nvalid_local = 0;
+    for (int j = lo; j < hi; ++j) {
+        U kj;
+        nvalid_local += key_of(j, &kj) ? 1 : 0;
+    }
+    int nvalid;
+    block_exclusive_sum(nvalid_local, sm->tmp, &nvalid);
+    const bool take_all = nvalid <= k;
+    const int nsel = take_all ? nvalid : max(k, 0);
+    U thr = 0;
+    if (!take_all && nsel > 0) thr = block_kth_largest<U>(n, nsel, key_of, sm);
+    // counts above the threshold and ties in this thread's chunk
+    int gt = 0, eq = 0;
+    if (nsel > 0) {
+        for (int j = lo; j < hi; ++j) {
+            U kj;
+            if (!key_of(j, &kj)) continue;
+            if (take_all || kj > thr) ++gt;
+            else if (kj == thr) ++eq;
+        }
+    }
+    int gt_total, eq_total;
+    int gt_before = block_exclusive_sum(gt, sm->tmp, &gt_total);
+    int eq_before = block_exclusive_sum(eq, sm->tmp, &eq_total);
+    const int ties_taken = nsel - gt_total;  // lowest-index ties fill the rest
+    if (nsel > 0) {
+        for (int j = lo; j < hi; ++j) {
+            U kj;
+            if (!key_of(j, &kj)) continue;
+            const bool above = take_all || kj > thr;
+            const bool tie = !above && kj == thr;
+            if (above) {
+                out[gt_before + min(eq_before, ties_taken)] = j;
+                ++gt_before;
+            } else if (tie) {
+                if (eq_before < ties_taken) out[gt_before + eq_before] = j;
+                ++eq_before;
+            }
+        }
+    }
+    for (int i = nsel + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
+    return nsel;
+}
+
+}  // namespace fdl

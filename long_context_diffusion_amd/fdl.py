@@ -1,0 +1,295 @@
+"""Python binding of the C ABI in include/fdl.h (libfdl.so, gfx950).
+
+Argument marshalling only: every step of the sparse attention path runs in the
+library's HIP kernels.  PyTorch provides device memory and the current stream.
+Functions take torch tensors on the GPU, pass their data pointers, sizes and
+element strides to the library, and return output tensors (allocated here when
+the caller passes none).  A missing library, or a status other than FDL_OK,
+raises FdlError: there is no fallback path.
+
+Entry points (same names as the C functions without the fdl_ prefix):
+  pcgi_select, dense_attention, sink_identify, block_score_topc, sparse_attention.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfdl.so")
+
+FDL_F32, FDL_BF16 = 0, 1
+STATUS = {0: "FDL_OK", 1: "FDL_ERR_NULL", 2: "FDL_ERR_SHAPE", 3: "FDL_ERR_DTYPE", 4: "FDL_ERR_ALIGN",
+          5: "FDL_ERR_WORKSPACE", 6: "FDL_ERR_HIP", 7: "FDL_ERR_UNSUPPORTED"}
+EXPORTS = (
+    "fdl_status_string", "fdl_focus_count",
+    "fdl_pcgi_select",
+    "fdl_dense_attention_workspace_bytes", "fdl_dense_attention",
+    "fdl_sink_identify_workspace_bytes", "fdl_sink_identify",
+    "fdl_block_score_topc_workspace_bytes", "fdl_block_score_topc",
+    "fdl_sparse_attention_workspace_bytes", "fdl_sparse_attention",
+)
+
+
+class FdlError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_status_text(status)})")
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("r", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_D = ctypes.c_double
+
+_SIGS = {
+    "fdl_status_string": (ctypes.c_char_p, [_I]),
+    "fdl_focus_count": (_I, [_I, _D]),
+    "fdl_pcgi_select": (_I, [_P, _P, _I, _I, _I, _D, _I, _P, _P, _I, _P, _P, _I, _P]),
+    "fdl_dense_attention_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "fdl_dense_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P, Strides,
+                                 _F, _P, Strides, _P, _P, _SZ, _P]),
+    "fdl_sink_identify_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "fdl_sink_identify": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F, _P, _I,
+                               _P, _P, _P, _SZ, _P]),
+    "fdl_block_score_topc_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "fdl_block_score_topc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
+                                  _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "fdl_sparse_attention_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
+                                  Strides, _P, _I, _P, _I, _I, _F, _P, Strides, _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfdl.so with argument types set; raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FdlError(-1, f"{LIB_PATH} is missing; build it with long_context_diffusion_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return lib().fdl_status_string(status).decode()
+    except Exception:  # library not loadable
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise FdlError(status, what)
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FDL_BF16
+    if t.dtype == torch.float32:
+        return FDL_F32
+    raise FdlError(3, f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides4(t: torch.Tensor) -> Strides:
+    """Element strides of a [B, H, rows, d] tensor whose last axis is contiguous."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise FdlError(2, "expected a [B, H, rows, d] tensor with a contiguous last axis")
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Workspace:
+    """A reusable device byte buffer, grown on demand (allocation outside the library)."""
+
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return ctypes.c_void_p(self.buf.data_ptr()), self.buf.numel()
+
+
+_default_ws = {}
+
+
+def _ws(workspace, device):
+    if workspace is None:
+        key = str(device)
+        if key not in _default_ws:
+            _default_ws[key] = Workspace(device)
+        workspace = _default_ws[key]
+    return workspace
+
+
+def focus_count(n_t: int, rho: float) -> int:
+    return int(lib().fdl_focus_count(int(n_t), float(rho)))
+
+
+# ------------------------------------------------------------------ entry points
+
+def pcgi_select(conf, mask, n_t: int, rho: float, w: int, *, k_cap=None, nq_max=None, out=None,
+                stream=None):
+    """I_focus and I_active (fdl_pcgi_select).  conf [B, L] fp32, mask [B, L] uint8.
+
+    Returns (focus_idx [B, k_cap], n_focus [B], active_idx [B, nq_max], n_active [B]), int32.
+    """
+    B, L = conf.shape
+    k = focus_count(n_t, rho)
+    k_cap = max(k, 1) if k_cap is None else k_cap
+    nq_max = max(min(k * w, L), 1) if nq_max is None else nq_max
+    dev = conf.device
+    if out is None:
+        out = (torch.empty((B, k_cap), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, nq_max), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    focus_idx, n_focus, active_idx, n_active = out
+    st = lib().fdl_pcgi_select(_ptr(conf), _ptr(mask), B, L, int(n_t), float(rho), int(w),
+                               _ptr(focus_idx), _ptr(n_focus), k_cap, _ptr(active_idx), _ptr(n_active),
+                               nq_max, _stream(stream))
+    _check(st, "fdl_pcgi_select")
+    return focus_idx, n_focus, active_idx, n_active
+
+
+def _rows(q, q_idx, n_q, nq_max):
+    if nq_max is None:
+        nq_max = q_idx.shape[1] if q_idx is not None else q.shape[2]
+    return _ptr(q_idx), _ptr(n_q), int(nq_max)
+
+
+def dense_attention_workspace_bytes(dtype_code, B, Hq, Hkv, L, d, nq_max) -> int:
+    return int(lib().fdl_dense_attention_workspace_bytes(dtype_code, B, Hq, Hkv, L, d, nq_max))
+
+
+def dense_attention(q, k, v, *, q_idx=None, n_q=None, nq_max=None, scale: float = 0.0, out=None,
+                    lse=None, want_lse=True, workspace=None, stream=None):
+    """Full attention of the selected query rows over all keys (fdl_dense_attention).
+
+    q [B, Hq, rows, d]; k, v [B, Hkv, L, d].  Returns (o [B, Hq, nq_max, d], lse [B, Hq, nq_max] or None).
+    """
+    B, Hq, _, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, Hq, nq_max, d), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, nq_max), dtype=torch.float32, device=q.device)
+    ws, ws_n = _ws(workspace, q.device).get(dense_attention_workspace_bytes(dt, B, Hq, Hkv, L, d, nq_max))
+    st = lib().fdl_dense_attention(dt, B, Hq, Hkv, L, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
+                                   _ptr(k), _strides4(k), _ptr(v), _strides4(v), float(scale),
+                                   _ptr(out), _strides4(out), _ptr(lse), ws, ws_n, _stream(stream))
+    _check(st, "fdl_dense_attention")
+    return out, lse
+
+
+def sink_identify(q, k, lse, n_sinks: int, *, q_idx=None, n_q=None, nq_max=None, scale: float = 0.0,
+                  out=None, scores=None, want_scores=False, workspace=None, stream=None):
+    """Attention-sink positions at layer l_dense (fdl_sink_identify).
+
+    Returns (sink_idx [B, n_sinks] int32, scores [B, L] fp32 or None).
+    """
+    B, Hq, _, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, max(n_sinks, 1)), dtype=torch.int32, device=q.device)
+    if scores is None and want_scores:
+        scores = torch.empty((B, L), dtype=torch.float32, device=q.device)
+    nbytes = int(lib().fdl_sink_identify_workspace_bytes(dt, B, Hq, Hkv, L, d, nq_max))
+    ws, ws_n = _ws(workspace, q.device).get(nbytes)
+    st = lib().fdl_sink_identify(dt, B, Hq, Hkv, L, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
+                                 _ptr(k), _strides4(k), float(scale), _ptr(lse), int(n_sinks),
+                                 _ptr(out), _ptr(scores), ws, ws_n, _stream(stream))
+    _check(st, "fdl_sink_identify")
+    return out[:, :n_sinks], scores
+
+
+def block_score_topc(q, k, P: int, bs: int, C: int, *, q_idx=None, n_q=None, nq_max=None,
+                     scale: float = 0.0, out=None, want_R=False, want_kbar=False, workspace=None,
+                     stream=None):
+    """Top-C prompt blocks by relevance to the active queries (fdl_block_score_topc).
+
+    Returns (block_idx [B, C] int32, R [B, nb] fp64 or None, kbar [B, Hkv, nb, d] fp32 or None).
+    """
+    B, Hq, _, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
+    dt = _dtype_code(q)
+    nb = -(-P // bs)
+    if out is None:
+        out = torch.empty((B, max(C, 1)), dtype=torch.int32, device=q.device)
+    R = torch.empty((B, nb), dtype=torch.float64, device=q.device) if want_R else None
+    kbar = torch.empty((B, Hkv, nb, d), dtype=torch.float32, device=q.device) if want_kbar else None
+    nbytes = int(lib().fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs))
+    ws, ws_n = _ws(workspace, q.device).get(nbytes)
+    st = lib().fdl_block_score_topc(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
+                                    _ptr(k), _strides4(k), float(scale), int(bs), int(C), _ptr(out),
+                                    _ptr(R), _ptr(kbar), ws, ws_n, _stream(stream))
+    _check(st, "fdl_block_score_topc")
+    return out[:, :C], R, kbar
+
+
+def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, q_idx=None, n_q=None,
+                     nq_max=None, scale: float = 0.0, out=None, lse=None, want_lse=False,
+                     workspace=None, stream=None):
+    """Attention of the active queries over I_p only (fdl_sparse_attention).
+
+    sink_idx [B, n_sinks] and block_idx [B, C] int32 (ascending, -1 padded) or None.
+    Returns (o [B, Hq, nq_max, d], lse or None).
+    """
+    B, Hq, _, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
+    dt = _dtype_code(q)
+    n_sinks = 0 if sink_idx is None else sink_idx.shape[1]
+    C = 0 if block_idx is None else block_idx.shape[1]
+    if sink_idx is not None and sink_idx.stride(1) != 1 or (block_idx is not None and block_idx.stride(1) != 1):
+        raise FdlError(2, "index tensors must be contiguous along their last axis")
+    if sink_idx is not None and n_sinks and sink_idx.stride(0) != n_sinks:
+        sink_idx = sink_idx.contiguous()
+    if block_idx is not None and C and block_idx.stride(0) != C:
+        block_idx = block_idx.contiguous()
+    if out is None:
+        out = torch.empty((B, Hq, nq_max, d), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, nq_max), dtype=torch.float32, device=q.device)
+    nbytes = int(lib().fdl_sparse_attention_workspace_bytes(dt, B, Hq, Hkv, L, P, d, nq_max, n_sinks, C, bs))
+    ws, ws_n = _ws(workspace, q.device).get(nbytes)
+    st = lib().fdl_sparse_attention(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
+                                    _ptr(k), _strides4(k), _ptr(v), _strides4(v), _ptr(sink_idx), n_sinks,
+                                    _ptr(block_idx), C, int(bs), float(scale), _ptr(out), _strides4(out),
+                                    _ptr(lse), ws, ws_n, _stream(stream))
+    _check(st, "fdl_sparse_attention")
+    return out, lse

@@ -1,0 +1,153 @@
+"""The C ABI on the host: exports, status strings, workspace sizes and argument validation.
+
+Nothing here launches a kernel: every call below is rejected by host-side
+validation before any HIP call, or is a pure host query.  Pointers passed are
+fake, aligned (or deliberately misaligned) integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_diffusion_amd import fdl as F
+from oracle import focus_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fdl.h")
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+NULL = None
+S = F.Strides
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fdl_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = F.lib()
+    names = declared_functions()
+    assert len(names) == 11, names
+    assert sorted(F.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(8):
+        s = F.lib().fdl_status_string(code)
+        assert s and len(s) > 1
+    assert F.lib().fdl_status_string(0) == b"ok"
+
+
+@pytest.mark.parametrize("n_t,rho", [(4, 2.0), (3, 2.5), (16, 4.0), (0, 4.0), (5, 0.1), (10, 0.3),
+                                      (7, 1.0 / 3.0), (1000, 0.999)])
+def test_focus_count_matches_oracle(n_t, rho):
+    assert F.focus_count(n_t, rho) == O.focus_count(n_t, rho)
+
+
+def test_focus_count_rejects_negative():
+    assert F.focus_count(-1, 2.0) == 0
+    assert F.focus_count(3, -1.0) == 0
+
+
+def test_workspace_sizes():
+    lib = F.lib()
+    # the block-entry refresh has enough query tiles: no key split, no workspace
+    assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 32768) == 0
+    # dense attention of <= 1024 active rows splits the 32K keys: partials in the workspace
+    n = lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024)
+    assert n > 0 and n % ((128 + 2) * 4) == 0
+    assert lib.fdl_sparse_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128,
+                                                     1024, 16, 64, 128) > 0
+    assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024) == \
+        (32 * 32768 + 32768) * 4
+    nb = 252
+    assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32256, 128, 128) == \
+        (32 * 128 + 32 * nb + nb) * 8
+    # invalid shapes report 0
+    assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 5, 1024, 128, 64) == 0
+    assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 4, 4, 0, 64, 64) == 0
+
+
+def _pcgi(**kw):
+    args = dict(conf=FAKE, mask=FAKE, B=1, L=2048, n_t=4, rho=2.0, w=8, focus=FAKE, n_focus=FAKE,
+                k_cap=8, active=FAKE, n_active=FAKE, nq_max=64)
+    args.update(kw)
+    return F.lib().fdl_pcgi_select(args["conf"], args["mask"], args["B"], args["L"], args["n_t"],
+                                   args["rho"], args["w"], args["focus"], args["n_focus"], args["k_cap"],
+                                   args["active"], args["n_active"], args["nq_max"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(conf=NULL), 1), (dict(active=NULL), 1), (dict(n_focus=NULL), 1),
+    (dict(B=0), 2), (dict(L=0), 2), (dict(w=0), 2), (dict(n_t=-1), 2), (dict(rho=float("nan")), 2),
+    (dict(rho=-1.0), 2), (dict(rho=float("inf")), 2),
+    (dict(k_cap=7), 2),            # k = 8 needs k_cap >= 8
+    (dict(nq_max=63), 2),          # k*w = 64 active positions at most
+])
+def test_pcgi_validation(kw, status):
+    assert _pcgi(**kw) == status
+
+
+def _dense(**kw):
+    a = dict(dt=F.FDL_BF16, B=1, Hq=4, Hkv=4, L=256, d=128, q=FAKE, qs=S(4 * 256 * 128, 256 * 128, 128),
+             q_idx=NULL, n_q=NULL, nq_max=256, k=FAKE, ks=S(4 * 256 * 128, 256 * 128, 128), v=FAKE,
+             vs=S(4 * 256 * 128, 256 * 128, 128), scale=0.0, o=FAKE, os=S(4 * 256 * 128, 256 * 128, 128),
+             lse=NULL, ws=NULL, ws_bytes=0)
+    a.update(kw)
+    return F.lib().fdl_dense_attention(a["dt"], a["B"], a["Hq"], a["Hkv"], a["L"], a["d"], a["q"], a["qs"],
+                                       a["q_idx"], a["n_q"], a["nq_max"], a["k"], a["ks"], a["v"], a["vs"],
+                                       a["scale"], a["o"], a["os"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(k=NULL), 1), (dict(v=NULL), 1), (dict(o=NULL), 1),
+    (dict(dt=2), 3), (dict(dt=-1), 3),
+    (dict(d=96), 7), (dict(d=256), 7),
+    (dict(Hkv=3), 2), (dict(B=0), 2), (dict(L=0), 2), (dict(nq_max=-1), 2),
+    (dict(q=MISALIGNED), 4), (dict(ks=S(4 * 256 * 128, 256 * 128, 132)), 4),
+    (dict(qs=S(4 * 256 * 128, 256 * 128, 64)), 2),       # rows overlap: |row stride| < d
+    (dict(nq_max=16, L=4096), 5),                        # few rows -> key split needs a workspace
+    (dict(nq_max=16, L=4096, ws=FAKE, ws_bytes=64), 5),
+    (dict(nq_max=16, L=4096, ws=MISALIGNED, ws_bytes=1 << 30), 4),
+    (dict(nq_max=0), 0),                                 # nothing to compute
+])
+def test_dense_validation(kw, status):
+    if status == 5 or status == 4 and "ws" in kw:
+        # these rows must reach the workspace check, i.e. the plan really splits the keys
+        assert F.lib().fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 4, 4, kw["L"], 128, 16) > 0
+    assert _dense(**kw) == status
+
+
+def test_sparse_and_sink_and_block_validation():
+    lib = F.lib()
+    st = S(4 * 256 * 128, 256 * 128, 128)
+    # sparse: too many sinks for the kernel's LDS bitmask
+    assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
+                                    FAKE, st, FAKE, 5000, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0,
+                                    None) == 7
+    # sparse: P > L, bs < 1, block list missing
+    assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 300, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
+                                    FAKE, st, FAKE, 4, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
+    assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
+                                    FAKE, st, FAKE, 4, FAKE, 2, 0, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
+    assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
+                                    FAKE, st, FAKE, 4, NULL, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 1
+    # sinks: lse and output required, n_sinks within [0, L], workspace
+    assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
+                                 NULL, 4, FAKE, NULL, FAKE, 1 << 20, None) == 1
+    assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
+                                 FAKE, 257, FAKE, NULL, FAKE, 1 << 20, None) == 2
+    assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
+                                 FAKE, 4, FAKE, NULL, FAKE, 16, None) == 5
+    # blocks: P outside [1, L], C < 0, workspace too small
+    for P, bs, C, ws_bytes, status in [(0, 64, 4, 1 << 20, 2), (257, 64, 4, 1 << 20, 2),
+                                       (192, 0, 4, 1 << 20, 2), (192, 64, -1, 1 << 20, 2),
+                                       (192, 64, 4, 8, 5)]:
+        assert lib.fdl_block_score_topc(F.FDL_BF16, 1, 4, 4, 256, P, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
+                                        0.0, bs, C, FAKE, NULL, NULL, FAKE, ws_bytes, None) == status
