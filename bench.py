@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Benchmark of the Focus-dLLM sparse attention step on one MI355X (gfx950).
+
+Workload (the 32K-context, 32-layer LLaDA-8B-shaped stack): 32 query and 32 KV
+heads, head dim 128, bf16; 32256 prompt + 512 generation tokens with 256 still
+masked; n(t) = 16, rho = 2 (k = 32), window w = 32, blocks of 128 keys, top-C = 64,
+16 sinks identified at layer l_dense = 2 and reused by layers 3..32.
+
+One step = PCGI + 2 dense layers on the active rows (+ log-sum-exp) + sink
+identification + 30 x (block top-C + sparse attention), every part in
+libfdl.so's HIP kernels.  Q, K and V of all 32 layers, the confidence and the
+mask are drawn once (seeded, synthetic) and stay resident in HBM; the timed
+region replays the captured step K times between two HIP events.
+
+Printed: one JSON line.  value = algorithmic HBM bytes of the step / step time
+(GB/s); ms_per_step = step time.  Extra fields: per-stage breakdown from events
+recorded around every entry-point call of K timed eager steps, the roofline of
+the dominant entry point, the block-entry dense refresh of one layer (TFLOP/s), and
+the fp64 oracle timed on the host cores on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+METRIC = "sparse-attn step µs + achieved HBM GB/s (% peak) at 32K ctx, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-refresh", action="store_true", help="skip the dense-refresh measurement")
+    ap.add_argument("--refresh-reps", type=int, default=3)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ accounting
+
+def step_accounting(wl, n_active, sinks, blocks_per_layer):
+    """Algorithmic HBM bytes and flops of every stage of one step (realised sets)."""
+    E = 2  # bf16
+    d, Hq, Hkv, L, P = wl.d, wl.Hq, wl.Hkv, wl.L, wl.P
+    na = int(n_active)
+    q_rows = Hq * na * d * E
+    acc = {}
+    acc["pcgi"] = dict(bytes=L * 5 + na * 4, flops=0, calls=1)
+    kv_all = 2 * Hkv * L * d * E
+    acc["dense"] = dict(bytes=wl.l_dense * (kv_all + 2 * q_rows + Hq * na * 4),
+                        flops=wl.l_dense * 4 * na * L * d * Hq, calls=wl.l_dense)
+    acc["sinks"] = dict(bytes=Hkv * L * d * E + q_rows + Hq * na * 4 + L * 4,
+                        flops=2 * na * L * d * Hq, calls=1)
+    n_sparse = wl.layers - wl.l_dense
+    scan = Hkv * P * d * E
+    sb, sf, kb, kf = 0, 0, 0, 0
+    snk = set(int(s) for s in sinks if s >= 0)
+    for blocks in blocks_per_layer:
+        sel = [int(b) for b in blocks if b >= 0]
+        blk_keys = sum(min(wl.bs, P - b * wl.bs) for b in sel)
+        covered = set(b for b in sel)
+        extra = sum(1 for s in snk if s < P and s // wl.bs not in covered)
+        n_keys = blk_keys + (L - P) + extra
+        kb += scan + q_rows + len(sel) * 4
+        kf += 2 * Hq * na * d
+        sb += 2 * Hkv * n_keys * d * E + 2 * q_rows
+        sf += 4 * na * n_keys * d * Hq
+    acc["blocks"] = dict(bytes=kb, flops=kf, calls=n_sparse)
+    acc["sparse"] = dict(bytes=sb, flops=sf, calls=n_sparse)
+    return acc
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=0.25):
+    """The fp64 oracle on a bounded sample of the step, timed on the host cores."""
+    import numpy as np
+    from oracle import focus_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing
+        threads = 1
+    t = {}
+    t0 = time.perf_counter()
+    focus = O.pcgi_focus(conf[0], mask[0], wl.k)
+    active = O.window_active(focus, wl.w, wl.L)
+    t["pcgi"] = time.perf_counter() - t0
+    na = len(active)
+    sub = active[: max(1, int(round(na * rows_frac)))]
+    scale_rows = na / len(sub)
+    Q, K, V = layer_host(wl.l_dense - 1)
+    t0 = time.perf_counter()
+    _, lse = O.dense_attention(Q[:, sub], K, V, wl.scale)
+    t["dense_layer"] = (time.perf_counter() - t0) * scale_rows
+    t0 = time.perf_counter()
+    O.sink_scores(Q[:, sub], K, lse, wl.scale)
+    t["sinks"] = (time.perf_counter() - t0) * scale_rows
+    sinks = synth_sinks = None
+    sparse_times = []
+    for l in (wl.l_dense, wl.layers - 1):
+        Q, K, V = layer_host(l)
+        t0 = time.perf_counter()
+        R = O.block_relevance(Q[:, active], O.block_means(K, wl.P, wl.bs), wl.scale)
+        blocks = O.top_blocks(R, wl.C)
+        if sinks is None:
+            from workloads import synth
+            synth_sinks = synth.sink_positions(wl, 0)
+            sinks = synth_sinks
+        I_p = O.key_set(sinks, blocks, wl.bs, wl.P, wl.L)
+        O.sparse_attention(Q[:, active], K, V, I_p, wl.scale)
+        sparse_times.append(time.perf_counter() - t0)
+    t["sparse_layer"] = float(np.mean(sparse_times))
+    step_s = (t["pcgi"] + wl.l_dense * t["dense_layer"] + t["sinks"] +
+              (wl.layers - wl.l_dense) * t["sparse_layer"])
+    measured = t["pcgi"] + t["dense_layer"] / scale_rows + t["sinks"] / scale_rows + sum(sparse_times)
+    return {
+        "value": step_bytes / step_s / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "step_s_extrapolated": step_s,
+        "measured_s": measured,
+        "sample": (f"fp64 NumPy oracle on host: PCGI; layer {wl.l_dense} dense attention and sink scores "
+                   f"on {len(sub)} of {na} active rows (scaled x{scale_rows:.2f}); block top-C + sparse "
+                   f"attention of layers {wl.l_dense + 1} and {wl.layers} on all rows (mean x "
+                   f"{wl.layers - wl.l_dense}); dense layers x{wl.l_dense}; sinks taken as the injected "
+                   f"positions; extrapolated to one full step"),
+        "stage_s": {k: round(v, 4) for k, v in t.items()},
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "reps": 5}))
+        return
+
+    import long_context_diffusion_amd as F
+    from long_context_diffusion_amd.step import StepRunner
+    from workloads import configs, synth
+
+    wl = configs.CTX32K_STACK
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    F.fdl.lib()
+    t_setup = time.time()
+    conf_np, mask_np = synth.step_inputs(wl)
+    conf = torch.from_numpy(conf_np).to(dev)
+    mask = torch.from_numpy(mask_np).to(dev)
+    qs, ks, vs = [], [], []
+    for l in range(wl.layers):
+        k, v = synth.make_kv(wl, l, dev)
+        ks.append(k)
+        vs.append(v)
+        qs.append(synth.make_q(wl, l, 0, dev))
+    torch.cuda.synchronize()
+    print(f"# inputs resident: {wl.layers} layers, {sum(t.numel() * 2 for t in qs + ks + vs) / 2**30:.1f} GiB "
+          f"in {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    run = StepRunner(B=wl.B, L=wl.L, P=wl.P, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, dtype=torch.bfloat16,
+                     n_t=wl.n_t, rho=wl.rho, w=wl.w, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
+                     layers=wl.layers, l_dense=wl.l_dense, scale=wl.scale, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(hooks=None):
+        run.sparse_step(conf, mask, qs, ks, vs, hooks=hooks)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+
+    # sanity: the injected sinks are found (a cheap guard; the parity tests check everything)
+    sinks_found = sorted(run.sinks[0, : wl.n_sinks].cpu().tolist())
+    if sinks_found != sorted(synth.sink_positions(wl, 0).tolist()):
+        print(f"# warning: sinks {sinks_found} differ from the injected positions", file=sys.stderr)
+
+    # stage events: one pair around every entry-point call
+    stage_events = {}
+
+    def make_hooks():
+        hooks = {}
+        for name in ("pcgi", "dense", "sinks", "blocks", "sparse"):
+            def before(name=name):
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                stage_events.setdefault(name, []).append(ev)
+                ev[0].record(stream)
+
+            def after(name=name):
+                stage_events[name][-1][1].record(stream)
+            hooks[name] = (before, after)
+        return hooks
+
+    # eager steps with per-call events (kernel durations of every entry point)
+    hooks = make_hooks()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(hooks)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+
+    mode = args.mode
+    if mode == "graph":
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+        except Exception as exc:  # capture unsupported: report eager numbers
+            print(f"# graph capture failed ({exc}); timing eager steps", file=sys.stderr)
+            mode = "eager"
+    if mode == "graph":
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+    else:
+        ms = eager_ms
+
+    nsteps = max(args.steps, 1)
+    stage_ms = {k: [a.elapsed_time(b) / nsteps for a, b in v] for k, v in stage_events.items()}
+    n_active = int(run.n_active[0])
+    sinks = run.sinks[0, : wl.n_sinks].cpu().numpy()
+    blocks = [run.blocks[l][0, : wl.C].cpu().numpy() for l in range(wl.l_dense, wl.layers)]
+    acc = step_accounting(wl, n_active, sinks, blocks)
+    step_bytes = sum(a["bytes"] for a in acc.values())
+    step_flops = sum(a["flops"] for a in acc.values())
+    breakdown = {}
+    for name, a in acc.items():
+        times = stage_ms.get(name, [])
+        tot = sum(times)              # per step (averaged over the timed eager steps)
+        calls = len(times) // nsteps
+        breakdown[name] = {
+            "calls": calls, "ms_total": round(tot, 4),
+            "us_per_call": round(1000 * tot / max(calls, 1), 2),
+            "GBps": round(a["bytes"] / (tot / 1000) / 1e9, 1) if tot else None,
+            "TFLOPps": round(a["flops"] / (tot / 1000) / 1e12, 1) if tot and a["flops"] else None,
+        }
+    # the dominant entry point: largest share of the step
+    dom = max(breakdown, key=lambda n: breakdown[n]["ms_total"])
+    a = acc[dom]
+    per_call_s = breakdown[dom]["ms_total"] / 1000 / max(breakdown[dom]["calls"], 1)
+    bytes_call = a["bytes"] / a["calls"]
+    flops_call = a["flops"] / a["calls"]
+    t_hbm = bytes_call / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_call / (BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        achieved = flops_call / per_call_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = bytes_call / per_call_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": dom, "traffic": None, "us_per_launch": round(per_call_s * 1e6, 2),
+                 "algorithmic_bytes_per_launch": int(bytes_call), "algorithmic_flops_per_launch": int(flops_call)})
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms / 1000) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.L, "prompt": wl.P, "gen": wl.G,
+                   "masked": wl.masked, "heads_q_kv": [wl.Hq, wl.Hkv], "head_dim": wl.d, "layers": wl.layers,
+                   "l_dense": wl.l_dense, "k": wl.k, "w": wl.w, "block": wl.bs, "top_c": wl.C,
+                   "n_sinks": wl.n_sinks, "parallelism": "single GPU"},
+        "step_us": round(ms * 1000, 1),
+        "pct_hbm_peak": round(100 * step_bytes / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 2),
+        "timing": mode,
+        "eager_ms_per_step_with_call_events": round(eager_ms, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "step_algorithmic_flops": int(step_flops),
+        "n_active": n_active,
+        "breakdown": breakdown,
+        "roofline": roof,
+    }
+
+    if not args.no_refresh:
+        # block-entry refresh of one layer: all 32768 rows attend to all keys
+        out = torch.empty_like(qs[0])
+        F.dense_attention(qs[0], ks[0], vs[0], out=out, want_lse=False, scale=wl.scale)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.refresh_reps):
+            F.dense_attention(qs[0], ks[0], vs[0], out=out, want_lse=False, scale=wl.scale)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / args.refresh_reps
+        rflops = 4.0 * wl.L * wl.L * wl.d * wl.Hq
+        result["dense_refresh"] = {"ms_per_layer": round(rms, 3),
+                                   "TFLOPps": round(rflops / (rms / 1000) / 1e12, 1),
+                                   "frac_bf16_peak": round(rflops / (rms / 1000) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                   "flops_per_layer": rflops}
+        del out
+
+    if not args.no_cpu_baseline:
+        def layer_host(l):
+            return (synth.to_f64(qs[l])[0], synth.to_f64(ks[l])[0], synth.to_f64(vs[l])[0])
+        result["cpu_baseline"] = cpu_baseline(wl, conf_np, mask_np, layer_host, step_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,8 +10,6 @@ using namespace fdl;
 
 namespace {
 
-constexpr int kMaxSparseSinks = 4096;  // LDS bitmask of the sparse attention kernel
-
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline size_t elem_size(fdl_dtype dt) { return dt == FDL_BF16 ? 2 : 4; }
@@ -114,7 +112,7 @@ fdl_status fdl_pcgi_select(const float* conf, const uint8_t* mask, int B, int L,
 size_t fdl_dense_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d,
                                            int nq_max) {
     if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 1) return 0;
-    return plan_attention(dt, B, Hq, Hkv, d, nq_max, L).ws_bytes;
+    return plan_attention(dt, B, Hq, Hkv, d, nq_max, L, false).ws_bytes;
 }
 
 fdl_status fdl_dense_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, const void* q,
@@ -130,7 +128,7 @@ fdl_status fdl_dense_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int 
     if ((st = check_tensor(v, vs, dt, d)) != FDL_OK) return st;
     if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
     if (nq_max == 0) return FDL_OK;
-    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, L);
+    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, L, false);
     if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
     AttnArgs a = attn_args(dt, B, Hq, Hkv, L, L, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, scale, d, o, os,
                            lse, ws);
@@ -201,7 +199,7 @@ size_t fdl_sparse_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv
     if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 1 || bs < 1 || P < 0 || P > L ||
         C < 0 || n_sinks < 0)
         return 0;
-    return plan_attention(dt, B, Hq, Hkv, d, nq_max, sparse_key_bound(L, P, n_sinks, C, bs)).ws_bytes;
+    return plan_attention(dt, B, Hq, Hkv, d, nq_max, sparse_key_bound(L, P, n_sinks, C, bs), true).ws_bytes;
 }
 
 fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
@@ -219,10 +217,10 @@ fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
     if (P < 0 || P > L || bs < 1 || C < 0 || n_sinks < 0) return FDL_ERR_SHAPE;
     if ((n_sinks > 0 && !sink_idx) || (C > 0 && !block_idx)) return FDL_ERR_NULL;
-    if (n_sinks > kMaxSparseSinks) return FDL_ERR_UNSUPPORTED;
-    if (nq_max == 0) return FDL_OK;
     const int64_t bound = sparse_key_bound(L, P, n_sinks, C, bs);
-    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, bound);
+    if (bound > (1ll << 30)) return FDL_ERR_SHAPE;
+    if (nq_max == 0) return FDL_OK;
+    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, bound, true);
     if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
     AttnArgs a = attn_args(dt, B, Hq, Hkv, L, P, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, scale, d, o, os,
                            lse, ws);

@@ -25,16 +25,20 @@ struct AttnArgs {
     int n_sinks;
     const int32_t* block_idx;
     int C, bs, nb;
-    int n_splits;          // key-range splits; > 1 writes partials merged by attn_merge
+    int n_splits;          // key-range splits; > 1: partials combined by attn_merge
     int tiles_per_split;   // key tiles per split
     int q_tiles;           // query tiles per (sequence, KV head)
+    int key_cap;           // row stride of kv_list (upper bound on |I_p|)
+    int32_t* kv_list;      // [B, key_cap] keys of I_p (sparse), built by attn_prep
+    int32_t* n_keys;       // [B] |I_p| (sparse)
     float* part_o;         // [B*Hq*nq_max][n_splits][d] unnormalised outputs
     float* part_ml;        // [B*Hq*nq_max][n_splits][2] running max (log2 domain) and sum
 };
 
 struct AttnPlan {
     int q_tiles, n_splits, tiles_per_split, tile_keys, rows_per_tile;
-    size_t ws_bytes;
+    int64_t key_cap;
+    size_t list_bytes, part_bytes, ws_bytes;
 };
 
 // Upper bound on |I_p| (keys attended by one sequence).
@@ -47,7 +51,7 @@ inline int64_t sparse_key_bound(int L, int P, int n_sinks, int C, int bs) {
 }
 
 AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_max,
-                        int64_t key_bound);
+                        int64_t key_bound, bool sparse);
 
 hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args, const AttnPlan& plan,
                             hipStream_t stream);

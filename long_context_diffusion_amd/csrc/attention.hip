@@ -5,6 +5,10 @@
 // (step (3)); sparse attention over I_p = sinks U selected prompt blocks U the
 // generation region (step (5)).  softmax(q k^T * scale) v with no mask.
 //
+// attn_prep (one workgroup per sequence) writes the keys of I_p as a compact
+// list (selected blocks, then [P, L), then the sinks that neither a selected
+// block nor the generation region already holds).
+//
 // bf16 path (gfx950 MFMA, v_mfma_f32_32x32x16_bf16), per workgroup of 4 waves:
 //   * 128 query rows of one KV head.  Query heads sharing the KV head are
 //     interleaved into the rows (packed row p -> head g*Gq + p % Gq, logical
@@ -16,17 +20,17 @@
 //   * O^T = V^T P^T: V is transposed while it is staged into LDS so the MFMA
 //     A operand is two 8-byte LDS reads; the key order inside a 16-key MFMA
 //     chunk follows the accumulator layout of S^T, so P needs no shuffle.
-//   * 64-key tiles of K and V^T are double-buffered in LDS (68 KB), with one
-//     barrier per tile; global loads for tile t+1 are in flight while tile t
-//     is computed.  Rows of LDS are padded so MFMA operand reads are
-//     bank-conflict free.
+//   * 64-key tiles of K and V^T are double-buffered in LDS (68 KB), one barrier
+//     per tile; global loads of tile t+1 are in flight while tile t is
+//     computed.  Sparse key indices come from the list two tiles ahead, through
+//     LDS, so no load waits on another inside the loop.  LDS rows are padded so
+//     MFMA operand reads are bank-conflict free.
 //   * Small query sets (the active rows of a sparse step) split the key range
-//     over several workgroups; attn_merge combines the partial results with
-//     their running max and sum.
-// Sparse key sets are never materialised: key position t of I_p maps to the
-// (t / bs)-th selected block, the generation region or the sink list, and a
-// sink already covered by a selected block or by [P, L) is masked out, so each
-// key is attended once.
+//     over several workgroups; attn_merge then combines the partial results
+//     of every output row in split order (one wave per row).  A merge inside
+//     the last-finishing split would need a device-scope release per
+//     workgroup, which on gfx950 writes back the XCD's L2: far dearer than
+//     one more launch.
 //
 // fp32 path: the same decomposition on the vector ALU (one wave, one row per
 // lane, 32-key tiles in LDS), for fp32 inputs.
@@ -39,100 +43,113 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of differences never sees inf-inf
-constexpr int kMaxSinkWords = 128;    // n_sinks <= 4096
 
-// Positions of I_p for one sequence: [0, n_blk) selected blocks, [n_blk, sink0)
-// the generation region, [sink0, n_keys) the sink list (some entries masked).
-struct KeyMap {
-    int n_blk, sink0, n_keys;
-};
+// ------------------------------------------------------------------ key list
 
-// Builds the key map of sequence b and the per-sink "attend" bits in LDS.
-__device__ KeyMap build_key_map(const AttnArgs& a, int b, uint32_t* s_sink_ok, int* s_tmp) {
-    KeyMap km;
-    if (!a.sparse) {
-        km.n_blk = 0;
-        km.sink0 = a.L;
-        km.n_keys = a.L;
-        return km;
+template <typename T>
+__global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d) {
+    __shared__ int s_tmp[17];
+    __shared__ int s_carry;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (blockIdx.y > 0) {
+        // padding rows r in [n_q[b], nq_max) of every query head: O = 0, lse = -inf
+        // (only without a key split: the split merge writes them otherwise)
+        if (!a.n_q || a.n_splits > 1) return;
+        const int nq = a.n_q[b];
+        const int64_t pad_rows = static_cast<int64_t>(a.Hq) * (a.nq_max - nq);
+        const int c4n = d / 4;
+        const int64_t items = pad_rows * c4n;
+        for (int64_t it = static_cast<int64_t>(blockIdx.y - 1) * blockDim.x + tid; it < items;
+             it += static_cast<int64_t>(gridDim.y - 1) * blockDim.x) {
+            const int64_t row = it / c4n;
+            const int c4 = static_cast<int>(it % c4n);
+            const int h = static_cast<int>(row / (a.nq_max - nq));
+            const int r = nq + static_cast<int>(row % (a.nq_max - nq));
+            T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr + 4 * c4;
+            for (int e = 0; e < 4; ++e) orow[e] = T(0);
+            if (a.lse && c4 == 0) a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] = -INFINITY;
+        }
+        return;
     }
+    if (!a.sparse) return;
     const int32_t* blk = a.block_idx + static_cast<int64_t>(b) * a.C;
     int cnt = 0;
-    for (int c = threadIdx.x; c < a.C; c += blockDim.x) cnt += blk[c] >= 0 ? 1 : 0;
+    for (int c = tid; c < a.C; c += blockDim.x) cnt += blk[c] >= 0 ? 1 : 0;
     int n_sel;
     block_exclusive_sum(cnt, s_tmp, &n_sel);
+    n_sel = min(n_sel, a.nb);
     int n_blk = n_sel * a.bs;
     if (n_sel > 0 && blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;  // short last block
-    for (int i = threadIdx.x; i < kMaxSinkWords; i += blockDim.x) s_sink_ok[i] = 0;
+    int32_t* list = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
+    for (int pos = tid; pos < n_blk; pos += blockDim.x) {
+        const int c = pos / a.bs;
+        // block ids come from fdl_block_score_topc; clamping keeps a malformed list in bounds
+        list[pos] = min(max(blk[c] * a.bs + (pos - c * a.bs), 0), a.L - 1);
+    }
+    const int G = a.L - a.P;
+    for (int i = tid; i < G; i += blockDim.x) list[n_blk + i] = a.P + i;
+    if (tid == 0) s_carry = 0;
     __syncthreads();
     const int32_t* snk = a.sink_idx + static_cast<int64_t>(b) * a.n_sinks;
-    for (int s = threadIdx.x; s < a.n_sinks; s += blockDim.x) {
-        const int j = snk[s];
-        bool attend = j >= 0 && j < a.P;
-        if (attend) {  // covered by a selected block?  (blocks ascending)
-            const int target = j / a.bs;
-            int lo = 0, hi = n_sel;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (blk[mid] < target) lo = mid + 1; else hi = mid;
+    for (int s0 = 0; s0 < a.n_sinks; s0 += blockDim.x) {
+        const int s = s0 + tid;
+        int j = -1;
+        bool take = false;
+        if (s < a.n_sinks) {
+            j = snk[s];
+            take = j >= 0 && j < a.P && (s == 0 || snk[s - 1] != j);
+            if (take) {  // already in a selected block?  (selected blocks ascend)
+                const int target = j / a.bs;
+                int lo = 0, hi = n_sel;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (blk[mid] < target) lo = mid + 1; else hi = mid;
+                }
+                take = !(lo < n_sel && blk[lo] == target);
             }
-            if (lo < n_sel && blk[lo] == target) attend = false;
         }
-        if (attend) atomicOr(&s_sink_ok[s >> 5], 1u << (s & 31));
+        int total;
+        const int off = block_exclusive_sum(take ? 1 : 0, s_tmp, &total) + s_carry;
+        if (take) list[n_blk + G + off] = j;
+        __syncthreads();
+        if (tid == 0) s_carry += total;
+        __syncthreads();
     }
-    __syncthreads();
-    km.n_blk = n_blk;
-    km.sink0 = n_blk + (a.L - a.P);
-    km.n_keys = km.sink0 + a.n_sinks;
-    return km;
+    if (tid == 0) a.n_keys[b] = n_blk + G + s_carry;
 }
 
-// Key index of position t of the key set; *ok is false for masked or out-of-range positions.
-__device__ __forceinline__ int key_at(const AttnArgs& a, const KeyMap& km, int b, int t,
-                                      const uint32_t* s_sink_ok, bool* ok) {
-    if (!a.sparse) {
-        *ok = t < a.L;
-        return *ok ? t : 0;
-    }
-    if (t < km.n_blk) {
-        const int c = t / a.bs;
-        *ok = true;
-        return a.block_idx[static_cast<int64_t>(b) * a.C + c] * a.bs + (t - c * a.bs);
-    }
-    if (t < km.sink0) {
-        *ok = true;
-        return a.P + (t - km.n_blk);
-    }
-    if (t < km.n_keys) {
-        const int s = t - km.sink0;
-        *ok = (s_sink_ok[s >> 5] >> (s & 31)) & 1u;
-        return *ok ? a.sink_idx[static_cast<int64_t>(b) * a.n_sinks + s] : 0;
-    }
-    *ok = false;
-    return 0;
-}
-
-__device__ __forceinline__ bool key_attended(const AttnArgs& a, const KeyMap& km, int t,
-                                             const uint32_t* s_sink_ok) {
-    if (t >= km.n_keys) return false;
-    if (!a.sparse || t < km.sink0) return true;
-    const int s = t - km.sink0;
-    return (s_sink_ok[s >> 5] >> (s & 31)) & 1u;
-}
-
-// Decodes the 1-D grid: q-tile fastest, then split, then KV head, then sequence.
+// Work units are (sequence b, KV head g, key split, query tile qt).  Only query tiles
+// that hold valid rows (from the device-side row counts) get a workgroup; the rest
+// of the grid exits at once.  A workgroup goes to XCD (blockIdx.x mod 8), so the
+// units are laid out such that all query tiles of one (b, g, split) group run on the
+// same XCD, one after another, and share that group's K/V tiles through its L2.
 struct WorkUnit {
     int qt, split, g, b;
+    bool valid;
 };
-__device__ __forceinline__ WorkUnit decode_unit(const AttnArgs& a) {
+__device__ __forceinline__ WorkUnit decode_unit(const AttnArgs& a, int rows_per_tile) {
     WorkUnit u;
-    int id = blockIdx.x;
-    u.qt = id % a.q_tiles;
-    id /= a.q_tiles;
-    u.split = id % a.n_splits;
-    id /= a.n_splits;
-    u.g = id % a.Hkv;
-    u.b = id / a.Hkv;
+    u.valid = false;
+    u.qt = u.split = u.g = u.b = 0;
+    // query tiles with valid rows, per sequence (the same bound for every group of b)
+    int nqt_max = 0;
+    for (int b = 0; b < a.B; ++b) {
+        const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+        nqt_max = max(nqt_max, (a.Gq * nq + rows_per_tile - 1) / rows_per_tile);
+    }
+    if (nqt_max == 0) return u;
+    const int n_groups = a.B * a.Hkv * a.n_splits;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int grp = (slot / nqt_max) * 8 + xcd;
+    if (grp >= n_groups) return u;
+    u.qt = slot % nqt_max;
+    u.split = grp % a.n_splits;
+    u.g = (grp / a.n_splits) % a.Hkv;
+    u.b = grp / (a.n_splits * a.Hkv);
+    const int nq = a.n_q ? a.n_q[u.b] : a.nq_max;
+    u.valid = u.qt * rows_per_tile < a.Gq * nq;
     return u;
 }
 
@@ -143,9 +160,50 @@ __device__ __forceinline__ void write_zero_row(const AttnArgs& a, int b, int h, 
     if (a.lse) a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] = -INFINITY;
 }
 
+// Merge of the key-range splits: one wave per output row (b, h, r).  Valid rows get
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s in split order; padding rows
+// (r >= n_q[b]) are written as zero with lse = -inf.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
+    constexpr int EPL = D / 64;   // elements per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t n_rows = static_cast<int64_t>(a.B) * a.Hq * a.nq_max;
+    if (row >= n_rows) return;
+    const int r = static_cast<int>(row % a.nq_max);
+    const int h = static_cast<int>((row / a.nq_max) % a.Hq);
+    const int b = static_cast<int>(row / (static_cast<int64_t>(a.nq_max) * a.Hq));
+    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+    T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr + EPL * lane;
+    if (r >= nq) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) orow[e] = T(0);
+        if (a.lse && lane == 0) a.lse[row] = -INFINITY;
+        return;
+    }
+    const float* ml = a.part_ml + row * a.n_splits * 2;
+    const float* po = a.part_o + row * a.n_splits * D + EPL * lane;
+    float M = kNegBig;
+    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, ml[2 * s]);
+    float Lsum = 0.0f;
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+    for (int s = 0; s < a.n_splits; ++s) {
+        const float w = exp2f(ml[2 * s] - M);
+        Lsum = fmaf(ml[2 * s + 1], w, Lsum);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = fmaf(po[static_cast<int64_t>(s) * D + e], w, o[e]);
+    }
+    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) Elem<T>::store(orow + e, o[e] * inv);
+    if (a.lse && lane == 0) a.lse[row] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+}
+
 // ------------------------------------------------------------------ bf16 MFMA kernel
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     constexpr int NCH = D / 8;               // 16-byte chunks per row
     constexpr int KP = D * 2 + 16;           // K row pitch in LDS (bytes)
@@ -161,15 +219,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     static_assert(KPT >= 1 && VPT >= 1, "head dim");
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-    __shared__ uint32_t s_sink_ok[kMaxSinkWords];
-    __shared__ int s_tmp[17];
+    __shared__ int s_kidx[SPARSE ? 2 : 1][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
     const int hf = lane >> 5;
     const int col = lane & 31;
-    const WorkUnit u = decode_unit(a);
+    const WorkUnit u = decode_unit(a, 128);
+    if (!u.valid) return;
     const int b = u.b, g = u.g;
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
     const int rows_valid = a.Gq * nq;
@@ -180,31 +238,36 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     const int h = g * a.Gq + p % a.Gq;
     const int r = p / a.Gq;
 
-    if (p0 >= rows_valid) {  // whole tile is padding
-        if (a.n_splits == 1 && hf == 0 && p < rows_all) write_zero_row<uint16_t>(a, b, h, r, D);
-        return;
-    }
-
-    const KeyMap km = build_key_map(a, b, s_sink_ok, s_tmp);
-    const int n_tiles = (km.n_keys + 63) / 64;
+    const int n_keys = SPARSE ? a.n_keys[b] : a.L;
+    const int n_tiles = (n_keys + 63) / 64;
     const int t_begin = u.split * a.tiles_per_split;
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
+    const int32_t* klist = SPARSE ? a.kv_list + static_cast<int64_t>(b) * a.key_cap : nullptr;
 
-    // Q fragments (B operand of S^T = K Q^T): lane holds row p, d = 16c + 8hf .. +7
+    // Key index of row `row` of tile t.  Rows outside the split or past n_keys read a
+    // clamped valid row instead: such rows are masked (-inf score) or never computed,
+    // so the loads need no per-lane branch and the loop body stays straight-line.
+    auto fetch_kidx = [&](int t) -> int {   // threads 0..63: key of row tid of tile t, or -1
+        const int pos = t * 64 + tid;
+        return (t < t_end && pos < n_keys) ? klist[pos] : -1;
+    };
+    auto key_of = [&](int t, int row) -> int {
+        if (SPARSE) return max(s_kidx[t & 1][row], 0);
+        return min(t * 64 + row, n_keys - 1);
+    };
+
+    // Q fragments (B operand of S^T = K Q^T): lane holds row p, d = 16c + 8hf .. +7.
+    // Padding lanes read a valid row; their outputs are never written.
     bf16x8 qf[NQC];
     {
-        const uint16_t* qrow = nullptr;
-        if (row_ok) {
-            const int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + r] : r;
-            qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh +
-                   static_cast<int64_t>(phys) * a.qsr;
-        }
+        const int rr = row_ok ? r : 0;
+        int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + rr] : rr;
+        phys = max(phys, 0);
+        const int hh = row_ok ? h : g * a.Gq;
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh +
+                               static_cast<int64_t>(phys) * a.qsr;
 #pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row_ok) x = *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf);
-            qf[c] = __builtin_bit_cast(bf16x8, x);
-        }
+        for (int c = 0; c < NQC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf));
     }
 
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + g * a.ksh;
@@ -213,28 +276,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     u32x4 kreg[KPT];
     u32x4 vreg[VPT][2];
     auto load_tile = [&](int t) {
-        const int base = t * 64;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-            const int row = i * KROWS + tid / NCH;
-            const int ch = tid % NCH;
-            bool ok;
-            const int key = key_at(a, km, b, base + row, s_sink_ok, &ok);
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (ok) x = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * a.ksr + ch * 8);
-            kreg[i] = x;
+            const int key = key_of(t, i * KROWS + tid / NCH);
+            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * a.ksr + (tid % NCH) * 8);
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int pr = tid & 31;
             const int ch = (tid >> 5) + 8 * i;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                bool ok;
-                const int key = key_at(a, km, b, base + 2 * pr + e, s_sink_ok, &ok);
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (ok) x = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(key) * a.vsr + ch * 8);
-                vreg[i][e] = x;
+                const int key = key_of(t, 2 * (tid & 31) + e);
+                vreg[i][e] = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(key) * a.vsr + ch * 8);
             }
         }
     };
@@ -244,8 +297,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int row = i * KROWS + tid / NCH;
-            const int ch = tid % NCH;
-            *reinterpret_cast<u32x4*>(kb + row * KP + ch * 16) = kreg[i];
+            *reinterpret_cast<u32x4*>(kb + row * KP + (tid % NCH) * 16) = kreg[i];
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -272,13 +324,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     float l_run = 0.0f;
 
     if (t_begin < t_end) {
+        if (SPARSE) {
+            if (tid < 64) {
+                s_kidx[t_begin & 1][tid] = fetch_kidx(t_begin);
+                s_kidx[(t_begin + 1) & 1][tid] = fetch_kidx(t_begin + 1);
+            }
+            __syncthreads();
+        }
         load_tile(t_begin);
         store_tile(0);
-    }
-    for (int t = t_begin; t < t_end; ++t) {
+      // the loop is entered only after the prologue, so no path reaches it with the
+      // Q-fragment loads still outstanding (which would force a full wait per tile)
+      for (int t = t_begin; t < t_end; ++t) {
         const int buf = (t - t_begin) & 1;
         __syncthreads();
-        if (t + 1 < t_end) load_tile(t + 1);
+        load_tile(t + 1);   // past the split's last tile this reads valid rows that are never used
+        int next_kidx = -1;
+        if (SPARSE && tid < 64) next_kidx = fetch_kidx(t + 2);
         const uint8_t* kb = smem + buf * STAGE;
         const uint8_t* vb = kb + KBUF;
 
@@ -295,15 +357,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
                 st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[c], st[kb2], 0, 0, 0);
             }
         }
-        const int base = t * 64;
-        const bool full = base + 64 <= km.sink0 && base + 64 <= km.n_keys;
-        if (!full) {
+        const int valid_here = n_keys - t * 64;   // keys of this tile that exist
+        if (valid_here < 64) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kl = kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                    if (!key_attended(a, km, base + kl, s_sink_ok)) st[kb2][i] = -INFINITY;
+                    if (kl >= valid_here) st[kb2][i] = -INFINITY;
                 }
         }
         // online softmax (log2 domain), one query per lane pair
@@ -325,11 +386,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
                 psum += pv;
             }
         l_run = fmaf(l_run, alpha, psum);
+        // the output only needs rescaling when some lane's running max moved
+        if (__any(m_new != m_run)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
         m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
 
         // O^T += V^T P^T, four 16-key chunks
         bf16x8 pf[4];
@@ -349,14 +413,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
                                                                   pf[kc], acc[db], 0, 0, 0);
             }
         }
-        if (t + 1 < t_end) store_tile(buf ^ 1);
+        store_tile(buf ^ 1);
+        if (SPARSE && tid < 64) s_kidx[t & 1][tid] = next_kidx;
+      }
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (a.n_splits == 1) {
         if (row_ok) {
-            uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh +
-                             static_cast<int64_t>(r) * a.osr;
+            uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -374,7 +439,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
         } else if (hf == 0 && p < rows_all) {
             write_zero_row<uint16_t>(a, b, h, r, D);
         }
-    } else if (row_ok) {
+        return;
+    }
+    if (row_ok) {
         const int64_t idx = ((static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r) * a.n_splits + u.split;
         float* po = a.part_o + idx * D;
 #pragma unroll
@@ -397,16 +464,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
 constexpr int kF32Rows = 64;   // one wave, one query row per lane
 constexpr int kF32Keys = 32;   // keys per LDS tile
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float s_k[kF32Keys][D];
     __shared__ __attribute__((aligned(16))) float s_v[kF32Keys][D];
-    __shared__ uint32_t s_sink_ok[kMaxSinkWords];
-    __shared__ int s_tmp[17];
-    __shared__ int s_ok[kF32Keys];
+    __shared__ int s_key[kF32Keys];
 
     const int lane = threadIdx.x;
-    const WorkUnit u = decode_unit(a);
+    const WorkUnit u = decode_unit(a, kF32Rows);
+    if (!u.valid) return;
     const int b = u.b, g = u.g;
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
     const int rows_valid = a.Gq * nq;
@@ -416,14 +482,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
     const bool row_ok = p < rows_valid;
     const int h = g * a.Gq + p % a.Gq;
     const int r = p / a.Gq;
-    if (p0 >= rows_valid) {
-        if (a.n_splits == 1 && p < rows_all) write_zero_row<float>(a, b, h, r, D);
-        return;
-    }
-    const KeyMap km = build_key_map(a, b, s_sink_ok, s_tmp);
-    const int n_tiles = (km.n_keys + kF32Keys - 1) / kF32Keys;
+    const int n_keys = SPARSE ? a.n_keys[b] : a.L;
+    const int n_tiles = (n_keys + kF32Keys - 1) / kF32Keys;
     const int t_begin = u.split * a.tiles_per_split;
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
+    const int32_t* klist = SPARSE ? a.kv_list + static_cast<int64_t>(b) * a.key_cap : nullptr;
 
     float qv[D];
     float acc[D];
@@ -446,17 +509,16 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
     for (int t = t_begin; t < t_end; ++t) {
         __syncthreads();
         if (lane < kF32Keys) {
-            bool ok;
-            key_at(a, km, b, t * kF32Keys + lane, s_sink_ok, &ok);
-            s_ok[lane] = ok ? 1 : 0;
+            const int pos = t * kF32Keys + lane;
+            s_key[lane] = pos < n_keys ? (SPARSE ? klist[pos] : pos) : -1;
         }
+        __syncthreads();
         for (int i = lane; i < kF32Keys * D / 4; i += 64) {
             const int row = i / (D / 4);
             const int c4 = i % (D / 4);
-            bool ok;
-            const int key = key_at(a, km, b, t * kF32Keys + row, s_sink_ok, &ok);
+            const int key = s_key[row];
             f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-            if (ok) {
+            if (key >= 0) {
                 kx = *reinterpret_cast<const f32x4*>(kbase + static_cast<int64_t>(key) * a.ksr + 4 * c4);
                 vx = *reinterpret_cast<const f32x4*>(vbase + static_cast<int64_t>(key) * a.vsr + 4 * c4);
             }
@@ -473,7 +535,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
                 float dot = 0.0f;
 #pragma unroll
                 for (int e = 0; e < D; ++e) dot = fmaf(qv[e], s_k[j0 + j][e], dot);
-                s[j] = s_ok[j0 + j] ? dot * a.sl2 : -INFINITY;
+                s[j] = s_key[j0 + j] >= 0 ? dot * a.sl2 : -INFINITY;
                 mx = fmaxf(mx, s[j]);
             }
             const float m_new = fmaxf(m_run, mx);
@@ -504,7 +566,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
         } else if (p < rows_all) {
             write_zero_row<float>(a, b, h, r, D);
         }
-    } else if (row_ok) {
+        return;
+    }
+    if (row_ok) {
         const int64_t idx = ((static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r) * a.n_splits + u.split;
 #pragma unroll
         for (int e = 0; e < D; ++e) a.part_o[idx * D + e] = acc[e];
@@ -513,41 +577,23 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ split merge
-
-// One workgroup per output row (b, h, r): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <typename T>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const AttnArgs a, int d) {
-    const int64_t row = blockIdx.x;
-    const int r = static_cast<int>(row % a.nq_max);
-    const int h = static_cast<int>((row / a.nq_max) % a.Hq);
-    const int b = static_cast<int>(row / (static_cast<int64_t>(a.nq_max) * a.Hq));
-    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
-    T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
-    if (r >= nq) {
-        for (int e = threadIdx.x; e < d; e += blockDim.x) orow[e] = T(0);
-        if (a.lse && threadIdx.x == 0) a.lse[row] = -INFINITY;
-        return;
+template <int D>
+void launch_kernel(fdl_dtype dtype, const AttnArgs& a, dim3 grid, hipStream_t stream) {
+    if (dtype == FDL_BF16) {
+        if (a.sparse) hipLaunchKernelGGL((attn_bf16_kernel<D, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_bf16_kernel<D, false>), grid, dim3(256), 0, stream, a);
+    } else {
+        if (a.sparse) hipLaunchKernelGGL((attn_f32_kernel<D, true>), grid, dim3(kF32Rows), 0, stream, a);
+        else hipLaunchKernelGGL((attn_f32_kernel<D, false>), grid, dim3(kF32Rows), 0, stream, a);
     }
-    const float* ml = a.part_ml + row * a.n_splits * 2;
-    float M = kNegBig;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float Lsum = 0.0f;
-    for (int s = 0; s < a.n_splits; ++s) Lsum += ml[2 * s + 1] * exp2f(ml[2 * s] - M);
-    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-    const float* po = a.part_o + row * a.n_splits * d;
-    for (int e = threadIdx.x; e < d; e += blockDim.x) {
-        float x = 0.0f;
-        for (int s = 0; s < a.n_splits; ++s) x = fmaf(po[static_cast<int64_t>(s) * d + e], exp2f(ml[2 * s] - M), x);
-        Elem<T>::store(orow + e, x * inv);
-    }
-    if (a.lse && threadIdx.x == 0) a.lse[row] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
+
+inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
 AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_max,
-                        int64_t key_bound) {
+                        int64_t key_bound, bool sparse) {
     AttnPlan pl;
     const bool bf16 = dtype == FDL_BF16;
     pl.rows_per_tile = bf16 ? 128 : kF32Rows;
@@ -565,11 +611,14 @@ AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_m
     pl.n_splits = static_cast<int>(splits);
     pl.tiles_per_split = static_cast<int>((tiles + splits - 1) / splits);
     if (pl.tiles_per_split < 1) pl.tiles_per_split = 1;
-    pl.ws_bytes = 0;
+    pl.key_cap = sparse ? key_bound : 0;
+    pl.list_bytes = sparse ? round_up(static_cast<size_t>(B) * (key_bound + 1) * sizeof(int32_t), 256) : 0;
+    pl.part_bytes = 0;
     if (pl.n_splits > 1) {
         const int64_t nrows = static_cast<int64_t>(B) * Hq * nq_max * pl.n_splits;
-        pl.ws_bytes = static_cast<size_t>(nrows) * (d + 2) * sizeof(float);
+        pl.part_bytes = static_cast<size_t>(nrows) * (d + 2) * sizeof(float);
     }
+    pl.ws_bytes = pl.list_bytes + pl.part_bytes;
     return pl;
 }
 
@@ -579,24 +628,41 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     a.q_tiles = pl.q_tiles;
     a.n_splits = pl.n_splits;
     a.tiles_per_split = pl.tiles_per_split;
-    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.nq_max;
-    if (pl.n_splits > 1) {
-        a.part_o = static_cast<float*>(a.part_o);
-        a.part_ml = a.part_o + nrows * pl.n_splits * d;
+    a.key_cap = static_cast<int>(pl.key_cap);
+    uint8_t* ws = reinterpret_cast<uint8_t*>(a.part_o);  // the caller's workspace base
+    a.kv_list = nullptr;
+    a.n_keys = nullptr;
+    if (a.sparse) {
+        a.kv_list = reinterpret_cast<int32_t*>(ws);
+        a.n_keys = a.kv_list + static_cast<int64_t>(a.B) * pl.key_cap;
     }
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * pl.n_splits * pl.q_tiles));
-    if (dtype == FDL_BF16) {
-        if (d == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
-    } else {
-        if (d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+    a.part_o = pl.part_bytes ? reinterpret_cast<float*>(ws + pl.list_bytes) : nullptr;
+    a.part_ml = a.part_o ? a.part_o + static_cast<int64_t>(a.B) * a.Hq * a.nq_max * pl.n_splits * d : nullptr;
+    const bool zero_pad = a.n_q && pl.n_splits == 1;
+    if (a.sparse || zero_pad) {
+        const int pad_wgs = zero_pad ? 64 : 0;   // extra workgroups that zero the padding rows
+        const dim3 pgrid(a.B, 1 + pad_wgs);
+        if (dtype == FDL_BF16) hipLaunchKernelGGL(attn_prep_kernel<uint16_t>, pgrid, dim3(256), 0, stream, a, d);
+        else hipLaunchKernelGGL(attn_prep_kernel<float>, pgrid, dim3(256), 0, stream, a, d);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
+    // groups of q_tiles consecutive slots per XCD: round the group count up to a multiple of 8
+    const int64_t groups = static_cast<int64_t>(a.B) * a.Hkv * pl.n_splits;
+    const dim3 grid(static_cast<unsigned>((groups + 7) / 8 * 8 * pl.q_tiles));
+    if (d == 128) launch_kernel<128>(dtype, a, grid, stream);
+    else launch_kernel<64>(dtype, a, grid, stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.n_splits == 1) return err;
-    const dim3 mgrid(static_cast<unsigned>(nrows));
-    if (dtype == FDL_BF16) hipLaunchKernelGGL(attn_merge_kernel<uint16_t>, mgrid, dim3(128), 0, stream, a, d);
-    else hipLaunchKernelGGL(attn_merge_kernel<float>, mgrid, dim3(128), 0, stream, a, d);
+    const int64_t n_rows = static_cast<int64_t>(a.B) * a.Hq * a.nq_max;
+    const dim3 mgrid(static_cast<unsigned>((n_rows + 3) / 4));
+    if (dtype == FDL_BF16) {
+        if (d == 128) hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 128>), mgrid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 64>), mgrid, dim3(256), 0, stream, a);
+    } else {
+        if (d == 128) hipLaunchKernelGGL((attn_merge_kernel<float, 128>), mgrid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((attn_merge_kernel<float, 64>), mgrid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

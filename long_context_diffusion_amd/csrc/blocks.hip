@@ -61,15 +61,28 @@ __global__ __launch_bounds__(kQsumThreads) void block_qsum_kernel(const BlockArg
     double acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
-    for (int p = rg; p < rows; p += RG) {
-        const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
-        const int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + r] : r;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + b * a.qsb + h * a.qsh +
-                                                       static_cast<int64_t>(phys) * a.qsr + piece * EPP);
-        float v[EPP];
-        unpack16<T>(x, v);
+    constexpr int kBatch = 4;
+    for (int p0 = rg; p0 < rows; p0 += RG * kBatch) {
+        u32x4 x[kBatch];
+        bool ok[kBatch];
 #pragma unroll
-        for (int e = 0; e < EPP; ++e) acc[e] += static_cast<double>(v[e]);
+        for (int u = 0; u < kBatch; ++u) {
+            const int p = p0 + u * RG;
+            ok[u] = p < rows;
+            const int pc = ok[u] ? p : rg;
+            const int h = g * a.Gq + pc % a.Gq, r = pc / a.Gq;
+            const int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + r] : r;
+            x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + b * a.qsb + h * a.qsh +
+                                                  static_cast<int64_t>(phys) * a.qsr + piece * EPP);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (!ok[u]) continue;
+            float v[EPP];
+            unpack16<T>(x[u], v);
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) acc[e] += static_cast<double>(v[e]);
+        }
     }
 #pragma unroll
     for (int e = 0; e < EPP; ++e) s_part[rg][piece * EPP + e] = acc[e];
@@ -169,27 +182,44 @@ __global__ __launch_bounds__(kScanThreads) void block_scan_kernel(const BlockArg
     }
 }
 
+constexpr int kSelectLds = 2048;   // blocks ranked in LDS
+
 __global__ __launch_bounds__(1024) void block_select_kernel(const BlockArgs a, int C, int32_t* block_idx,
                                                             double* R_out) {
     __shared__ SelectSmem sm;
+    __shared__ uint64_t s_key[kSelectLds];
     const int b = blockIdx.x;
     double* R = a.rfull + static_cast<int64_t>(b) * a.nb;
     for (int blk = threadIdx.x; blk < a.nb; blk += blockDim.x) {
         const double* rp = a.rpart + static_cast<int64_t>(b) * a.Hkv * a.nb + blk;
         double s = 0.0;
-        for (int g = 0; g < a.Hkv; ++g) s += rp[static_cast<int64_t>(g) * a.nb];
+        int g = 0;
+        for (; g + 8 <= a.Hkv; g += 8) {
+            double x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = rp[static_cast<int64_t>(g + u) * a.nb];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += x[u];
+        }
+        for (; g < a.Hkv; ++g) s += rp[static_cast<int64_t>(g) * a.nb];
         const int cnt = min(a.bs, a.P - blk * a.bs);
         const double val = s * (static_cast<double>(a.scale) / static_cast<double>(cnt));
-        R[blk] = val;
+        if (a.nb <= kSelectLds) s_key[blk] = okey64(val);
+        else R[blk] = val;
         if (R_out) R_out[static_cast<int64_t>(b) * a.nb + blk] = val;
     }
     __syncthreads();
     __threadfence_block();
-    auto key_of = [&](int j, uint64_t* key) -> bool {
-        *key = okey64(R[j]);
-        return true;
-    };
-    block_emit_topk<uint64_t>(a.nb, C, key_of, block_idx + static_cast<int64_t>(b) * C, C, &sm);
+    int32_t* out = block_idx + static_cast<int64_t>(b) * C;
+    if (a.nb <= kSelectLds) {
+        block_topk_lds<uint64_t>(a.nb, C, s_key, [](int j) { return j; }, out, C, &sm);
+    } else {
+        auto key_of = [&](int j, uint64_t* key) -> bool {
+            *key = okey64(R[j]);
+            return true;
+        };
+        block_emit_topk<uint64_t>(a.nb, C, key_of, [](int j) { return j; }, out, C, &sm);
+    }
 }
 
 }  // namespace

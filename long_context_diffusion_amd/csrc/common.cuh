@@ -96,8 +96,13 @@ __device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
 }
 
 // ------------------------------------------------------------------ top-k selection
+//
+// Selections keep the k entries with the largest ordered keys, the lower index
+// first among equal keys, and write them in ascending index order.  KeyFn(j, &key)
+// loads the key of entry j and returns whether j takes part; it must be safe to call
+// for every j in [0, n).  Keys are read in batches of independent loads.
 
-// Shared scratch for block_kth_largest / block_emit_topk.
+// Shared scratch for the selection helpers.
 struct SelectSmem {
     int hist[256];
     int tmp[17];
@@ -112,9 +117,27 @@ __device__ __forceinline__ void thread_chunk(int n, int* lo, int* hi) {
     *hi = min(n, *lo + chunk);
 }
 
+// Calls body(j, key) for every valid j in [lo, hi), loading 8 keys at a time.
+template <typename U, typename KeyFn, typename Body>
+__device__ __forceinline__ void for_each_key(int lo, int hi, KeyFn key_of, Body body) {
+    constexpr int kBatch = 8;
+    for (int j0 = lo; j0 < hi; j0 += kBatch) {
+        U keys[kBatch];
+        bool ok[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = j0 + u;
+            const bool in = j < hi;
+            ok[u] = key_of(in ? j : lo, &keys[u]) && in;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (ok[u]) body(j0 + u, keys[u]);
+    }
+}
+
 // Radix select: the k-th largest ordered key among the valid entries of [0, n)
-// (1 <= k <= number of valid entries).  KeyFn(j, &key) returns whether entry j
-// takes part.  Every thread of the block must call it; all get the same result.
+// (1 <= k <= number of valid entries).  Every thread of the block must call it.
 template <typename U, typename KeyFn>
 __device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
     constexpr int kBits = 8 * sizeof(U);
@@ -125,22 +148,19 @@ __device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
     for (int shift = kBits - 8; shift >= 0; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += blockDim.x) sm->hist[i] = 0;
         __syncthreads();
-        for (int j = lo; j < hi; ++j) {
-            U kj;
-            if (key_of(j, &kj) && (kj & prefix_mask) == prefix)
-                atomicAdd(&sm->hist[static_cast<int>((kj >> shift) & 0xff)], 1);
-        }
+        for_each_key<U>(lo, hi, key_of, [&](int, U kj) {
+            if ((kj & prefix_mask) == prefix) atomicAdd(&sm->hist[static_cast<int>((kj >> shift) & 0xff)], 1);
+        });
         __syncthreads();
         if (threadIdx.x < kWave) {
             // lane l owns bins 4l..4l+3; find the bin holding the remaining-th largest
             const int l = threadIdx.x;
             int h[4];
             for (int q = 0; q < 4; ++q) h[q] = sm->hist[4 * l + q];
-            int mine = h[0] + h[1] + h[2] + h[3];
-            // sum over lanes above l (bins above 4l+3)
-            int suffix = mine;
+            const int mine = h[0] + h[1] + h[2] + h[3];
+            int suffix = mine;  // sum over lanes >= l
             for (int off = 1; off < kWave; off <<= 1) {
-                int y = __shfl_down(suffix, off, kWave);
+                const int y = __shfl_down(suffix, off, kWave);
                 if (l + off < kWave) suffix += y;
             }
             int above = suffix - mine;
@@ -162,54 +182,80 @@ __device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
     return prefix;
 }
 
-// Writes, in ascending index order, the k valid entries with the largest keys
-// (lower index first among equal keys) to out[0..), pads out[..cap) with -1 and
-// returns the number written (min(k, valid)).  Every thread must call it.
-template <typename U, typename KeyFn>
-__device__ int block_emit_topk(int n, int k, KeyFn key_of, int32_t* out, int cap,
+// Writes idx_of(j) for the k valid entries with the largest keys, in ascending j,
+// to out[0..), pads out[..cap) with -1 and returns the number written.
+template <typename U, typename KeyFn, typename IdxFn>
+__device__ int block_emit_topk(int n, int k, KeyFn key_of, IdxFn idx_of, int32_t* out, int cap,
                                SelectSmem* sm) {
     int lo, hi;
     thread_chunk(n, &lo, &hi);
     int nvalid_local = 0;
-    for (int j = lo; j < hi; ++j) {
-        U kj;
-        nvalid_local += key_of(j, &kj) ? 1 : 0;
-    }
+    for_each_key<U>(lo, hi, key_of, [&](int, U) { ++nvalid_local; });
     int nvalid;
     block_exclusive_sum(nvalid_local, sm->tmp, &nvalid);
     const bool take_all = nvalid <= k;
     const int nsel = take_all ? nvalid : max(k, 0);
     U thr = 0;
     if (!take_all && nsel > 0) thr = block_kth_largest<U>(n, nsel, key_of, sm);
-    // counts above the threshold and ties in this thread's chunk
     int gt = 0, eq = 0;
     if (nsel > 0) {
-        for (int j = lo; j < hi; ++j) {
-            U kj;
-            if (!key_of(j, &kj)) continue;
+        for_each_key<U>(lo, hi, key_of, [&](int, U kj) {
             if (take_all || kj > thr) ++gt;
             else if (kj == thr) ++eq;
-        }
+        });
     }
     int gt_total, eq_total;
     int gt_before = block_exclusive_sum(gt, sm->tmp, &gt_total);
     int eq_before = block_exclusive_sum(eq, sm->tmp, &eq_total);
     const int ties_taken = nsel - gt_total;  // lowest-index ties fill the rest
     if (nsel > 0) {
-        for (int j = lo; j < hi; ++j) {
-            U kj;
-            if (!key_of(j, &kj)) continue;
-            const bool above = take_all || kj > thr;
-            const bool tie = !above && kj == thr;
-            if (above) {
-                out[gt_before + min(eq_before, ties_taken)] = j;
+        for_each_key<U>(lo, hi, key_of, [&](int j, U kj) {
+            if (take_all || kj > thr) {
+                out[gt_before + min(eq_before, ties_taken)] = idx_of(j);
                 ++gt_before;
-            } else if (tie) {
-                if (eq_before < ties_taken) out[gt_before + eq_before] = j;
+            } else if (kj == thr) {
+                if (eq_before < ties_taken) out[gt_before + eq_before] = idx_of(j);
                 ++eq_before;
             }
+        });
+    }
+    for (int i = nsel + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
+    return nsel;
+}
+
+// Selection over keys already in LDS (every entry valid).  Up to 2048 entries each
+// thread ranks its own entries against all others; larger sets use the radix select.
+template <typename U, typename IdxFn>
+__device__ int block_topk_lds(int n, int k, const U* keys, IdxFn idx_of, int32_t* out, int cap,
+                              SelectSmem* sm) {
+    const int nsel = min(max(k, 0), n);
+    if (n > 2048 || blockDim.x * 32 < static_cast<unsigned>(n)) {
+        auto key_of = [&](int j, U* key) -> bool {
+            *key = keys[j];
+            return true;
+        };
+        return block_emit_topk<U>(n, k, key_of, idx_of, out, cap, sm);
+    }
+    int lo, hi;
+    thread_chunk(n, &lo, &hi);
+    uint32_t sel = 0;
+    int cnt = 0;
+    for (int j = lo; j < hi; ++j) {
+        const U kj = keys[j];
+        int rank = 0;
+        for (int i = 0; i < n; ++i) {
+            const U ki = keys[i];
+            rank += (ki > kj || (ki == kj && i < j)) ? 1 : 0;
+        }
+        if (rank < nsel) {
+            sel |= 1u << (j - lo);
+            ++cnt;
         }
     }
+    int total;
+    int off = block_exclusive_sum(cnt, sm->tmp, &total);
+    for (int j = lo; j < hi; ++j)
+        if ((sel >> (j - lo)) & 1u) out[off++] = idx_of(j);
     for (int i = nsel + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
     return nsel;
 }

@@ -6,18 +6,24 @@
 // widened to the w positions [p - floor(w/2), p - floor(w/2) + w) clipped to
 // [0, L), and their union is I_active.
 //
-// One 1024-thread workgroup per sequence.  Selection is a byte-wise radix
-// select on order-preserving confidence keys followed by an ordered scan over
-// the positions, so I_focus comes out ascending with the lower index winning
-// among equal confidences.  The windows of an ascending focus list have
-// ascending ends, so each window adds the positions past the previous window's
-// end; a scan over those counts places every active position.
+// One 1024-thread workgroup per sequence.  A first pass reads the confidence
+// and mask in per-thread runs of 16 positions (independent loads) and compacts
+// the masked slots, in position order, into LDS as order-preserving keys.  The
+// top-k is then selected among those candidates (a rank count when there are at
+// most 2048 of them, a byte-wise radix select otherwise), which gives I_focus in
+// ascending order with the lower index winning among equal confidences.  More
+// than 8192 masked slots fall back to a radix select that reads the keys from
+// global memory.  The windows of an ascending focus list have ascending ends, so
+// each window adds the positions past the previous window's end; a scan over
+// those counts places every active position.
 
 #include "ops.cuh"
 
 namespace fdl {
 
 constexpr int kPcgiThreads = 1024;
+constexpr int kPcgiRun = 16;        // positions per thread per pass
+constexpr int kPcgiCap = 8192;      // masked slots kept in LDS
 
 __global__ __launch_bounds__(kPcgiThreads) void pcgi_select_kernel(
     const float* __restrict__ conf, const uint8_t* __restrict__ mask, int L, int k, int w,
@@ -25,27 +31,67 @@ __global__ __launch_bounds__(kPcgiThreads) void pcgi_select_kernel(
     int32_t* __restrict__ active_idx, int32_t* __restrict__ n_active, int nq_max) {
     __shared__ SelectSmem sm;
     __shared__ int s_carry;
+    __shared__ uint32_t s_key[kPcgiCap];
+    __shared__ int32_t s_pos[kPcgiCap];
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
     const float* c = conf + static_cast<int64_t>(b) * L;
     const uint8_t* m = mask + static_cast<int64_t>(b) * L;
     int32_t* focus = focus_idx + static_cast<int64_t>(b) * k_cap;
     int32_t* active = active_idx + static_cast<int64_t>(b) * nq_max;
 
-    auto key_of = [&](int j, uint32_t* key) -> bool {
-        if (!m[j]) return false;
-        *key = okey32(c[j]);
-        return true;
-    };
-    const int nf = block_emit_topk<uint32_t>(L, k, key_of, focus, k_cap, &sm);
-    __syncthreads();  // focus[] written by other threads is read below (global, same block)
+    // compact the masked slots into LDS, in position order
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int base = 0; base < L; base += kPcgiThreads * kPcgiRun) {
+        const int lo = base + tid * kPcgiRun;
+        uint32_t keys[kPcgiRun];
+        bool msk[kPcgiRun];
+#pragma unroll
+        for (int u = 0; u < kPcgiRun; ++u) {
+            const int j = min(lo + u, L - 1);
+            keys[u] = okey32(c[j]);
+            msk[u] = m[j] != 0 && lo + u < L;
+        }
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < kPcgiRun; ++u) cnt += msk[u] ? 1 : 0;
+        int total;
+        int off = block_exclusive_sum(cnt, sm.tmp, &total) + s_carry;
+#pragma unroll
+        for (int u = 0; u < kPcgiRun; ++u) {
+            if (msk[u]) {
+                if (off < kPcgiCap) {
+                    s_key[off] = keys[u];
+                    s_pos[off] = lo + u;
+                }
+                ++off;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) s_carry += total;
+        __syncthreads();
+    }
+    const int n_masked = s_carry;
+    int nf;
+    if (n_masked <= kPcgiCap) {
+        nf = block_topk_lds<uint32_t>(n_masked, k, s_key, [&](int j) { return s_pos[j]; }, focus, k_cap, &sm);
+    } else {
+        auto key_of = [&](int j, uint32_t* key) -> bool {
+            *key = okey32(c[j]);
+            return m[j] != 0;
+        };
+        nf = block_emit_topk<uint32_t>(L, k, key_of, [](int j) { return j; }, focus, k_cap, &sm);
+    }
+    __syncthreads();  // focus[] written by other threads of the block is read below
     __threadfence_block();
 
     // Window union over the ascending focus list, processed in chunks of the block size.
     const int half = w / 2;
-    if (threadIdx.x == 0) s_carry = 0;
+    if (tid == 0) s_carry = 0;
     __syncthreads();
     for (int f0 = 0; f0 < nf; f0 += blockDim.x) {
-        const int f = f0 + threadIdx.x;
+        const int f = f0 + tid;
         int start = 0, stop = 0, cnt = 0;
         if (f < nf) {
             const int p = focus[f];
@@ -65,12 +111,12 @@ __global__ __launch_bounds__(kPcgiThreads) void pcgi_select_kernel(
         const int off = block_exclusive_sum(cnt, sm.tmp, &total) + s_carry;
         for (int i = 0; i < cnt; ++i) active[off + i] = start + i;
         __syncthreads();
-        if (threadIdx.x == 0) s_carry += total;
+        if (tid == 0) s_carry += total;
         __syncthreads();
     }
     const int na = s_carry;
-    for (int i = na + threadIdx.x; i < nq_max; i += blockDim.x) active[i] = -1;
-    if (threadIdx.x == 0) {
+    for (int i = na + tid; i < nq_max; i += blockDim.x) active[i] = -1;
+    if (tid == 0) {
         n_focus[b] = nf;
         n_active[b] = na;
     }

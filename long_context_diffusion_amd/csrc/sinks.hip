@@ -28,12 +28,13 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kSinkKeysPerWg = 256;  // 4 waves x 64 keys
 
 template <int D>
-__global__ __launch_bounds__(256) void sink_colsum_bf16_kernel(const SinkArgs a) {
+__global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs a) {
     constexpr int NQC = D / 16;
     constexpr int NCH = D / 8;
-    constexpr int QP = D * 2 + 16;     // Q row pitch in LDS (bytes)
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[32 * QP];
-    __shared__ float s_lse[32];
+    constexpr int QP = D * 2 + 16;         // Q row pitch in LDS (bytes)
+    constexpr int QPT = 32 * NCH / 256;    // 16-byte Q pieces staged per thread per block
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[2][32 * QP];
+    __shared__ float s_lse[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, col = lane & 31;
     const int kt = blockIdx.x % a.key_tiles;
@@ -41,6 +42,7 @@ __global__ __launch_bounds__(256) void sink_colsum_bf16_kernel(const SinkArgs a)
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
     const int rows = a.Gq * nq;
+    const int n_blocks = (rows + 31) / 32;
     const int key0 = kt * kSinkKeysPerWg + wv * 64;
 
     // K fragments (B operand): key = key0 + 32*kg + col, d = 16c + 8hf .. +7
@@ -48,57 +50,89 @@ __global__ __launch_bounds__(256) void sink_colsum_bf16_kernel(const SinkArgs a)
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + g * a.ksh;
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
-        const int key = key0 + 32 * kg + col;
+        const int key = min(key0 + 32 * kg + col, a.L - 1);
 #pragma unroll
-        for (int c = 0; c < NQC; ++c) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (key < a.L) x = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * a.ksr + 16 * c + 8 * hf);
-            kf[kg][c] = __builtin_bit_cast(bf16x8, x);
-        }
+        for (int c = 0; c < NQC; ++c)
+            kf[kg][c] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * a.ksr + 16 * c + 8 * hf));
     }
-    float acc[2] = {0.0f, 0.0f};
 
-    for (int r0 = 0; r0 < rows; r0 += 32) {
-        __syncthreads();
-        // stage 32 packed query rows (zero beyond `rows`) and their lse in log2 units
-        for (int i = tid; i < 32 * NCH; i += 256) {
-            const int rr = i / NCH, ch = i % NCH;
-            const int p = r0 + rr;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (p < rows) {
-                const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
-                const int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + r] : r;
-                x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh +
-                                                   static_cast<int64_t>(phys) * a.qsr + 8 * ch);
-            }
-            *reinterpret_cast<u32x4*>(s_q + rr * QP + 16 * ch) = x;
+    // Staging of Q block i (packed rows 32i .. 32i+31): thread stages pieces (rr, ch).
+    // Physical row offsets are resolved one block ahead of the loads.
+    auto row_offset = [&](int i, int x) -> int64_t {   // element offset of the row of piece x
+        const int item = tid + 256 * x;
+        const int p = min(32 * i + item / NCH, max(rows - 1, 0));
+        const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
+        const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
+        return b * a.qsb + h * a.qsh + static_cast<int64_t>(phys) * a.qsr + 8 * ((tid + 256 * x) % NCH);
+    };
+    auto lse_of = [&](int i) -> float {   // lse (log2 units) of row 32i + tid % 32, +inf past the end
+        const int p = 32 * i + (tid & 31);
+        const int pc = min(p, rows - 1);
+        const int h = g * a.Gq + pc % a.Gq, r = pc / a.Gq;
+        const float v = a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] * kLog2e;
+        return p < rows ? v : INFINITY;
+    };
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+    u32x4 qreg[QPT];
+    int64_t off_next[QPT];
+    float lse_next = INFINITY;
+    auto load_block = [&](int64_t* off) {
+#pragma unroll
+        for (int x = 0; x < QPT; ++x) qreg[x] = *reinterpret_cast<const u32x4*>(qb + off[x]);
+    };
+    auto store_block = [&](int buf) {
+#pragma unroll
+        for (int x = 0; x < QPT; ++x) {
+            const int item = tid + 256 * x;
+            *reinterpret_cast<u32x4*>(&s_q[buf][(item / NCH) * QP + 16 * (item % NCH)]) = qreg[x];
         }
-        if (tid < 32) {
-            const int p = r0 + tid;
-            float l2 = INFINITY;
-            if (p < rows) {
-                const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
-                l2 = a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] * kLog2e;
-            }
-            s_lse[tid] = l2;
+        if (tid < 32) s_lse[buf][tid] = lse_next;
+    };
+
+    float acc[2] = {0.0f, 0.0f};
+    if (n_blocks > 0) {
+        int64_t off0[QPT];
+#pragma unroll
+        for (int x = 0; x < QPT; ++x) {
+            off0[x] = row_offset(0, x);
+            off_next[x] = row_offset(1, x);
         }
+        lse_next = lse_of(0);
+        load_block(off0);
+        store_block(0);
         __syncthreads();
-        float lrow[16];
+        for (int i = 0; i < n_blocks; ++i) {
+            const int buf = i & 1;
+            // prefetch block i+1 (valid rows are clamped; past the end it is never used)
+            load_block(off_next);
+            const float lse_pref = lse_of(i + 1);
+            int64_t off_after[QPT];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) lrow[i] = s_lse[8 * (i >> 2) + 4 * hf + (i & 3)];
-        const uint8_t* qrow = s_q + col * QP + 16 * hf;
+            for (int x = 0; x < QPT; ++x) off_after[x] = row_offset(i + 2, x);
+
+            float lrow[16];
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-            f32x16 s;
+            for (int e = 0; e < 16; ++e) lrow[e] = s_lse[buf][8 * (e >> 2) + 4 * hf + (e & 3)];
+            const uint8_t* qrow = &s_q[buf][col * QP + 16 * hf];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+            for (int kg = 0; kg < 2; ++kg) {
+                f32x16 sc;
 #pragma unroll
-            for (int c = 0; c < NQC; ++c) {
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kg][c], s, 0, 0, 0);
+                for (int e = 0; e < 16; ++e) sc[e] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NQC; ++c) {
+                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
+                    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kg][c], sc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[kg] += exp2f(fmaf(sc[e], a.sl2, -lrow[e]));
             }
+            lse_next = lse_pref;
+            store_block(buf ^ 1);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[kg] += exp2f(fmaf(s[i], a.sl2, -lrow[i]));
+            for (int x = 0; x < QPT; ++x) off_next[x] = off_after[x];
+            __syncthreads();
         }
     }
 #pragma unroll
@@ -158,6 +192,7 @@ __global__ __launch_bounds__(256) void sink_colsum_f32_kernel(const SinkArgs a) 
     if (key < a.L) a.part[(static_cast<int64_t>(b) * a.Hkv + g) * a.L + key] = acc;
 }
 
+// scores[b][j] = sum over KV heads of the partial column sums, in head order.
 __global__ __launch_bounds__(256) void sink_reduce_kernel(const SinkArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= static_cast<int64_t>(a.B) * a.L) return;
@@ -165,20 +200,38 @@ __global__ __launch_bounds__(256) void sink_reduce_kernel(const SinkArgs a) {
     const int j = static_cast<int>(i % a.L);
     const float* p = a.part + static_cast<int64_t>(b) * a.Hkv * a.L + j;
     float s = 0.0f;
-    for (int g = 0; g < a.Hkv; ++g) s += p[static_cast<int64_t>(g) * a.L];
+    int g = 0;
+    for (; g + 8 <= a.Hkv; g += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p[static_cast<int64_t>(g + u) * a.L];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += x[u];
+    }
+    for (; g < a.Hkv; ++g) s += p[static_cast<int64_t>(g) * a.L];
     a.scores[i] = s;
 }
+
+constexpr int kSinkLdsKeys = 32768;   // scores kept in LDS by the selection (128 KB)
 
 __global__ __launch_bounds__(1024) void sink_select_kernel(const float* __restrict__ scores, int L,
                                                            int n_sinks, int32_t* __restrict__ sink_idx) {
     __shared__ SelectSmem sm;
+    extern __shared__ uint32_t s_keys[];
     const int b = blockIdx.x;
     const float* s = scores + static_cast<int64_t>(b) * L;
-    auto key_of = [&](int j, uint32_t* key) -> bool {
-        *key = okey32(s[j]);
-        return true;
-    };
-    block_emit_topk<uint32_t>(L, n_sinks, key_of, sink_idx + static_cast<int64_t>(b) * n_sinks, n_sinks, &sm);
+    int32_t* out = sink_idx + static_cast<int64_t>(b) * n_sinks;
+    if (L <= kSinkLdsKeys) {
+        for (int j = threadIdx.x; j < L; j += blockDim.x) s_keys[j] = okey32(s[j]);
+        __syncthreads();
+        block_topk_lds<uint32_t>(L, n_sinks, s_keys, [](int j) { return j; }, out, n_sinks, &sm);
+    } else {
+        auto key_of = [&](int j, uint32_t* key) -> bool {
+            *key = okey32(s[j]);
+            return true;
+        };
+        block_emit_topk<uint32_t>(L, n_sinks, key_of, [](int j) { return j; }, out, n_sinks, &sm);
+    }
 }
 
 }  // namespace
@@ -206,7 +259,8 @@ hipError_t launch_sink_identify(fdl_dtype dtype, int d, SinkArgs a, int n_sinks,
     hipLaunchKernelGGL(sink_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(sink_select_kernel, dim3(a.B), dim3(1024), 0, stream, a.scores, a.L, n_sinks, sink_idx);
+    const size_t lds = a.L <= kSinkLdsKeys ? static_cast<size_t>(a.L) * sizeof(uint32_t) : 0;
+    hipLaunchKernelGGL(sink_select_kernel, dim3(a.B), dim3(1024), lds, stream, a.scores, a.L, n_sinks, sink_idx);
     return hipGetLastError();
 }
 

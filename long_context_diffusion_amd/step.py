@@ -1,0 +1,105 @@
+"""One Focus-dLLM denoising step over a stack of attention layers, through the C ABI.
+
+Focus-dLLM structured summary (paper.rainbus.top/paper/2602.02159), "Method
+steps": a block-entry step refreshes densely (every row attends to every key
+in every layer); any other step runs (1) PCGI, (2) windows, (3) dense layers
+1..l_dense on the active rows with sinks taken from layer l_dense, then (4)
+block top-C and (5) sparse attention in every deeper layer, reusing the sinks.
+
+StepRunner only sequences the library's entry points on one stream with
+buffers allocated once, so a whole step can be captured in a HIP graph and
+replayed; it performs no arithmetic of its own.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import fdl as F
+
+
+class StepRunner:
+    def __init__(self, *, B, L, P, Hq, Hkv, d, dtype, n_t, rho, w, bs, C, n_sinks, layers, l_dense,
+                 scale=0.0, device="cuda"):
+        self.B, self.L, self.P, self.Hq, self.Hkv, self.d = B, L, P, Hq, Hkv, d
+        self.n_t, self.rho, self.w, self.bs, self.C, self.n_sinks = n_t, rho, w, bs, C, n_sinks
+        self.layers, self.l_dense, self.scale = layers, l_dense, scale
+        self.k = F.focus_count(n_t, rho)
+        self.nq_max = max(min(self.k * w, L), 1)
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.focus = torch.empty((B, max(self.k, 1)), **i32)
+        self.n_focus = torch.empty((B,), **i32)
+        self.active = torch.empty((B, self.nq_max), **i32)
+        self.n_active = torch.empty((B,), **i32)
+        self.sinks = torch.empty((B, max(n_sinks, 1)), **i32)
+        self.blocks = [torch.empty((B, max(C, 1)), **i32) for _ in range(layers)]
+        self.out = [torch.empty((B, Hq, self.nq_max, d), dtype=dtype, device=dev) for _ in range(layers)]
+        self.lse = torch.empty((B, Hq, self.nq_max), dtype=torch.float32, device=dev)
+        self.workspace = F.Workspace(dev)
+        # size the shared workspace once, so a captured step never allocates
+        dt = F.FDL_BF16 if dtype == torch.bfloat16 else F.FDL_F32
+        lib = F.lib()
+        need = max(
+            lib.fdl_dense_attention_workspace_bytes(dt, B, Hq, Hkv, L, d, self.nq_max),
+            lib.fdl_sink_identify_workspace_bytes(dt, B, Hq, Hkv, L, d, self.nq_max),
+            lib.fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs),
+            lib.fdl_sparse_attention_workspace_bytes(dt, B, Hq, Hkv, L, P, d, self.nq_max, n_sinks, C, bs),
+        )
+        self.workspace.get(need)
+
+    def _rows(self):
+        return dict(q_idx=self.active, n_q=self.n_active, nq_max=self.nq_max, scale=self.scale,
+                    workspace=self.workspace)
+
+    def pcgi(self, conf, mask):
+        F.pcgi_select(conf, mask, self.n_t, self.rho, self.w, k_cap=self.focus.shape[1], nq_max=self.nq_max,
+                      out=(self.focus, self.n_focus, self.active, self.n_active))
+
+    def dense_layer(self, l, q, k, v):
+        F.dense_attention(q, k, v, out=self.out[l], lse=self.lse, **self._rows())
+
+    def sinks_at(self, q, k):
+        if self.n_sinks:
+            F.sink_identify(q, k, self.lse, self.n_sinks, out=self.sinks, **self._rows())
+
+    def sparse_layer(self, l, q, k, v):
+        sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
+        blocks = self.blocks[l][:, : self.C] if self.C else None
+        if self.C:
+            F.block_score_topc(q, k, self.P, self.bs, self.C, out=self.blocks[l], **self._rows())
+        F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs, out=self.out[l], **self._rows())
+
+    def sparse_step(self, conf, mask, qs, ks, vs, hooks=None):
+        """A non-block-entry step; qs/ks/vs are per-layer [B, H, L, d] tensors.
+
+        `hooks` (optional) maps a stage name ("pcgi", "dense", "sinks", "blocks",
+        "sparse") to a (before, after) pair of callables run around each call of
+        that stage, e.g. to record events."""
+        def run(name, fn):
+            h = hooks.get(name) if hooks else None
+            if h:
+                h[0]()
+            fn()
+            if h:
+                h[1]()
+        run("pcgi", lambda: self.pcgi(conf, mask))
+        for l in range(self.layers):
+            q, k, v = qs[l], ks[l], vs[l]
+            if l < self.l_dense:
+                run("dense", lambda: self.dense_layer(l, q, k, v))
+                if l == self.l_dense - 1:
+                    run("sinks", lambda: self.sinks_at(q, k))
+            else:
+                if self.C:
+                    run("blocks", lambda: F.block_score_topc(q, k, self.P, self.bs, self.C,
+                                                            out=self.blocks[l], **self._rows()))
+                sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
+                blocks = self.blocks[l][:, : self.C] if self.C else None
+                run("sparse", lambda: F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs,
+                                                        out=self.out[l], **self._rows()))
+
+    def dense_refresh(self, qs, ks, vs, outs):
+        """A block-entry step: every query row of every layer attends to all L keys."""
+        for l in range(self.layers):
+            F.dense_attention(qs[l], ks[l], vs[l], out=outs[l], want_lse=False, scale=self.scale,
+                              workspace=self.workspace)

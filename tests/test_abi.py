@@ -61,7 +61,7 @@ def test_workspace_sizes():
     assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 32768) == 0
     # dense attention of <= 1024 active rows splits the 32K keys: partials in the workspace
     n = lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024)
-    assert n > 0 and n % ((128 + 2) * 4) == 0
+    assert n >= 2 * 32 * 1024 * (128 + 2) * 4     # at least two splits of fp32 partials
     assert lib.fdl_sparse_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128,
                                                      1024, 16, 64, 128) > 0
     assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024) == \
@@ -127,10 +127,10 @@ def test_dense_validation(kw, status):
 def test_sparse_and_sink_and_block_validation():
     lib = F.lib()
     st = S(4 * 256 * 128, 256 * 128, 128)
-    # sparse: too many sinks for the kernel's LDS bitmask
+    # sparse: the key list always needs a workspace
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
                                     FAKE, st, FAKE, 5000, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0,
-                                    None) == 7
+                                    None) == 5
     # sparse: P > L, bs < 1, block list missing
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 300, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
                                     FAKE, st, FAKE, 4, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
