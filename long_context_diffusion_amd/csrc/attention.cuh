@@ -50,6 +50,59 @@ inline int64_t sparse_key_bound(int L, int P, int n_sinks, int C, int bs) {
     return blk_keys + (L - P) + n_sinks;
 }
 
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of differences never sees inf-inf
+
+// Work units are (sequence b, KV head g, key split, query tile qt).  Only query tiles
+// that hold valid rows (from the device-side row counts) get a workgroup; the rest
+// of the grid exits at once.  A workgroup goes to XCD (blockIdx.x mod 8), so the
+// units are laid out such that all query tiles of one (b, g, split) group run on the
+// same XCD, one after another, and share that group's K/V tiles through its L2.
+struct WorkUnit {
+    int qt, split, g, b;
+    bool valid;
+};
+__device__ __forceinline__ WorkUnit decode_unit(const AttnArgs& a, int rows_per_tile) {
+    WorkUnit u;
+    u.valid = false;
+    u.qt = u.split = u.g = u.b = 0;
+    // query tiles with valid rows, per sequence (the same bound for every group of b)
+    int nqt_max = 0;
+    for (int b = 0; b < a.B; ++b) {
+        const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+        nqt_max = max(nqt_max, (a.Gq * nq + rows_per_tile - 1) / rows_per_tile);
+    }
+    if (nqt_max == 0) return u;
+    const int n_groups = a.B * a.Hkv * a.n_splits;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int grp = (slot / nqt_max) * 8 + xcd;
+    if (grp >= n_groups) return u;
+    u.qt = slot % nqt_max;
+    u.split = grp % a.n_splits;
+    u.g = (grp / a.n_splits) % a.Hkv;
+    u.b = grp / (a.n_splits * a.Hkv);
+    const int nq = a.n_q ? a.n_q[u.b] : a.nq_max;
+    u.valid = u.qt * rows_per_tile < a.Gq * nq;
+    return u;
+}
+
+template <typename T>
+__device__ __forceinline__ void write_zero_row(const AttnArgs& a, int b, int h, int r, int d) {
+    T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
+    for (int e = 0; e < d; ++e) orow[e] = T(0);
+    if (a.lse) a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] = -INFINITY;
+}
+
+
+// Keys of one sparse key set that the d = 128 kernel can map in LDS by itself.
+constexpr int kMapBlocks = 1024;
+constexpr int kMapSinks = 1024;
+__host__ __device__ inline bool sparse_map_in_lds(const AttnArgs& a) { return a.C <= kMapBlocks && a.n_sinks <= kMapSinks; }
+
+// The bf16, head-dim-128 attention kernel (attention_d128.hip).
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, dim3 grid, hipStream_t stream);
+
 AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_max,
                         int64_t key_bound, bool sparse);
 

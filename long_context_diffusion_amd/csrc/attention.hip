@@ -41,18 +41,23 @@ namespace fdl {
 
 namespace {
 
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of differences never sees inf-inf
 
 // ------------------------------------------------------------------ key list
 
+constexpr int kPrepBlocksLds = 2048;   // selected-block ids staged in LDS by attn_prep
+constexpr int kPrepListWgs = 8;        // workgroups per sequence writing the key list
+
+// grid (B, kPrepListWgs + padding workgroups).  y < kPrepListWgs: write a slice of the
+// key list (y == 0 also appends the uncovered sinks and |I_p|); y >= kPrepListWgs:
+// zero padding rows when there is no key split.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d) {
+__global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d, bool build_list) {
     __shared__ int s_tmp[17];
     __shared__ int s_carry;
+    __shared__ int s_blk[kPrepBlocksLds];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    if (blockIdx.y > 0) {
+    if (blockIdx.y >= kPrepListWgs) {
         // padding rows r in [n_q[b], nq_max) of every query head: O = 0, lse = -inf
         // (only without a key split: the split merge writes them otherwise)
         if (!a.n_q || a.n_splits > 1) return;
@@ -60,8 +65,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d)
         const int64_t pad_rows = static_cast<int64_t>(a.Hq) * (a.nq_max - nq);
         const int c4n = d / 4;
         const int64_t items = pad_rows * c4n;
-        for (int64_t it = static_cast<int64_t>(blockIdx.y - 1) * blockDim.x + tid; it < items;
-             it += static_cast<int64_t>(gridDim.y - 1) * blockDim.x) {
+        const int64_t nwg = gridDim.y - kPrepListWgs;
+        for (int64_t it = static_cast<int64_t>(blockIdx.y - kPrepListWgs) * blockDim.x + tid; it < items;
+             it += nwg * blockDim.x) {
             const int64_t row = it / c4n;
             const int c4 = static_cast<int>(it % c4n);
             const int h = static_cast<int>(row / (a.nq_max - nq));
@@ -72,23 +78,38 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d)
         }
         return;
     }
-    if (!a.sparse) return;
-    const int32_t* blk = a.block_idx + static_cast<int64_t>(b) * a.C;
+    if (!a.sparse || !build_list) return;
+    const int32_t* blk_g = a.block_idx + static_cast<int64_t>(b) * a.C;
+    const bool in_lds = a.C <= kPrepBlocksLds;
     int cnt = 0;
-    for (int c = tid; c < a.C; c += blockDim.x) cnt += blk[c] >= 0 ? 1 : 0;
+    for (int c = tid; c < a.C; c += blockDim.x) {
+        const int v = blk_g[c];
+        if (in_lds) s_blk[c] = v;
+        cnt += v >= 0 ? 1 : 0;
+    }
     int n_sel;
-    block_exclusive_sum(cnt, s_tmp, &n_sel);
+    block_exclusive_sum(cnt, s_tmp, &n_sel);   // also orders the s_blk writes before the reads
     n_sel = min(n_sel, a.nb);
+    const int32_t* blk = in_lds ? s_blk : blk_g;
     int n_blk = n_sel * a.bs;
     if (n_sel > 0 && blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;  // short last block
     int32_t* list = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
-    for (int pos = tid; pos < n_blk; pos += blockDim.x) {
-        const int c = pos / a.bs;
-        // block ids come from fdl_block_score_topc; clamping keeps a malformed list in bounds
-        list[pos] = min(max(blk[c] * a.bs + (pos - c * a.bs), 0), a.L - 1);
-    }
     const int G = a.L - a.P;
-    for (int i = tid; i < G; i += blockDim.x) list[n_blk + i] = a.P + i;
+    const int n_fixed = n_blk + G;
+    const int per = (n_fixed + kPrepListWgs - 1) / kPrepListWgs;
+    const int lo = blockIdx.y * per, hi = min(n_fixed, lo + per);
+    for (int pos = lo + tid; pos < hi; pos += blockDim.x) {
+        int key;
+        if (pos < n_blk) {
+            const int c = pos / a.bs;
+            // block ids come from fdl_block_score_topc; clamping keeps a malformed list in bounds
+            key = min(max(blk[c] * a.bs + (pos - c * a.bs), 0), a.L - 1);
+        } else {
+            key = a.P + (pos - n_blk);
+        }
+        list[pos] = key;
+    }
+    if (blockIdx.y != 0) return;
     if (tid == 0) s_carry = 0;
     __syncthreads();
     const int32_t* snk = a.sink_idx + static_cast<int64_t>(b) * a.n_sinks;
@@ -101,104 +122,93 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d)
             take = j >= 0 && j < a.P && (s == 0 || snk[s - 1] != j);
             if (take) {  // already in a selected block?  (selected blocks ascend)
                 const int target = j / a.bs;
-                int lo = 0, hi = n_sel;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (blk[mid] < target) lo = mid + 1; else hi = mid;
+                int l = 0, h = n_sel;
+                while (l < h) {
+                    const int mid = (l + h) >> 1;
+                    if (blk[mid] < target) l = mid + 1; else h = mid;
                 }
-                take = !(lo < n_sel && blk[lo] == target);
+                take = !(l < n_sel && blk[l] == target);
             }
         }
         int total;
         const int off = block_exclusive_sum(take ? 1 : 0, s_tmp, &total) + s_carry;
-        if (take) list[n_blk + G + off] = j;
+        if (take) list[n_fixed + off] = j;
         __syncthreads();
         if (tid == 0) s_carry += total;
         __syncthreads();
     }
-    if (tid == 0) a.n_keys[b] = n_blk + G + s_carry;
+    if (tid == 0) a.n_keys[b] = n_fixed + s_carry;
 }
 
-// Work units are (sequence b, KV head g, key split, query tile qt).  Only query tiles
-// that hold valid rows (from the device-side row counts) get a workgroup; the rest
-// of the grid exits at once.  A workgroup goes to XCD (blockIdx.x mod 8), so the
-// units are laid out such that all query tiles of one (b, g, split) group run on the
-// same XCD, one after another, and share that group's K/V tiles through its L2.
-struct WorkUnit {
-    int qt, split, g, b;
-    bool valid;
-};
-__device__ __forceinline__ WorkUnit decode_unit(const AttnArgs& a, int rows_per_tile) {
-    WorkUnit u;
-    u.valid = false;
-    u.qt = u.split = u.g = u.b = 0;
-    // query tiles with valid rows, per sequence (the same bound for every group of b)
-    int nqt_max = 0;
-    for (int b = 0; b < a.B; ++b) {
-        const int nq = a.n_q ? a.n_q[b] : a.nq_max;
-        nqt_max = max(nqt_max, (a.Gq * nq + rows_per_tile - 1) / rows_per_tile);
-    }
-    if (nqt_max == 0) return u;
-    const int n_groups = a.B * a.Hkv * a.n_splits;
-    const int id = blockIdx.x;
-    const int xcd = id & 7, slot = id >> 3;
-    const int grp = (slot / nqt_max) * 8 + xcd;
-    if (grp >= n_groups) return u;
-    u.qt = slot % nqt_max;
-    u.split = grp % a.n_splits;
-    u.g = (grp / a.n_splits) % a.Hkv;
-    u.b = grp / (a.n_splits * a.Hkv);
-    const int nq = a.n_q ? a.n_q[u.b] : a.nq_max;
-    u.valid = u.qt * rows_per_tile < a.Gq * nq;
-    return u;
-}
-
-template <typename T>
-__device__ __forceinline__ void write_zero_row(const AttnArgs& a, int b, int h, int r, int d) {
-    T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
-    for (int e = 0; e < d; ++e) orow[e] = T(0);
-    if (a.lse) a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] = -INFINITY;
-}
-
-// Merge of the key-range splits: one wave per output row (b, h, r).  Valid rows get
+// Merge of the key-range splits.  Each thread owns 8 elements of one output row
+// (b, h, r); its loads of the running maxima/sums and of the partial outputs are
+// independent, so a row costs one memory round trip.  Valid rows get
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s in split order; padding rows
 // (r >= n_q[b]) are written as zero with lse = -inf.
+constexpr int kMergeEpt = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
-    constexpr int EPL = D / 64;   // elements per lane
-    const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    constexpr int TPR = D / kMergeEpt;              // threads per row
+    constexpr int RPW = 256 / TPR;                  // rows per workgroup
+    constexpr int kMaxSplits = 16;
+    const int sub = threadIdx.x % TPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPW + threadIdx.x / TPR;
     const int64_t n_rows = static_cast<int64_t>(a.B) * a.Hq * a.nq_max;
     if (row >= n_rows) return;
     const int r = static_cast<int>(row % a.nq_max);
     const int h = static_cast<int>((row / a.nq_max) % a.Hq);
     const int b = static_cast<int>(row / (static_cast<int64_t>(a.nq_max) * a.Hq));
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
-    T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr + EPL * lane;
-    if (r >= nq) {
+    T* orow = static_cast<T*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr + kMergeEpt * sub;
+    float o[kMergeEpt];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) orow[e] = T(0);
-        if (a.lse && lane == 0) a.lse[row] = -INFINITY;
-        return;
+    for (int e = 0; e < kMergeEpt; ++e) o[e] = 0.0f;
+    float M = kNegBig, Lsum = 0.0f;
+    if (r < nq) {
+        const int ns = min(a.n_splits, kMaxSplits);
+        const float* ml = a.part_ml + row * a.n_splits * 2;
+        const float* po = a.part_o + row * a.n_splits * D + kMergeEpt * sub;
+        float m[kMaxSplits], l[kMaxSplits];
+        f32x4 x[kMaxSplits][2];
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            if (s < ns) {
+                m[s] = ml[2 * s];
+                l[s] = ml[2 * s + 1];
+                x[s][0] = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(s) * D);
+                x[s][1] = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(s) * D + 4);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < ns) M = fmaxf(M, m[s]);
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            if (s < ns) {
+                const float w = exp2f(m[s] - M);
+                Lsum = fmaf(l[s], w, Lsum);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[e] = fmaf(x[s][0][e], w, o[e]);
+                    o[4 + e] = fmaf(x[s][1][e], w, o[4 + e]);
+                }
+            }
+        }
+        const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+#pragma unroll
+        for (int e = 0; e < kMergeEpt; ++e) o[e] *= inv;
     }
-    const float* ml = a.part_ml + row * a.n_splits * 2;
-    const float* po = a.part_o + row * a.n_splits * D + EPL * lane;
-    float M = kNegBig;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float Lsum = 0.0f;
-    float o[EPL];
+    if (sizeof(T) == 2) {
+        u32x4 w;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
-    for (int s = 0; s < a.n_splits; ++s) {
-        const float w = exp2f(ml[2 * s] - M);
-        Lsum = fmaf(ml[2 * s + 1], w, Lsum);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+        *reinterpret_cast<u32x4*>(orow) = w;
+    } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = fmaf(po[static_cast<int64_t>(s) * D + e], w, o[e]);
+        for (int e = 0; e < kMergeEpt; ++e) Elem<T>::store(orow + e, o[e]);
     }
-    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) Elem<T>::store(orow + e, o[e] * inv);
-    if (a.lse && lane == 0) a.lse[row] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+    if (a.lse && sub == 0)
+        a.lse[row] = (r < nq && Lsum > 0.0f) ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
@@ -375,13 +385,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[1][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx * a.sl2);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = fast_exp2(m_run - m_new);
         float psum = 0.0f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float pv = exp2f(fmaf(st[kb2][i], a.sl2, -m_new));
+                const float pv = fast_exp2(fmaf(st[kb2][i], a.sl2, -m_new));
                 st[kb2][i] = pv;
                 psum += pv;
             }
@@ -579,7 +589,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
 
 template <int D>
 void launch_kernel(fdl_dtype dtype, const AttnArgs& a, dim3 grid, hipStream_t stream) {
-    if (dtype == FDL_BF16) {
+    if (dtype == FDL_BF16 && D == 128) {
+        launch_attn_bf16_d128(a, grid, stream);
+    } else if (dtype == FDL_BF16) {
         if (a.sparse) hipLaunchKernelGGL((attn_bf16_kernel<D, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((attn_bf16_kernel<D, false>), grid, dim3(256), 0, stream, a);
     } else {
@@ -607,6 +619,7 @@ AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_m
     int64_t splits = (target + units - 1) / units;
     const int64_t max_splits = tiles / min_tiles > 1 ? tiles / min_tiles : 1;
     if (splits > max_splits) splits = max_splits;
+    if (splits > 16) splits = 16;   // attn_merge holds at most 16 splits per row in registers
     if (splits < 1) splits = 1;
     pl.n_splits = static_cast<int>(splits);
     pl.tiles_per_split = static_cast<int>((tiles + splits - 1) / splits);
@@ -639,11 +652,13 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     a.part_o = pl.part_bytes ? reinterpret_cast<float*>(ws + pl.list_bytes) : nullptr;
     a.part_ml = a.part_o ? a.part_o + static_cast<int64_t>(a.B) * a.Hq * a.nq_max * pl.n_splits * d : nullptr;
     const bool zero_pad = a.n_q && pl.n_splits == 1;
-    if (a.sparse || zero_pad) {
+    // the bf16 d = 128 kernel maps small sparse key sets itself; everything else reads the list
+    const bool need_list = a.sparse && !(dtype == FDL_BF16 && d == 128 && sparse_map_in_lds(a));
+    if (need_list || zero_pad) {
         const int pad_wgs = zero_pad ? 64 : 0;   // extra workgroups that zero the padding rows
-        const dim3 pgrid(a.B, 1 + pad_wgs);
-        if (dtype == FDL_BF16) hipLaunchKernelGGL(attn_prep_kernel<uint16_t>, pgrid, dim3(256), 0, stream, a, d);
-        else hipLaunchKernelGGL(attn_prep_kernel<float>, pgrid, dim3(256), 0, stream, a, d);
+        const dim3 pgrid(a.B, kPrepListWgs + pad_wgs);
+        if (dtype == FDL_BF16) hipLaunchKernelGGL(attn_prep_kernel<uint16_t>, pgrid, dim3(256), 0, stream, a, d, need_list);
+        else hipLaunchKernelGGL(attn_prep_kernel<float>, pgrid, dim3(256), 0, stream, a, d, need_list);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -655,7 +670,8 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.n_splits == 1) return err;
     const int64_t n_rows = static_cast<int64_t>(a.B) * a.Hq * a.nq_max;
-    const dim3 mgrid(static_cast<unsigned>((n_rows + 3) / 4));
+    const int64_t rows_per_wg = 256 / (d / kMergeEpt);
+    const dim3 mgrid(static_cast<unsigned>((n_rows + rows_per_wg - 1) / rows_per_wg));
     if (dtype == FDL_BF16) {
         if (d == 128) hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 128>), mgrid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 64>), mgrid, dim3(256), 0, stream, a);

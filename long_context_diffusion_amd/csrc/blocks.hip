@@ -27,7 +27,7 @@ namespace fdl {
 
 namespace {
 
-constexpr int kQsumThreads = 512;
+constexpr int kQsumThreads = 1024;
 constexpr int kScanThreads = 256;
 
 template <typename T>
@@ -61,23 +61,23 @@ __global__ __launch_bounds__(kQsumThreads) void block_qsum_kernel(const BlockArg
     double acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
-    constexpr int kBatch = 4;
+    // all row indices of a batch first, then all rows: two memory round trips per batch
+    constexpr int kBatch = 16;
     for (int p0 = rg; p0 < rows; p0 += RG * kBatch) {
-        u32x4 x[kBatch];
-        bool ok[kBatch];
+        int64_t off[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int p = p0 + u * RG;
-            ok[u] = p < rows;
-            const int pc = ok[u] ? p : rg;
-            const int h = g * a.Gq + pc % a.Gq, r = pc / a.Gq;
-            const int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + r] : r;
-            x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + b * a.qsb + h * a.qsh +
-                                                  static_cast<int64_t>(phys) * a.qsr + piece * EPP);
+            const int p = min(p0 + u * RG, rows - 1);
+            const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
+            const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
+            off[u] = b * a.qsb + h * a.qsh + static_cast<int64_t>(phys) * a.qsr + piece * EPP;
         }
+        u32x4 x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + off[u]);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (!ok[u]) continue;
+            if (p0 + u * RG >= rows) continue;
             float v[EPP];
             unpack16<T>(x[u], v);
 #pragma unroll
@@ -87,11 +87,15 @@ __global__ __launch_bounds__(kQsumThreads) void block_qsum_kernel(const BlockArg
 #pragma unroll
     for (int e = 0; e < EPP; ++e) s_part[rg][piece * EPP + e] = acc[e];
     __syncthreads();
-    for (int e = tid; e < D; e += kQsumThreads) {
-        double s = 0.0;
-        for (int i = 0; i < RG; ++i) s += s_part[i][e];
-        a.qsum[(static_cast<int64_t>(b) * a.Hkv + g) * D + e] = s;
+    // pairwise tree over the row groups (fixed order, so the sum is deterministic)
+    for (int half = RG / 2; half >= 1; half >>= 1) {
+        for (int i = tid; i < half * D; i += kQsumThreads) {
+            const int r = i / D, e = i % D;
+            s_part[r][e] += s_part[r + half][e];
+        }
+        __syncthreads();
     }
+    for (int e = tid; e < D; e += kQsumThreads) a.qsum[(static_cast<int64_t>(b) * a.Hkv + g) * D + e] = s_part[0][e];
 }
 
 __device__ __forceinline__ double wave_sum_f64(double x) {
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kScanThreads) void block_scan_kernel(const BlockArg
 
 constexpr int kSelectLds = 2048;   // blocks ranked in LDS
 
-__global__ __launch_bounds__(1024) void block_select_kernel(const BlockArgs a, int C, int32_t* block_idx,
+__global__ __launch_bounds__(256) void block_select_kernel(const BlockArgs a, int C, int32_t* block_idx,
                                                             double* R_out) {
     __shared__ SelectSmem sm;
     __shared__ uint64_t s_key[kSelectLds];
@@ -259,7 +263,7 @@ hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, i
 #undef FDL_SCAN
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(1024), 0, stream, a, C, block_idx, R_out);
+    hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(256), 0, stream, a, C, block_idx, R_out);
     return hipGetLastError();
 }
 

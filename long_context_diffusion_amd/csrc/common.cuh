@@ -46,6 +46,11 @@ template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
     }
 };
 
+// 2^x on the transcendental unit (v_exp_f32).  Results below 2^-126 flush to zero,
+// which is harmless for softmax weights and saves the denormal-range fix-up that
+// the libm exp2f wraps around the instruction.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------ ordered keys
 
 // Monotone map of a float to uint32: a < b  <=>  okey(a) < okey(b); -0.0 maps like +0.0.
@@ -102,9 +107,11 @@ __device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
 // loads the key of entry j and returns whether j takes part; it must be safe to call
 // for every j in [0, n).  Keys are read in batches of independent loads.
 
-// Shared scratch for the selection helpers.
+// Shared scratch for the selection helpers.  Each wave counts into its own histogram
+// (skewed keys would otherwise pile every atomic onto one or two LDS words).
+constexpr int kMaxWaves = 16;
 struct SelectSmem {
-    int hist[256];
+    int hist[kMaxWaves][256];
     int tmp[17];
     int digit;
     int remaining;
@@ -145,18 +152,21 @@ __device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
     int remaining = k;
     int lo, hi;
     thread_chunk(n, &lo, &hi);
+    const int nw = blockDim.x / kWave;
+    const int wv = threadIdx.x / kWave;
     for (int shift = kBits - 8; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) sm->hist[i] = 0;
+        for (int i = threadIdx.x; i < nw * 256; i += blockDim.x) sm->hist[i / 256][i % 256] = 0;
         __syncthreads();
         for_each_key<U>(lo, hi, key_of, [&](int, U kj) {
-            if ((kj & prefix_mask) == prefix) atomicAdd(&sm->hist[static_cast<int>((kj >> shift) & 0xff)], 1);
+            if ((kj & prefix_mask) == prefix) atomicAdd(&sm->hist[wv][static_cast<int>((kj >> shift) & 0xff)], 1);
         });
         __syncthreads();
         if (threadIdx.x < kWave) {
             // lane l owns bins 4l..4l+3; find the bin holding the remaining-th largest
             const int l = threadIdx.x;
-            int h[4];
-            for (int q = 0; q < 4; ++q) h[q] = sm->hist[4 * l + q];
+            int h[4] = {0, 0, 0, 0};
+            for (int w = 0; w < nw; ++w)
+                for (int q = 0; q < 4; ++q) h[q] += sm->hist[w][4 * l + q];
             const int mine = h[0] + h[1] + h[2] + h[3];
             int suffix = mine;  // sum over lanes >= l
             for (int off = 1; off < kWave; off <<= 1) {
@@ -243,7 +253,15 @@ __device__ int block_topk_lds(int n, int k, const U* keys, IdxFn idx_of, int32_t
     for (int j = lo; j < hi; ++j) {
         const U kj = keys[j];
         int rank = 0;
-        for (int i = 0; i < n; ++i) {
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {   // eight independent LDS reads in flight
+            U ki[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ki[u] = keys[i + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += (ki[u] > kj || (ki[u] == kj && i + u < j)) ? 1 : 0;
+        }
+        for (; i < n; ++i) {
             const U ki = keys[i];
             rank += (ki > kj || (ki == kj && i < j)) ? 1 : 0;
         }

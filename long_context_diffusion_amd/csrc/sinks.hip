@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs
                     sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kg][c], sc, 0, 0, 0);
                 }
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[kg] += exp2f(fmaf(sc[e], a.sl2, -lrow[e]));
+                for (int e = 0; e < 16; ++e) acc[kg] += fast_exp2(fmaf(sc[e], a.sl2, -lrow[e]));
             }
             lse_next = lse_pref;
             store_block(buf ^ 1);
