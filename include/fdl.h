@@ -25,7 +25,8 @@
  *   - dtype (fdl_dtype) is shared by Q, K, V and O: FDL_F32, or FDL_BF16 with fp32
  *     accumulation.  Head dim d is 64 or 128 and is contiguous in memory.
  *     Q, K, V and O are addressed as base + b*s.b + h*s.h + row*s.r (element
- *     strides, fdl_strides); each row must start on a 16-byte boundary.
+ *     strides, fdl_strides); each row must start on a 16-byte boundary, and the
+ *     row stride must lie below 2^31 elements in magnitude (FDL_ERR_SHAPE).
  *   - Query rows: the logical query row r of sequence b reads the physical row
  *     q_idx[b*nq_max + r] of Q when q_idx is non-NULL (e.g. the active_idx output
  *     of fdl_pcgi_select), else row r.  Rows r >= n_q[b] are padding (n_q NULL:

@@ -22,14 +22,15 @@ fdl_status check_dtype_dims(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d) 
     return FDL_OK;
 }
 
-// Row starts base + b*s.b + h*s.h + r*s.r must be 16-byte aligned, and d contiguous elements
-// must fit between rows (|s.r| >= d) unless there is a single row.
+// Row starts base + b*s.b + h*s.h + r*s.r must be 16-byte aligned, d contiguous elements
+// must fit between rows (|s.r| >= d) and the row stride must be below 2^31 elements.
 fdl_status check_tensor(const void* p, fdl_strides s, fdl_dtype dt, int d) {
     if (!p) return FDL_ERR_NULL;
     if (!aligned16(p)) return FDL_ERR_ALIGN;
     const int64_t e = static_cast<int64_t>(elem_size(dt));
     if ((s.b * e) % 16 || (s.h * e) % 16 || (s.r * e) % 16) return FDL_ERR_ALIGN;
     if (s.r < d && s.r > -d) return FDL_ERR_SHAPE;
+    if (s.r >= (1ll << 31) || s.r <= -(1ll << 31)) return FDL_ERR_SHAPE;
     return FDL_OK;
 }
 

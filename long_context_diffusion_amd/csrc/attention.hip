@@ -165,18 +165,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     for (int e = 0; e < kMergeEpt; ++e) o[e] = 0.0f;
     float M = kNegBig, Lsum = 0.0f;
     if (r < nq) {
-        const int ns = min(a.n_splits, kMaxSplits);
-        const float* ml = a.part_ml + row * a.n_splits * 2;
-        const float* po = a.part_o + row * a.n_splits * D + kMergeEpt * sub;
+        // partial of split s at index base + s * step (per row, or per work item when the
+        // persistent kernel chose the split count)
+        int ns = min(a.n_splits, kMaxSplits);
+        int64_t base = row * a.n_splits, step = 1;
+        if (a.dyn) {
+            const int nqt_max = valid_q_tiles(a, kD128Rows);
+            ns = dyn_splits(a, nqt_max);
+            if (ns == 1) return;   // the attention kernel wrote this row itself
+            const int g = h / a.Gq;
+            const int p = r * a.Gq + (h - g * a.Gq);
+            base = d128_part_index(a, nqt_max, ns, b, g, 0, p);
+            step = static_cast<int64_t>(nqt_max) * kD128Rows;
+        }
         float m[kMaxSplits], l[kMaxSplits];
         f32x4 x[kMaxSplits][2];
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
             if (s < ns) {
-                m[s] = ml[2 * s];
-                l[s] = ml[2 * s + 1];
-                x[s][0] = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(s) * D);
-                x[s][1] = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(s) * D + 4);
+                const int64_t idx = base + s * step;
+                m[s] = a.part_ml[2 * idx];
+                l[s] = a.part_ml[2 * idx + 1];
+                const float* po = a.part_o + idx * D + kMergeEpt * sub;
+                x[s][0] = *reinterpret_cast<const f32x4*>(po);
+                x[s][1] = *reinterpret_cast<const f32x4*>(po + 4);
             }
         }
 #pragma unroll
@@ -589,9 +601,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
 
 template <int D>
 void launch_kernel(fdl_dtype dtype, const AttnArgs& a, dim3 grid, hipStream_t stream) {
-    if (dtype == FDL_BF16 && D == 128) {
-        launch_attn_bf16_d128(a, grid, stream);
-    } else if (dtype == FDL_BF16) {
+    if (dtype == FDL_BF16) {
         if (a.sparse) hipLaunchKernelGGL((attn_bf16_kernel<D, true>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((attn_bf16_kernel<D, false>), grid, dim3(256), 0, stream, a);
     } else {
@@ -608,18 +618,26 @@ AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_m
                         int64_t key_bound, bool sparse) {
     AttnPlan pl;
     const bool bf16 = dtype == FDL_BF16;
-    pl.rows_per_tile = bf16 ? 128 : kF32Rows;
+    const bool d128 = bf16 && d == 128;
+    pl.rows_per_tile = d128 ? kD128Rows : bf16 ? 128 : kF32Rows;
     pl.tile_keys = bf16 ? 64 : kF32Keys;
     const int64_t rows = static_cast<int64_t>(Hq / Hkv) * nq_max;
     pl.q_tiles = static_cast<int>((rows + pl.rows_per_tile - 1) / pl.rows_per_tile);
     const int64_t tiles = (key_bound + pl.tile_keys - 1) / pl.tile_keys;
+    pl.tiles_total = static_cast<int>(tiles > 0 ? tiles : 1);
     const int64_t units = static_cast<int64_t>(B) * Hkv * pl.q_tiles;
-    const int64_t target = 1024;  // workgroups that keep 256 CUs busy
-    const int64_t min_tiles = 8;  // keep each split long enough to amortise its merge
-    int64_t splits = (target + units - 1) / units;
-    const int64_t max_splits = tiles / min_tiles > 1 ? tiles / min_tiles : 1;
-    if (splits > max_splits) splits = max_splits;
-    if (splits > 16) splits = 16;   // attn_merge holds at most 16 splits per row in registers
+    const int64_t max_splits = tiles / kMinSplitTiles > 1 ? tiles / kMinSplitTiles : 1;
+    int64_t splits;
+    if (d128) {
+        // the kernel picks the split count on the device (it knows the valid rows);
+        // the workspace covers the most it can pick
+        splits = max_splits < 16 ? max_splits : 16;
+    } else {
+        const int64_t target = 1024;  // workgroups that keep 256 CUs busy
+        splits = (target + units - 1) / units;
+        if (splits > max_splits) splits = max_splits;
+        if (splits > 16) splits = 16;   // attn_merge holds at most 16 splits per row in registers
+    }
     if (splits < 1) splits = 1;
     pl.n_splits = static_cast<int>(splits);
     pl.tiles_per_split = static_cast<int>((tiles + splits - 1) / splits);
@@ -628,7 +646,13 @@ AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_m
     pl.list_bytes = sparse ? round_up(static_cast<size_t>(B) * (key_bound + 1) * sizeof(int32_t), 256) : 0;
     pl.part_bytes = 0;
     if (pl.n_splits > 1) {
-        const int64_t nrows = static_cast<int64_t>(B) * Hq * nq_max * pl.n_splits;
+        int64_t nrows;
+        if (d128) {
+            const int64_t items = units * pl.n_splits;
+            nrows = (items < kD128MaxSlots ? items : kD128MaxSlots) * kD128Rows;
+        } else {
+            nrows = static_cast<int64_t>(B) * Hq * nq_max * pl.n_splits;
+        }
         pl.part_bytes = static_cast<size_t>(nrows) * (d + 2) * sizeof(float);
     }
     pl.ws_bytes = pl.list_bytes + pl.part_bytes;
@@ -650,7 +674,12 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
         a.n_keys = a.kv_list + static_cast<int64_t>(a.B) * pl.key_cap;
     }
     a.part_o = pl.part_bytes ? reinterpret_cast<float*>(ws + pl.list_bytes) : nullptr;
-    a.part_ml = a.part_o ? a.part_o + static_cast<int64_t>(a.B) * a.Hq * a.nq_max * pl.n_splits * d : nullptr;
+    a.part_ml = a.part_o ? a.part_o + static_cast<int64_t>(pl.part_bytes / ((d + 2) * sizeof(float))) * d : nullptr;
+    a.tiles_total = pl.tiles_total;
+    a.bs_magic = a.bs >= 2 ? static_cast<uint32_t>(((uint64_t(1) << 32) + a.bs - 1) / a.bs) : 0u;
+    const bool d128 = dtype == FDL_BF16 && d == 128;
+    a.dyn = d128 ? 1 : 0;
+    a.slots = d128 ? d128_slots() : 0;
     const bool zero_pad = a.n_q && pl.n_splits == 1;
     // the bf16 d = 128 kernel maps small sparse key sets itself; everything else reads the list
     const bool need_list = a.sparse && !(dtype == FDL_BF16 && d == 128 && sparse_map_in_lds(a));
@@ -665,7 +694,8 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     // groups of q_tiles consecutive slots per XCD: round the group count up to a multiple of 8
     const int64_t groups = static_cast<int64_t>(a.B) * a.Hkv * pl.n_splits;
     const dim3 grid(static_cast<unsigned>((groups + 7) / 8 * 8 * pl.q_tiles));
-    if (d == 128) launch_kernel<128>(dtype, a, grid, stream);
+    if (d128) launch_attn_bf16_d128(a, stream);
+    else if (d == 128) launch_kernel<128>(dtype, a, grid, stream);
     else launch_kernel<64>(dtype, a, grid, stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || pl.n_splits == 1) return err;

@@ -1,31 +1,33 @@
-// bf16 attention, head dim 128: dense or sparse key set, software-pipelined.
+// bf16 attention, head dim 128: dense or sparse key set.
 //
 // Focus-dLLM structured summary (paper.rainbus.top/paper/2602.02159), "Method
 // steps" (3) and (5): dense attention of the active rows (and of every row at a
 // block-entry refresh), and attention of the active rows over I_p only.
 //
-// Per workgroup: 4 waves x 32 query rows of one KV head (grouped-query heads
-// interleaved into the rows), 64-key tiles.
-//   * K and V tiles go from global memory straight into LDS (global_load_lds,
-//     16 bytes per lane), with no staging registers.  Rows are 256 bytes and
-//     unpadded; the 16-byte chunk c of row r sits at slot c ^ 2*(r & 7), which
-//     keeps both LDS read patterns below free of bank conflicts.
-//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16, keys on the M axis): one lane owns
-//     one query's softmax state.
-//   * O^T += V^T P^T: V stays row-major in LDS and the V^T operand is read with
-//     ds_read_b64_tr_b16.  In each 16-lane group, lane j points at 4 consecutive
-//     d of key key0 + j/4; lane i then receives keys key0..key0+3 at d0 + i, the
-//     4 k-slots the MFMA wants.  Two such reads fill one 8-slot operand, whose key
-//     order matches the accumulator layout of S^T, so P needs no shuffle.
-//   * Pipeline: S for tile t+1 is computed while tile t's softmax and P V run;
-//     K runs one tile ahead of V (K tiles t+1, t+2 and V tiles t, t+1 in LDS);
-//     the loads for the next tiles are in flight during the whole iteration, and
-//     one barrier closes it.
-//   * Key indices reach the loads through a 4-deep ring in LDS filled by wave 0:
-//     dense keys are t*64 + row; sparse keys are mapped in-kernel from LDS copies
-//     of the selected blocks and of the sinks that no block or the generation
-//     region holds (or read from the list written by attn_prep when those sets are
-//     too large for LDS).
+// A workgroup (8 waves x 32 query rows of one KV head; grouped-query heads are
+// interleaved into the rows) walks a range of 64-key tiles, one workgroup per CU
+// (two waves per SIMD).  The grid is persistent: it walks (query tile, key split)
+// items, and the number of key splits comes from the device-side row counts, so a
+// sparse step with few active rows still fills every CU.
+//   * K and V tiles go from global memory straight into LDS (global_load_lds, 16
+//     bytes per lane) through a 3-deep ring: while tile t is finished, K and V of
+//     tiles t+2 and t+3 are in flight, so every load has two iterations to land.
+//     Rows are 256 bytes, unpadded; 16-byte chunk c of LDS row r of K sits at slot
+//     c ^ (r & 15), which makes the 128-bit reads of S = K Q^T conflict-free.  One
+//     DMA instruction fills 4 LDS rows, and a lane's 2 rows of a tile hold 2
+//     consecutive key positions, so every lane maps its own keys: no index ring, no
+//     wave waiting on another.
+//   * Each V tile is transposed once, in LDS, one tile ahead of its use: every lane
+//     turns 2 rows x 8 d into 8 words of V^T.  P V then reads V^T with
+//     conflict-free 128-bit reads (transposing LDS reads of the row-major tile run
+//     at about a third of that rate on gfx950).
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16, keys on the M axis): one lane owns one
+//     query's softmax state.  S of tile t+1 is computed while tile t is finished.
+//   * O^T += V^T P^T, with the V^T slots ordered like the rows of the S^T
+//     accumulator, so P goes to the MFMA straight from the softmax registers.
+//   * The running max is only raised when a tile's max exceeds it by more than 2^8
+//     (exp2 units), so rescaling the accumulators is rare; the final
+//     normalisation is exact either way.
 
 #include "attention.cuh"
 
@@ -37,51 +39,99 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRowB = 256;             // bytes per K/V row in LDS
-constexpr int kTileB = 64 * kRowB;     // one 64-key tile: 16 KB
+constexpr int kRowB = 256;           // bytes per K/V row in LDS
+constexpr int kTileB = 64 * kRowB;   // one 64-key tile: 16 KB
+constexpr float kSlack = 8.0f;       // max growth (log2 units) tolerated before a rescale
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row & 7) << 1); }
+// key sets: every key of [0, L); I_p mapped from LDS copies of its parts; I_p read
+// from the list attn_prep wrote (parts too large for LDS)
+enum KeyMode { kDense = 0, kSparseLds = 1, kSparseList = 2 };
 
-template <bool SPARSE>
-__global__ __launch_bounds__(256, 2) void attn_d128_kernel(const AttnArgs a) {
-    constexpr int D = 128;
-    constexpr int NQC = D / 16;   // 16-wide d chunks of Q . K
-    constexpr int NDB = D / 32;   // 32-wide d blocks of the output
-    // four separate LDS objects, so the compiler can tell a tile being loaded by DMA
-    // from the tiles being read (one shared array would force a wait on every read)
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+// V^T tile: 128 rows (d) of 128 bytes.  Slot s (0..63) of row d holds V of LDS row
+// vt_row(s), which swaps bits 2 and 3 of s: the 8 slots of 16-byte chunk 2kc + hf then
+// hold S^T rows 16kc + 8(j/4) + 4hf + j%4, j = 0..7, the order a lane's P fragment
+// has.  Chunk c of row d sits at c ^ ((d >> 1) & 7), so 16 consecutive rows read at
+// one chunk hit distinct banks.
+__device__ __forceinline__ int vt_row(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+__device__ __forceinline__ int vt_off(int d, int s) { return d * 128 + 16 * ((s >> 3) ^ ((d >> 1) & 7)) + 2 * (s & 7); }
+
+// key position (within the tile) held by LDS row r: rows 8w + 4i + g hold 8w + 2g + i
+__device__ __forceinline__ int row_pos(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// floor(n / d) for 0 <= n < 2^30 and d >= 1, with m = ceil(2^32 / d) for d >= 2.
+__device__ __forceinline__ int div_magic(int n, int d, uint32_t m) {
+    if (d == 1) return n;
+    uint32_t q = __umulhi(static_cast<uint32_t>(n), m);   // floor(n/d) or one more
+    if (q * static_cast<uint32_t>(d) > static_cast<uint32_t>(n)) --q;
+    return static_cast<int>(q);
+}
+
+// Workgroup barrier that leaves this wave's newest `keep` loads in flight: LDS reads
+// have returned and every older load (LDS DMA included) has landed.  A plain
+// __syncthreads() would also wait for the newest loads: its release fence drains
+// every outstanding memory operation.
+template <int keep>
+__device__ __forceinline__ void barrier_keep() {
+    static_assert(keep >= 0 && keep < 16, "vmcnt field");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(keep | (7 << 4));   // vmcnt(keep) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The value this lane's partner (lane ^ 32) holds.
+__device__ __forceinline__ float xhalf(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
+    constexpr int NQC = 8;   // 16-wide d chunks of Q . K
+    constexpr int NDB = 4;   // 32-wide d blocks of the output
+    // separate LDS objects for every tile buffer: the compiler tells a tile being loaded by DMA from the
+    // tiles being read only when they are different objects
+    __shared__ __attribute__((aligned(1024))) uint8_t s_t0[kTileB];   // V^T tiles
+    __shared__ __attribute__((aligned(1024))) uint8_t s_t1[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_t2[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kTileB];   // row-major V tiles
+    __shared__ __attribute__((aligned(1024))) uint8_t s_v1[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_v2[kTileB];
     __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kTileB];
     __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kTileB];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kTileB];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_v1[kTileB];
-    __shared__ int s_kidx[4][64];
-    __shared__ int s_blk[SPARSE ? kMapBlocks : 1];
-    __shared__ int s_unc[SPARSE ? kMapSinks : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_k2[kTileB];
+    __shared__ int s_blk[MODE == kSparseLds ? kMapBlocks : 1];
+    __shared__ int s_unc[MODE == kSparseLds ? kMapSinks : 1];
     __shared__ int s_tmp[17];
     __shared__ int s_carry;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5;
     const int col = lane & 31;
-    const WorkUnit u = decode_unit(a, 128);
-    if (!u.valid) return;
-    const int b = u.b, g = u.g;
-    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
-    const int rows_valid = a.Gq * nq;
-    const int rows_all = a.Gq * a.nq_max;
-    const int p0 = u.qt * 128;
-    const int p = p0 + wv * 32 + col;
-    const bool row_ok = p < rows_valid;
-    const int h = g * a.Gq + p % a.Gq;
-    const int r = p / a.Gq;
+    const int g4 = lane >> 4;
 
-    // ---- key set of this sequence
-    int n_keys = a.L, n_blk = 0, sink0 = a.L;
-    const bool in_lds = !SPARSE || sparse_map_in_lds(a);
-    const int32_t* klist = nullptr;
-    if (SPARSE) {
-        if (in_lds) {
+    const int nqt_max = valid_q_tiles(a, kD128Rows);
+    const int n_splits = dyn_splits(a, nqt_max);
+    const int tps = (a.tiles_total + n_splits - 1) / n_splits;
+    const int n_items = (a.B * a.Hkv * n_splits + 7) / 8 * 8 * nqt_max;
+    const int rows_all = a.Gq * a.nq_max;
+
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const WorkUnit u = decode_unit_id(a, kD128Rows, item, n_splits, nqt_max);
+        if (!u.valid) continue;
+        __syncthreads();   // the previous item's readers of the LDS maps are done
+        const int b = u.b, g = u.g;
+        const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+        const int rows_valid = a.Gq * nq;
+
+        // ---- key set of this sequence: n_keys positions; blocks first, then [P, L),
+        // then the sinks no selected block holds
+        int n_keys = a.L, n_blk = 0, sink0 = a.L;
+        const int32_t* klist = nullptr;
+        if (MODE == kSparseLds) {
             const int32_t* blk_g = a.block_idx + static_cast<int64_t>(b) * a.C;
             int cnt = 0;
             for (int c = tid; c < a.C; c += blockDim.x) {
@@ -123,223 +173,284 @@ __global__ __launch_bounds__(256, 2) void attn_d128_kernel(const AttnArgs a) {
                 __syncthreads();
             }
             n_keys = sink0 + s_carry;
-        } else {
+        } else if (MODE == kSparseList) {
             n_keys = a.n_keys[b];
             klist = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
         }
-    }
-    const int n_tiles = (n_keys + 63) / 64;
-    const int t_begin = u.split * a.tiles_per_split;
-    const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
+        const int n_tiles = (n_keys + 63) / 64;
+        const int t_begin = u.split * tps;
+        const int t_end = min(n_tiles, t_begin + tps);
 
-    // key of position pos of tile t; past the split or past n_keys: row 0 (never used)
-    auto key_at = [&](int t, int pos) -> int {
-        if (t >= t_end || pos >= n_keys) return 0;
-        if (!SPARSE) return pos;
-        if (!in_lds) return klist[pos];
-        if (pos < n_blk) {
-            const int c = pos / a.bs;
-            return min(max(s_blk[c] * a.bs + (pos - c * a.bs), 0), a.L - 1);
-        }
-        if (pos < sink0) return a.P + (pos - n_blk);
-        return s_unc[pos - sink0];
-    };
-
-    // ---- Q fragments (B operand of S^T = K Q^T): row p, d = 16c + 8hf .. +7
-    bf16x8 qf[NQC];
-    {
-        const int rr = row_ok ? r : 0;
-        int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + rr] : rr;
-        phys = max(phys, 0);
-        const int hh = row_ok ? h : g * a.Gq;
-        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh +
-                               static_cast<int64_t>(phys) * a.qsr;
+        // rows of this lane's 2 key positions of tile t (row 0 past the split or the key set)
+        auto keys2 = [&](int t, int (&key)[2]) __attribute__((always_inline)) {
+            const int q0 = t * 64 + 8 * wv + 2 * g4;
+            const bool live = t < t_end;
 #pragma unroll
-        for (int c = 0; c < NQC; ++c)
-            qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf));
-    }
-    const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + g * a.ksh;
-    const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.vsb + g * a.vsh;
-
-    // ---- direct global -> LDS loads of one tile (4 instructions per wave)
-    auto issue_tile = [&](const uint16_t* base, int64_t rstride, int t, uint8_t* dst) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int blk1k = 4 * wv + i;                 // 1 KB block of the tile
-            const int row = 4 * blk1k + (lane >> 4);
-            const int chunk = swz(row, lane & 15);        // global chunk held at slot (lane & 15)
-            const int key = s_kidx[t & 3][row];
-            const uint16_t* src = base + static_cast<int64_t>(key) * rstride + 8 * chunk;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * blk1k), 16, 0, 0);
-        }
-    };
-
-    // ---- S^T tile = K Q^T from an LDS K tile
-    auto qk = [&](const uint8_t* kt, f32x16* st) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
-            const int row = kb2 * 32 + col;
-            const uint8_t* krow = kt + row * kRowB;
-#pragma unroll
-            for (int c = 0; c < NQC; ++c) {
-                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(krow + 16 * swz(row, 2 * c + hf));
-                st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[c], st[kb2], 0, 0, 0);
-            }
-        }
-    };
-
-    f32x16 acc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-    float m_run = kNegBig;
-    float l_run = 0.0f;
-
-    if (t_begin < t_end) {
-        if (wv == 0) {
-            s_kidx[t_begin & 3][lane] = key_at(t_begin, t_begin * 64 + lane);
-            s_kidx[(t_begin + 1) & 3][lane] = key_at(t_begin + 1, (t_begin + 1) * 64 + lane);
-            s_kidx[(t_begin + 2) & 3][lane] = key_at(t_begin + 2, (t_begin + 2) * 64 + lane);
-        }
-        __syncthreads();
-        issue_tile(kbase, a.ksr, t_begin, s_k0);
-        issue_tile(vbase, a.vsr, t_begin, s_v0);
-        issue_tile(kbase, a.ksr, t_begin + 1, s_k1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        f32x16 st[2];
-        qk(s_k0, st);
-
-        // One pipelined iteration: tile t's K was read last iteration (it sits in kdma),
-        // tile t+1's K is in kread, tile t's V is in vread, tile t+1's V goes to vdma.
-        auto iteration = [&](int t, uint8_t* kread, uint8_t* kdma, uint8_t* vread, uint8_t* vdma) {
-            // the key map is read before the DMA loads go out: an LDS read issued behind
-            // them would have to wait for their completion
-            int next_key = 0;
-            if (wv == 0) next_key = key_at(t + 3, (t + 3) * 64 + lane);
-            issue_tile(kbase, a.ksr, t + 2, kdma);
-            issue_tile(vbase, a.vsr, t + 1, vdma);
-
-            // S for tile t+1 (its K is resident) while this tile's softmax runs
-            f32x16 sn[2];
-            qk(kread, sn);
-
-            const int valid_here = n_keys - t * 64;
-            if (valid_here < 64) {
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int kl = kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                        if (kl >= valid_here) st[kb2][i] = -INFINITY;
-                    }
-            }
-            float mx = fmaxf(st[0][0], st[0][1]);
-#pragma unroll
-            for (int i = 2; i < 16; ++i) mx = fmaxf(mx, st[0][i]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[1][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx * a.sl2);
-            const float alpha = fast_exp2(m_run - m_new);
-            float psum = 0.0f;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float pv = fast_exp2(fmaf(st[kc >> 1][8 * (kc & 1) + j], a.sl2, -m_new));
-                    psum += pv;
-                    pf[kc][j] = static_cast<__bf16>(pv);
+            for (int i = 0; i < 2; ++i) {
+                const int q = q0 + i;
+                const bool ok = live && q < n_keys;
+                int k;
+                if (MODE == kDense) {
+                    k = q;
+                } else if (MODE == kSparseList) {
+                    k = ok ? klist[q] : 0;
+                } else {
+                    // branch-free: both LDS lookups use in-range indices
+                    const bool in_blk = q < n_blk;
+                    const int qb = in_blk ? q : 0;
+                    const int c = div_magic(qb, a.bs, a.bs_magic);
+                    const int kb = min(max(s_blk[c] * a.bs + (qb - c * a.bs), 0), a.L - 1);
+                    const int ku = s_unc[min(max(q - sink0, 0), kMapSinks - 1)];
+                    k = in_blk ? kb : (q < sink0 ? a.P + (q - n_blk) : ku);
                 }
-            l_run = fmaf(l_run, alpha, psum);
-            if (__any(m_new != m_run)) {
+                key[i] = ok ? k : 0;
+            }
+        };
+
+        // ---- Q fragments (B operand of S^T = K Q^T): d = 16c + 8hf .. +7 of the row
+        const int p = u.qt * kD128Rows + wv * 32 + col;   // 8 waves x 32 rows
+        const bool row_ok = p < rows_valid;
+        bf16x8 qf[NQC];
+        {
+            const int rr = row_ok ? p / a.Gq : 0;
+            const int hh = row_ok ? g * a.Gq + p % a.Gq : g * a.Gq;
+            int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + rr] : rr;
+            phys = max(phys, 0);
+            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh +
+                                   static_cast<int64_t>(phys) * a.qsr;
+#pragma unroll
+            for (int c = 0; c < NQC; ++c)
+                qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf));
+        }
+        const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + g * a.ksh;
+        const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.vsb + g * a.vsh;
+        const int ksr = static_cast<int>(a.ksr), vsr = static_cast<int>(a.vsr);
+
+        // ---- direct global -> LDS loads of one tile's rows (2 instructions per wave)
+        auto issue_k = [&](const int (&key)[2], uint8_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 8 * wv + 4 * i + g4;
+                const uint16_t* src = kbase + static_cast<int64_t>(key[i]) * ksr + 8 * swz_k(r, lane & 15);
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * (2 * wv + i)), 16, 0, 0);
+            }
+        };
+        auto issue_v = [&](const int (&key)[2], uint8_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 8 * wv + 4 * i + g4;
+                const uint16_t* src = vbase + static_cast<int64_t>(key[i]) * vsr + 8 * (lane & 15);
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * (2 * wv + i)), 16, 0, 0);
+            }
+        };
+
+        // ---- S^T tile (two 32-key blocks) = K Q^T from an LDS K tile.  The swizzled
+        // offset of (row col, chunk 2c + hf) is kofs ^ 32c; key block kb adds 8 KB.
+        const int kofs = col * kRowB + ((16 * hf) ^ (16 * (col & 15)));
+        auto qk = [&](const uint8_t* kt, f32x16 (&st)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                // all 8 fragments of the key block in flight before the first MFMA
+                bf16x8 kf[NQC];
+#pragma unroll
+                for (int c = 0; c < NQC; ++c)
+                    kf[c] = *reinterpret_cast<const bf16x8*>(kt + kb * 32 * kRowB + (kofs ^ (32 * c)));
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st[kb][i] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NQC; ++c)
+                    st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], st[kb], 0, 0, 0);
+            }
+        };
+
+        // V^T operand of (kc, db): row d = 32db + col, chunk 2kc + hf, at
+        // 4096 db + (tofs ^ 32 kc)
+        const int tofs = col * 128 + ((16 * hf) ^ (16 * ((col >> 1) & 7)));
+
+        // ---- V tile -> V^T: lane (k, c8) moves rows 2k, 2k+1 x d = 8c8 .. 8c8+7
+        const int tr_c8 = tid & 15, tr_k = tid >> 4;
+        const int tr_s = vt_row(2 * tr_k);   // slots of rows 2k, 2k+1: tr_s, tr_s + 1
+        auto transpose_v = [&](const uint8_t* vraw, uint8_t* vt) __attribute__((always_inline)) {
+            const u32x4 ra = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k) * kRowB + 16 * tr_c8);
+            const u32x4 rb = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k + 1) * kRowB + 16 * tr_c8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t x = ra[e >> 1], y = rb[e >> 1];
+                const uint32_t w = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+                *reinterpret_cast<uint32_t*>(vt + vt_off(8 * tr_c8 + e, tr_s)) = w;
+            }
+        };
+        f32x16 acc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+        float m_run = kNegBig;
+        float l_run = 0.0f;
+
+        if (t_begin < t_end) {
+            // prologue: K and V of tiles t0 .. t0+2; those of t0 and t0+1 must land
+            int kn[2];
+            keys2(t_begin, kn);
+            issue_k(kn, s_k0);
+            issue_v(kn, s_v0);
+            keys2(t_begin + 1, kn);
+            issue_k(kn, s_k1);
+            issue_v(kn, s_v1);
+            keys2(t_begin + 2, kn);
+            issue_k(kn, s_k2);
+            issue_v(kn, s_v2);
+            barrier_keep<4>();   // K(t0+2) and V(t0+2) may still be in flight
+            transpose_v(s_v0, s_t0);
+            f32x16 st[2];
+            qk(s_k0, st);
+            barrier_keep<4>();   // V^T(t0) is complete; s_k0, s_v0 are free for tile t0+3
+
+            // Iteration for tile t (stage j = (t - t0) % 3): K and V of tile t+3 go to
+            // stage j, V(t+1) becomes V^T(t+1), S(t+1) is computed from K(t+1), and the
+            // softmax of S(t) and O += V(t) P(t) run on stage j.
+            auto iteration = [&](int t, const uint8_t* kread, uint8_t* kdma, uint8_t* vdma, const uint8_t* vnext,
+                                 uint8_t* tnext, const uint8_t* tread) __attribute__((always_inline)) {
+                keys2(t + 3, kn);
+                issue_k(kn, kdma);
+                issue_v(kn, vdma);
+                transpose_v(vnext, tnext);
+
+                f32x16 sn[2];
+                qk(kread, sn);
+                const int valid_here = n_keys - t * 64;
+                if (valid_here < 64) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int r = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+                            if (row_pos(r) >= valid_here) st[kb][i] = -INFINITY;
+                        }
+                }
+                float mx = fmaxf(st[0][0], st[0][1]);
+#pragma unroll
+                for (int i = 2; i < 16; ++i) mx = fmaxf(mx, st[0][i]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[1][i]);
+                mx = fmaxf(mx, xhalf(mx));
+                const float mc = mx * a.sl2;
+                const bool need = mc > m_run + kSlack;
+                if (__any(need)) {
+                    const float m_new = need ? mc : m_run;
+                    const float alpha = fast_exp2(m_run - m_new);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+                    l_run *= alpha;
+                    m_run = m_new;
+                }
+                const float mneg = -m_run;
+                float psum = 0.0f;
+                bf16x8 pf[4];
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float pv = fast_exp2(fmaf(st[kc >> 1][8 * (kc & 1) + j], a.sl2, mneg));
+                        psum += pv;
+                        pf[kc][j] = static_cast<__bf16>(pv);
+                    }
+                l_run += psum;
+
+                // O^T += V^T P^T, the 4 fragments of a key chunk read before its MFMAs
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    const int o = tofs ^ (32 * kc);
+                    bf16x8 vf[NDB];
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) vf[db] = *reinterpret_cast<const bf16x8*>(tread + db * 4096 + o);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[kc], acc[db], 0, 0, 0);
+                }
+                // this iteration's 4 loads may stay in flight; every older one has landed
+                barrier_keep<4>();
+                st[0] = sn[0];
+                st[1] = sn[1];
+            };
+            // tile t_begin + j: K in s_k[j % 3], V in s_v[j % 3], V^T in s_t[j % 3]
+            for (int t = t_begin; t < t_end; t += 3) {
+                iteration(t, s_k1, s_k0, s_v0, s_v1, s_t1, s_t0);
+                if (t + 1 < t_end) iteration(t + 1, s_k2, s_k1, s_v1, s_v2, s_t2, s_t1);
+                if (t + 2 < t_end) iteration(t + 2, s_k0, s_k2, s_v2, s_v0, s_t0, s_t2);
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // drain the loads past the split before LDS is reused
+        }
+
+        // ---- epilogue: normalised rows (one split) or unnormalised partials
+        const int r = p / a.Gq;
+        const int h = g * a.Gq + p % a.Gq;
+        const float l_tot = l_run + xhalf(l_run);
+        if (n_splits == 1) {
+            if (row_ok) {
+                uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const int d0 = db * 32 + 8 * qd + 4 * hf;
+                        u32x2 w;
+                        w[0] = pack_bf16x2(acc[db][4 * qd + 0] * inv, acc[db][4 * qd + 1] * inv);
+                        w[1] = pack_bf16x2(acc[db][4 * qd + 2] * inv, acc[db][4 * qd + 3] * inv);
+                        *reinterpret_cast<u32x2*>(orow + d0) = w;
+                    }
+                if (a.lse && hf == 0)
+                    a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] =
+                        l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+            } else if (hf == 0 && p < rows_all) {
+                write_zero_row<uint16_t>(a, b, h, r, 128);
             }
-            m_run = m_new;
-
-            // O^T += V^T P^T with transposing LDS reads of the row-major V tile
-            const int grp = lane >> 4, j16 = lane & 15;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int e = db * 32 + 16 * (grp & 1) + 4 * (j16 & 3);   // first d of this lane's pointer
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    const int key0 = kc * 16 + 4 * hf + (j16 >> 2);
-                    const int key1 = key0 + 8;
-                    uint8_t* p0v = vread + key0 * kRowB + 16 * swz(key0, e >> 3) + 2 * (e & 7);
-                    uint8_t* p1v = vread + key1 * kRowB + 16 * swz(key1, e >> 3) + 2 * (e & 7);
-                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0v);
-                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1v);
-                    const bf16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[kc], acc[db], 0, 0, 0);
-                }
-            }
-            if (wv == 0) s_kidx[(t + 3) & 3][lane] = next_key;
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            st[0] = sn[0];
-            st[1] = sn[1];
-        };
-        // even iterations read K from s_k1 and V from s_v0; odd ones the other way round
-        for (int t = t_begin; t < t_end; t += 2) {
-            iteration(t, s_k1, s_k0, s_v0, s_v1);
-            if (t + 1 < t_end) iteration(t + 1, s_k0, s_k1, s_v1, s_v0);
-        }
-    }
-
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (a.n_splits == 1) {
-        if (row_ok) {
-            uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        } else if (row_ok) {
+            const int64_t idx = d128_part_index(a, nqt_max, n_splits, b, g, u.split, p);
+            float* po = a.part_o + idx * 128;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
                     const int d0 = db * 32 + 8 * qd + 4 * hf;
-                    u32x2 w;
-                    w[0] = pack_bf16x2(acc[db][4 * qd + 0] * inv, acc[db][4 * qd + 1] * inv);
-                    w[1] = pack_bf16x2(acc[db][4 * qd + 2] * inv, acc[db][4 * qd + 3] * inv);
-                    *reinterpret_cast<u32x2*>(orow + d0) = w;
+                    f32x4 w = {acc[db][4 * qd + 0], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
+                    *reinterpret_cast<f32x4*>(po + d0) = w;
                 }
-            if (a.lse && hf == 0)
-                a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] =
-                    l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-        } else if (hf == 0 && p < rows_all) {
-            write_zero_row<uint16_t>(a, b, h, r, D);
-        }
-        return;
-    }
-    if (row_ok) {
-        const int64_t idx = ((static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r) * a.n_splits + u.split;
-        float* po = a.part_o + idx * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int d0 = db * 32 + 8 * qd + 4 * hf;
-                f32x4 w = {acc[db][4 * qd + 0], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
-                *reinterpret_cast<f32x4*>(po + d0) = w;
+            if (hf == 0) {
+                a.part_ml[idx * 2 + 0] = m_run;
+                a.part_ml[idx * 2 + 1] = l_tot;
             }
-        if (hf == 0) {
-            a.part_ml[idx * 2 + 0] = m_run;
-            a.part_ml[idx * 2 + 1] = l_tot;
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16_d128(const AttnArgs& a, dim3 grid, hipStream_t stream) {
-    if (a.sparse) hipLaunchKernelGGL(attn_d128_kernel<true>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(attn_d128_kernel<false>, grid, dim3(256), 0, stream, a);
+int d128_slots() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_d128_kernel<kSparseLds>, 512, 0) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        int slots = cus * per_cu;
+        slots = slots < kD128MaxSlots ? slots : kD128MaxSlots;
+        cached[dev] = slots / 8 * 8 > 0 ? slots / 8 * 8 : 8;
+    }
+    return cached[dev];
+}
+
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.slots));
+    if (!a.sparse) hipLaunchKernelGGL(attn_d128_kernel<kDense>, grid, dim3(512), 0, stream, a);
+    else if (sparse_map_in_lds(a)) hipLaunchKernelGGL(attn_d128_kernel<kSparseLds>, grid, dim3(512), 0, stream, a);
+    else hipLaunchKernelGGL(attn_d128_kernel<kSparseList>, grid, dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

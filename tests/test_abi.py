@@ -57,11 +57,18 @@ def test_focus_count_rejects_negative():
 
 def test_workspace_sizes():
     lib = F.lib()
-    # the block-entry refresh has enough query tiles: no key split, no workspace
-    assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 32768) == 0
-    # dense attention of <= 1024 active rows splits the 32K keys: partials in the workspace
-    n = lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024)
-    assert n >= 2 * 32 * 1024 * (128 + 2) * 4     # at least two splits of fp32 partials
+    # bf16 d = 128: the split count is picked on the device from the valid rows, so the
+    # workspace covers fp32 partials of at most 512 work items of 256 rows, whatever
+    # nq_max is
+    cap = 512 * 256 * (128 + 2) * 4
+    for nq_max in (1024, 32768):
+        n = lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, nq_max)
+        assert n == cap
+    # a short key range leaves nothing to split
+    assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 512, 128, 1024) == 0
+    # fp32 splits per row: at least two splits of fp32 partials for <= 1024 active rows
+    n = lib.fdl_dense_attention_workspace_bytes(F.FDL_F32, 1, 32, 32, 32768, 128, 1024)
+    assert n >= 2 * 32 * 1024 * (128 + 2) * 4
     assert lib.fdl_sparse_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128,
                                                      1024, 16, 64, 128) > 0
     assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024) == \
@@ -112,6 +119,7 @@ def _dense(**kw):
     (dict(Hkv=3), 2), (dict(B=0), 2), (dict(L=0), 2), (dict(nq_max=-1), 2),
     (dict(q=MISALIGNED), 4), (dict(ks=S(4 * 256 * 128, 256 * 128, 132)), 4),
     (dict(qs=S(4 * 256 * 128, 256 * 128, 64)), 2),       # rows overlap: |row stride| < d
+    (dict(vs=S(0, 0, 1 << 31)), 2), (dict(ks=S(0, 0, -(1 << 31))), 2),   # row stride beyond 2^31
     (dict(nq_max=16, L=4096), 5),                        # few rows -> key split needs a workspace
     (dict(nq_max=16, L=4096, ws=FAKE, ws_bytes=64), 5),
     (dict(nq_max=16, L=4096, ws=MISALIGNED, ws_bytes=1 << 30), 4),
