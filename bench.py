@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-refresh", action="store_true", help="skip the dense-refresh measurement")
     ap.add_argument("--refresh-reps", type=int, default=3)
+    ap.add_argument("--serial-means", action="store_true",
+                    help="block means right before each layer's scoring instead of on a second stream")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -65,7 +67,10 @@ def step_accounting(wl, n_active, sinks, blocks_per_layer):
     acc["sinks"] = dict(bytes=Hkv * L * d * E + q_rows + Hq * na * 4 + L * 4,
                         flops=2 * na * L * d * Hq, calls=1)
     n_sparse = wl.layers - wl.l_dense
+    nb = -(-P // wl.bs)
     scan = Hkv * P * d * E
+    # block means of every sparse layer: one read of the prompt keys, the means written
+    acc["means"] = dict(bytes=n_sparse * (scan + Hkv * nb * d * 4), flops=0, calls=n_sparse)
     sb, sf, kb, kf = 0, 0, 0, 0
     snk = set(int(s) for s in sinks if s >= 0)
     for blocks in blocks_per_layer:
@@ -74,8 +79,8 @@ def step_accounting(wl, n_active, sinks, blocks_per_layer):
         covered = set(b for b in sel)
         extra = sum(1 for s in snk if s < P and s // wl.bs not in covered)
         n_keys = blk_keys + (L - P) + extra
-        kb += scan + q_rows + len(sel) * 4
-        kf += 2 * Hq * na * d
+        kb += Hkv * nb * d * 4 + q_rows + len(sel) * 4       # scoring reads the means and the queries
+        kf += 2 * Hq * na * d + 2 * Hkv * nb * d
         sb += 2 * Hkv * n_keys * d * E + 2 * q_rows
         sf += 4 * na * n_keys * d * Hq
     acc["blocks"] = dict(bytes=kb, flops=kf, calls=n_sparse)
@@ -160,10 +165,20 @@ def main():
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        for _ in range(2):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "reps": 5}))
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        c0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / reps
+        # a copy reads and writes every byte once
+        print(json.dumps({"calibrate_copy_bytes": n, "reps": reps + 2, "ms_per_copy": round(ms, 4),
+                          "GBps_read_plus_write": round(2 * n / (ms / 1000) / 1e9, 1)}))
         return
 
     import long_context_diffusion_amd as F
@@ -190,7 +205,8 @@ def main():
 
     run = StepRunner(B=wl.B, L=wl.L, P=wl.P, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, dtype=torch.bfloat16,
                      n_t=wl.n_t, rho=wl.rho, w=wl.w, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
-                     layers=wl.layers, l_dense=wl.l_dense, scale=wl.scale, device=dev)
+                     layers=wl.layers, l_dense=wl.l_dense, scale=wl.scale, device=dev,
+                     overlap_means=not args.serial_means)
     stream = torch.cuda.current_stream()
 
     def step(hooks=None):
@@ -210,14 +226,14 @@ def main():
 
     def make_hooks():
         hooks = {}
-        for name in ("pcgi", "dense", "sinks", "blocks", "sparse"):
-            def before(name=name):
+        for name in ("pcgi", "dense", "sinks", "means", "blocks", "sparse"):
+            def before(name=name):   # on the stream the stage runs on (block means: the second one)
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 stage_events.setdefault(name, []).append(ev)
-                ev[0].record(stream)
+                ev[0].record()
 
             def after(name=name):
-                stage_events[name][-1][1].record(stream)
+                stage_events[name][-1][1].record()
             hooks[name] = (before, after)
         return hooks
 

@@ -9,7 +9,8 @@
  *   fdl_pcgi_select       (1) top-k masked positions by previous confidence, (2) windows
  *   fdl_dense_attention   (3) dense layers 1..l_dense, and the block-entry full refresh
  *   fdl_sink_identify     (3) attention sinks from layer l_dense's attention distribution
- *   fdl_block_score_topc  (4) mean key per prompt block, relevance R_b, top-C blocks
+ *   fdl_block_means       (4) mean key per prompt block (keys only: can run ahead)
+ *   fdl_block_score_topc  (4) relevance R_b of the active queries, top-C blocks
  *   fdl_sparse_attention  (5) attention of the active queries over I_p only
  *
  * Conventions shared by every entry point
@@ -141,21 +142,41 @@ fdl_status fdl_sink_identify(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * fdl_block_score_topc - prompt-block pruning.
+ * fdl_block_means - the mean key of every prompt block.
  * Summary page, "Method steps" (4): split the P prompt keys into nb = ceil(P/bs)
- * contiguous blocks, represent each by the mean of its keys kbar_b, score every
- * block by its relevance to the candidate queries and keep the C best.
+ * contiguous blocks and represent each by the mean of its keys (a short last
+ * block by the mean of its own keys).  The means depend on the keys only, so a
+ * caller may compute them for every layer ahead of the layers that score them.
+ *   k, ks   [B, Hkv, L, d] with strides ks (rows 0..P-1 are read)
+ *   P, bs   prompt length (1 <= P <= L), block size (>= 1)
+ *   kbar    [B, Hkv, nb, d] fp32 out, dense; each mean is summed in fp64 (exact for
+ *           fp32/bf16 keys) and rounded once
+ * Errors: NULL pointers (FDL_ERR_NULL), bad shapes (FDL_ERR_SHAPE), as for the
+ * other entry points.  No workspace.
+ */
+fdl_status fdl_block_means(fdl_dtype dtype, int B, int Hkv, int L, int P, int d,
+                           const void* k, fdl_strides ks, int bs, float* kbar, hipStream_t stream);
+
+/*
+ * fdl_block_score_topc - prompt-block pruning.
+ * Summary page, "Method steps" (4): score every prompt block by its relevance to
+ * the candidate queries and keep the C best.
  * R_b = scale * sum over query heads h and valid query rows i of q_{h,i} . kbar_{g(h),b}
- * (one block set per sequence, shared by all heads).  The kernels accumulate R_b
- * in fp64.
- *   q, q_idx, n_q, nq_max, k, ks, scale   as in fdl_dense_attention
+ * (one block set per sequence, shared by all heads), accumulated in fp64 from the
+ * fp32 block means.
+ *   q, q_idx, n_q, nq_max, scale   as in fdl_dense_attention
+ *   k, ks   the keys: the block means are computed first (as fdl_block_means does),
+ *           into kbar when kbar is non-NULL, else into the workspace.  k NULL: kbar
+ *           must hold the means already (from fdl_block_means) and only the scoring
+ *           runs.
  *   P, bs, C   prompt length (P <= L), block size (>= 1), blocks kept (>= 0)
  *   block_idx  [B, C] out, ascending, -1 padded when C > nb
  *   R          [B, nb] fp64 out, or NULL
- *   kbar       [B, Hkv, nb, d] fp32 out (block means, rounded once from fp64), or NULL
+ *   kbar       [B, Hkv, nb, d] fp32 block means: out (k given) or in (k NULL), or NULL
+ * The workspace size depends on nq_max (the query rows are scored in slices).
  */
 size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int P,
-                                            int d, int bs);
+                                            int d, int bs, int nq_max);
 fdl_status fdl_block_score_topc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int P, int d,
                                 const void* q, fdl_strides qs, const int32_t* q_idx,
                                 const int32_t* n_q, int nq_max,

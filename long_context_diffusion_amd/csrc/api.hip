@@ -166,9 +166,26 @@ fdl_status fdl_sink_identify(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d,
     return hip_status(launch_sink_identify(dt, d, a, n_sinks, sink_idx, scores, ws, stream));
 }
 
-size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int P, int d, int bs) {
-    if (check_dtype_dims(dt, B, Hq, Hkv, P < 1 ? 1 : P, d) != FDL_OK || P < 1 || bs < 1) return 0;
-    return block_workspace_bytes(B, Hkv, P, d, bs);
+fdl_status fdl_block_means(fdl_dtype dt, int B, int Hkv, int L, int P, int d, const void* k, fdl_strides ks,
+                           int bs, float* kbar, hipStream_t stream) {
+    fdl_status st = check_dtype_dims(dt, B, Hkv, Hkv, L, d);
+    if (st != FDL_OK) return st;
+    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if (!kbar) return FDL_ERR_NULL;
+    if (P < 1 || P > L || bs < 1) return FDL_ERR_SHAPE;
+    BlockArgs a{};
+    a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
+    a.B = B; a.Hq = Hkv; a.Hkv = Hkv; a.P = P; a.Gq = 1; a.bs = bs;
+    a.nb = static_cast<int>((static_cast<int64_t>(P) + bs - 1) / bs);
+    a.kbar = kbar;
+    return hip_status(launch_block_means(dt, d, a, stream));
+}
+
+size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int P, int d, int bs,
+                                            int nq_max) {
+    if (check_dtype_dims(dt, B, Hq, Hkv, P < 1 ? 1 : P, d) != FDL_OK || P < 1 || bs < 1 || nq_max < 0)
+        return 0;
+    return block_workspace_bytes(B, Hq, Hkv, P, d, bs, nq_max);
 }
 
 fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
@@ -180,10 +197,11 @@ fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if (st != FDL_OK) return st;
     if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
     if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
-    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if (k && (st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if (!k && !kbar) return FDL_ERR_NULL;
     if (!block_idx) return FDL_ERR_NULL;
     if (P < 1 || P > L || bs < 1 || C < 0) return FDL_ERR_SHAPE;
-    if ((st = check_ws(ws, ws_bytes, block_workspace_bytes(B, Hkv, P, d, bs))) != FDL_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, block_workspace_bytes(B, Hq, Hkv, P, d, bs, nq_max))) != FDL_OK) return st;
     BlockArgs a{};
     a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
     a.q_idx = q_idx; a.n_q = n_q; a.nq_max = nq_max;

@@ -610,7 +610,6 @@ void launch_kernel(fdl_dtype dtype, const AttnArgs& a, dim3 grid, hipStream_t st
     }
 }
 
-inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 

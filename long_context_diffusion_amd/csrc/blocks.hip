@@ -6,20 +6,19 @@
 // candidate queries to every block is scored and the C most relevant blocks
 // are kept.  R_b = scale * sum_h sum_i q_{h,i} . kbar_{g(h),b}.
 //
-// R_b is linear in the queries and in the keys of the block, so it is
-// evaluated as  R_b = scale / |b| * sum_g sum_{j in b} qsum_g . k_{g,j},  with
-// qsum_g the sum of every active query row of every query head that reads KV
-// head g.  The step is then one streaming read of the prompt keys:
-//   block_qsum    qsum_g in fp64 (exact for bf16/fp32 inputs up to rounding of
-//                 the final sum), one workgroup per (sequence, KV head).
-//   block_scan    reads each prompt key once, 16 bytes per lane, fully
-//                 coalesced; 8-term partial dot products in fp32, everything
-//                 above them in fp64; writes one fp64 partial per (KV head,
-//                 block).  Optionally also the block means (fp64 sums, one
-//                 rounding to fp32).
-//   block_select  sums the partials in KV-head order, scales by scale/|b|,
-//                 and keeps the top-C blocks (radix select on the fp64 keys,
-//                 lower block index first among equal scores), ascending.
+// The block means depend on the prompt keys only, so they are a separate pass
+// (block_means) that a caller can run for every layer ahead of the layer that
+// needs them, e.g. on a second stream while earlier layers attend.  Scoring is
+// then a small pass over the means:
+//   block_means      one streaming read of the prompt keys, 16 bytes per lane,
+//                    fp64 sums (exact for bf16/fp32 inputs), one rounding of the
+//                    mean to fp32.
+//   block_relevance  R is linear in the queries: qsum = sum of the query rows of a
+//                    slice of the active rows of one KV head's query heads (fp64),
+//                    then that slice's partial R_b = qsum . kbar_b for every block.
+//   block_select     sums the partials in a fixed order (KV head, then slice),
+//                    scales by scale, and keeps the top-C blocks (lower block index
+//                    first among equal scores), ascending.
 
 #include "ops.cuh"
 
@@ -27,8 +26,10 @@ namespace fdl {
 
 namespace {
 
-constexpr int kQsumThreads = 1024;
-constexpr int kScanThreads = 256;
+constexpr int kThreads = 256;
+constexpr int kPartRows = 128;     // active rows per relevance slice (at most kMaxParts slices)
+constexpr int kMaxParts = 64;
+constexpr int kMeansBlocks = 2;    // blocks per block_means workgroup
 
 template <typename T>
 __device__ __forceinline__ void unpack16(const u32x4& x, float* out);
@@ -46,38 +47,137 @@ __device__ __forceinline__ void unpack16<float>(const u32x4& x, float* out) {
     for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(x[i]);
 }
 
-// qsum[b][g][e] = sum over packed rows p < Gq*nq of Q[b][g*Gq + p%Gq][row(p/Gq)][e], fp64.
+// Relevance slices of sequence b: as many kPartRows-row slices as its active rows
+// need, at most a.nparts (the grid's bound); rows are split evenly between them.
+__device__ __forceinline__ int relevance_parts(const BlockArgs& a, int rows) {
+    return max(1, min(a.nparts, (rows + kPartRows - 1) / kPartRows));
+}
+
+// kbar[b][g][blk][e] = mean of K[b][g][blk*bs .. min((blk+1)*bs, P))[e], one rounding.
+// A workgroup takes kMeansBlocks consecutive blocks and keeps the loads of all of them
+// in flight together.
 template <typename T, int D>
-__global__ __launch_bounds__(kQsumThreads) void block_qsum_kernel(const BlockArgs a) {
-    constexpr int EPP = 16 / sizeof(T);       // elements per 16-byte piece
-    constexpr int NP = D / EPP;               // pieces per row
-    constexpr int RG = kQsumThreads / NP;     // row groups
-    __shared__ double s_part[RG][D];
+__global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a) {
+    constexpr int EPP = 16 / sizeof(T);     // elements per 16-byte piece
+    constexpr int NP = D / EPP;             // pieces per key row
+    constexpr int RG = kThreads / NP;       // rows read together by the workgroup
+    constexpr int kBatch = 8;               // loads per thread and block in flight
+    __shared__ double s_sum[kMeansBlocks][RG][D];
     const int tid = threadIdx.x;
-    const int g = blockIdx.x % a.Hkv, b = blockIdx.x / a.Hkv;
+    const int chunks = (a.nb + kMeansBlocks - 1) / kMeansBlocks;
+    const int chunk = blockIdx.x % chunks;
+    const int bg = blockIdx.x / chunks;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int piece = tid % NP, rg = tid / NP;
+    const T* kbase = static_cast<const T*>(a.k) + b * a.ksb + g * a.ksh + piece * EPP;
+    float* out = a.kbar + (static_cast<int64_t>(b) * a.Hkv + g) * a.nb * D;
+    const int blk0 = chunk * kMeansBlocks;
+    double acc[kMeansBlocks][EPP];
+#pragma unroll
+    for (int c = 0; c < kMeansBlocks; ++c)
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) acc[c][e] = 0.0;
+    // rows lo + rg + RG*u of every block of the chunk; blocks past nb read nothing
+    int lo[kMeansBlocks], hi[kMeansBlocks];
+#pragma unroll
+    for (int c = 0; c < kMeansBlocks; ++c) {
+        lo[c] = min(blk0 + c, a.nb - 1) * a.bs;
+        hi[c] = blk0 + c < a.nb ? min(lo[c] + a.bs, a.P) : lo[c];
+    }
+    for (int j0 = rg; j0 < a.bs; j0 += RG * kBatch) {
+        u32x4 x[kMeansBlocks][kBatch];
+#pragma unroll
+        for (int c = 0; c < kMeansBlocks; ++c)
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int j = min(lo[c] + j0 + u * RG, max(hi[c] - 1, lo[c]));
+                x[c][u] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * a.ksr);
+            }
+#pragma unroll
+        for (int c = 0; c < kMeansBlocks; ++c)
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (lo[c] + j0 + u * RG >= hi[c]) continue;
+                float v[EPP];
+                unpack16<T>(x[c][u], v);
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) acc[c][e] += static_cast<double>(v[e]);
+            }
+    }
+#pragma unroll
+    for (int c = 0; c < kMeansBlocks; ++c)
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) s_sum[c][rg][piece * EPP + e] = acc[c][e];
+    __syncthreads();
+    for (int i = tid; i < kMeansBlocks * D; i += kThreads) {
+        const int c = i / D, e = i % D;
+        if (blk0 + c >= a.nb) continue;
+        double s = 0.0;
+        for (int r = 0; r < RG; ++r) s += s_sum[c][r][e];
+        out[static_cast<int64_t>(blk0 + c) * D + e] = static_cast<float>(s / static_cast<double>(hi[c] - lo[c]));
+    }
+}
+
+// rpart[b][g][part][blk] = qsum_part . kbar[b][g][blk], qsum_part = sum of the query rows of
+// slice `part` of the Gq*nq packed rows of KV head g (packed row p: head g*Gq + p%Gq, row p/Gq).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void block_relevance_kernel(const BlockArgs a) {
+    constexpr int EPP = 16 / sizeof(T);
+    constexpr int NP = D / EPP;
+    constexpr int RG = kThreads / NP;
+    constexpr int kBatch = 8;
+    constexpr int LPB = 4;                  // lanes per block in the dot products
+    constexpr int EPL = D / LPB;            // kbar elements per lane
+    __shared__ double s_q[RG][D];
+    __shared__ double s_qsum[D];
+    const int tid = threadIdx.x;
+    const int part = blockIdx.x % a.nparts;
+    const int bg = blockIdx.x / a.nparts;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
     const int rows = a.Gq * nq;
+    const int parts = relevance_parts(a, rows);
+    if (part >= parts) return;
+    const int rpp = (rows + parts - 1) / parts;
+    const int p_lo = part * rpp, p_hi = min(rows, p_lo + rpp);
+
+    // the block means of the first pass go out before the queries: both round trips overlap
+    const float* kb = a.kbar_in + (static_cast<int64_t>(b) * a.Hkv + g) * a.nb * D;
+    const int sub = tid % LPB;
+    f32x4 kx[EPL / 4];
+    {
+        const int blk = min(tid / LPB, a.nb - 1);
+        const float* row = kb + static_cast<int64_t>(blk) * D + sub * EPL;
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) kx[i] = *reinterpret_cast<const f32x4*>(row + 4 * i);
+    }
+
+    // ---- qsum of this slice (fp64)
     const int piece = tid % NP, rg = tid / NP;
     double acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
-    // all row indices of a batch first, then all rows: two memory round trips per batch
-    constexpr int kBatch = 16;
-    for (int p0 = rg; p0 < rows; p0 += RG * kBatch) {
+    // packed row p = r * Gq + hh (query head g*Gq + hh, row r); this thread's rows advance by RG
+    const int step_r = RG / a.Gq, step_h = RG % a.Gq;
+    int r_cur = (p_lo + rg) / a.Gq, h_cur = (p_lo + rg) % a.Gq;
+    for (int p0 = p_lo + rg; p0 < p_hi; p0 += RG * kBatch) {
         int64_t off[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int p = min(p0 + u * RG, rows - 1);
-            const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
+            const bool in = p0 + u * RG < p_hi;
+            const int r = in ? r_cur : 0, hh = in ? h_cur : 0;
             const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
-            off[u] = b * a.qsb + h * a.qsh + static_cast<int64_t>(phys) * a.qsr + piece * EPP;
+            off[u] = b * a.qsb + (g * a.Gq + hh) * a.qsh + static_cast<int64_t>(phys) * a.qsr + piece * EPP;
+            r_cur += step_r;
+            h_cur += step_h;
+            if (h_cur >= a.Gq) { h_cur -= a.Gq; ++r_cur; }
         }
         u32x4 x[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + off[u]);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (p0 + u * RG >= rows) continue;
+            if (p0 + u * RG >= p_hi) continue;
             float v[EPP];
             unpack16<T>(x[u], v);
 #pragma unroll
@@ -85,134 +185,93 @@ __global__ __launch_bounds__(kQsumThreads) void block_qsum_kernel(const BlockArg
         }
     }
 #pragma unroll
-    for (int e = 0; e < EPP; ++e) s_part[rg][piece * EPP + e] = acc[e];
+    for (int e = 0; e < EPP; ++e) s_q[rg][piece * EPP + e] = acc[e];
     __syncthreads();
-    // pairwise tree over the row groups (fixed order, so the sum is deterministic)
-    for (int half = RG / 2; half >= 1; half >>= 1) {
-        for (int i = tid; i < half * D; i += kQsumThreads) {
-            const int r = i / D, e = i % D;
-            s_part[r][e] += s_part[r + half][e];
-        }
-        __syncthreads();
+    for (int e = tid; e < D; e += kThreads) {
+        double s = 0.0;
+        for (int r = 0; r < RG; ++r) s += s_q[r][e];
+        s_qsum[e] = s;
     }
-    for (int e = tid; e < D; e += kQsumThreads) a.qsum[(static_cast<int64_t>(b) * a.Hkv + g) * D + e] = s_part[0][e];
-}
+    __syncthreads();
 
-__device__ __forceinline__ double wave_sum_f64(double x) {
+    // ---- partial relevance of every block: LPB consecutive lanes share a block
+    double* rp = a.rpart + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nparts + part) * a.nb;
+    for (int blk = tid / LPB; blk < a.nb; blk += kThreads / LPB) {
+        f32x4 x[EPL / 4];
+        if (blk < kThreads / LPB) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-// One workgroup per (sequence, KV head, run of blocks_per_wg blocks).
-template <typename T, int D, bool KBAR>
-__global__ __launch_bounds__(kScanThreads) void block_scan_kernel(const BlockArgs a) {
-    constexpr int EPP = 16 / sizeof(T);
-    constexpr int NP = D / EPP;                 // pieces per key row
-    constexpr int RPI = kScanThreads / NP;      // key rows per block-wide load
-    __shared__ double s_red[kScanThreads / 64];
-    __shared__ double s_kbar[KBAR ? RPI : 1][KBAR ? D : 1];
-
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int chunk = blockIdx.x % a.scan_chunks;
-    const int bg = blockIdx.x / a.scan_chunks;
-    const int g = bg % a.Hkv, b = bg / a.Hkv;
-    const int piece = tid % NP, roff = tid / NP;
-    float qg[EPP];
-    {
-        const double* qs = a.qsum + (static_cast<int64_t>(b) * a.Hkv + g) * D + piece * EPP;
+            for (int i = 0; i < EPL / 4; ++i) x[i] = kx[i];
+        } else {
+            const float* row = kb + static_cast<int64_t>(blk) * D + sub * EPL;
 #pragma unroll
-        for (int e = 0; e < EPP; ++e) qg[e] = static_cast<float>(qs[e]);
-    }
-    const T* kbase = static_cast<const T*>(a.k) + b * a.ksb + g * a.ksh + piece * EPP;
-    const int blk0 = chunk * a.blocks_per_wg;
-    const int blk1 = min(a.nb, blk0 + a.blocks_per_wg);
-    for (int blk = blk0; blk < blk1; ++blk) {
-        const int lo = blk * a.bs;
-        const int hi = min(lo + a.bs, a.P);
-        double part = 0.0;
-        double ksum[KBAR ? EPP : 1];
-        if (KBAR) {
-#pragma unroll
-            for (int e = 0; e < EPP; ++e) ksum[e] = 0.0;
+            for (int i = 0; i < EPL / 4; ++i) x[i] = *reinterpret_cast<const f32x4*>(row + 4 * i);
         }
-        // rows lo + roff, lo + roff + RPI, ...; loads of one block are issued together
-        for (int j0 = lo; j0 < hi; j0 += 4 * RPI) {
-            u32x4 x[4];
+        double s = 0.0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = j0 + u * RPI + roff;
-                x[u] = u32x4{0u, 0u, 0u, 0u};
-                if (j < hi) x[u] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * a.ksr);
-            }
+        for (int i = 0; i < EPL / 4; ++i)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float v[EPP];
-                unpack16<T>(x[u], v);
-                float dot = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPP; ++e) dot = fmaf(v[e], qg[e], dot);
-                part += static_cast<double>(dot);
-                if (KBAR) {
-#pragma unroll
-                    for (int e = 0; e < EPP; ++e) ksum[e] += static_cast<double>(v[e]);
-                }
-            }
-        }
-        part = wave_sum_f64(part);
-        if (lane == 0) s_red[wv] = part;
-        if (KBAR) {
-            // rows handled by the same piece live in threads piece + NP*roff; combine through LDS
-            if (roff < RPI) {
-#pragma unroll
-                for (int e = 0; e < EPP; ++e) s_kbar[roff][piece * EPP + e] = ksum[e];
-            }
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double s = 0.0;
-            for (int w = 0; w < kScanThreads / 64; ++w) s += s_red[w];
-            a.rpart[(static_cast<int64_t>(b) * a.Hkv + g) * a.nb + blk] = s;
-        }
-        if (KBAR) {
-            for (int e = tid; e < D; e += kScanThreads) {
-                double s = 0.0;
-                for (int i = 0; i < RPI; ++i) s += s_kbar[i][e];
-                a.kbar[((static_cast<int64_t>(b) * a.Hkv + g) * a.nb + blk) * D + e] =
-                    static_cast<float>(s / static_cast<double>(hi - lo));
-            }
-        }
-        __syncthreads();
+            for (int j = 0; j < 4; ++j) s = fma(static_cast<double>(x[i][j]), s_qsum[sub * EPL + 4 * i + j], s);
+        s += __shfl_xor(s, 1, 64);   // (s0 + s1) + (s2 + s3) in every lane of the four
+        s += __shfl_xor(s, 2, 64);
+        if (sub == 0) rp[blk] = s;
     }
 }
 
+constexpr int kSelectThreads = 1024;
 constexpr int kSelectLds = 2048;   // blocks ranked in LDS
+constexpr int kSlices = 4;         // threads summing the partials of one block
 
-__global__ __launch_bounds__(256) void block_select_kernel(const BlockArgs a, int C, int32_t* block_idx,
-                                                            double* R_out) {
+__global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const BlockArgs a, int C,
+                                                                       int32_t* block_idx, double* R_out) {
     __shared__ SelectSmem sm;
     __shared__ uint64_t s_key[kSelectLds];
+    __shared__ double s_slice[kSlices][kSelectThreads / kSlices];
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+    const int parts = relevance_parts(a, a.Gq * nq);
+    // thread slice `slice` sums KV heads [slice*per, (slice+1)*per) x every slice of rows
+    const int per = (a.Hkv + kSlices - 1) / kSlices;
     double* R = a.rfull + static_cast<int64_t>(b) * a.nb;
-    for (int blk = threadIdx.x; blk < a.nb; blk += blockDim.x) {
-        const double* rp = a.rpart + static_cast<int64_t>(b) * a.Hkv * a.nb + blk;
+    const double* rp = a.rpart + static_cast<int64_t>(b) * a.Hkv * a.nparts * a.nb;
+    const int slice = tid / (kSelectThreads / kSlices), lb = tid % (kSelectThreads / kSlices);
+    const int g0 = slice * per, g1 = min(a.Hkv, g0 + per);
+    const int terms = max(g1 - g0, 0) * parts;
+    for (int blk0 = 0; blk0 < a.nb; blk0 += kSelectThreads / kSlices) {
+        const int blk = blk0 + lb;
         double s = 0.0;
-        int g = 0;
-        for (; g + 8 <= a.Hkv; g += 8) {
-            double x[8];
+        if (blk < a.nb) {
+            // term t: KV head g0 + t / parts, row slice t % parts; addresses advance without a division
+            int g = g0, pi = 0;
+            for (int t = 0; t < terms; t += 16) {
+                double x[16];
+                int gg = g, pp = pi;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = rp[static_cast<int64_t>(g + u) * a.nb];
+                for (int u = 0; u < 16; ++u) {
+                    const bool in = t + u < terms;
+                    const double y = rp[(static_cast<int64_t>(in ? gg : g0) * a.nparts + (in ? pp : 0)) * a.nb + blk];
+                    x[u] = in ? y : 0.0;
+                    if (++pp == parts) { pp = 0; ++gg; }
+                }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) s += x[u];
+                for (int u = 0; u < 16; ++u) s += x[u];
+                g = gg;
+                pi = pp;
+            }
         }
-        for (; g < a.Hkv; ++g) s += rp[static_cast<int64_t>(g) * a.nb];
-        const int cnt = min(a.bs, a.P - blk * a.bs);
-        const double val = s * (static_cast<double>(a.scale) / static_cast<double>(cnt));
-        if (a.nb <= kSelectLds) s_key[blk] = okey64(val);
-        else R[blk] = val;
-        if (R_out) R_out[static_cast<int64_t>(b) * a.nb + blk] = val;
+        s_slice[slice][lb] = s;
+        __syncthreads();
+        if (slice == 0 && blk < a.nb) {
+            double tot = 0.0;
+#pragma unroll
+            for (int i = 0; i < kSlices; ++i) tot += s_slice[i][lb];
+            const double val = tot * static_cast<double>(a.scale);
+            if (a.nb <= kSelectLds) s_key[blk] = okey64(val);
+            else R[blk] = val;
+            if (R_out) R_out[static_cast<int64_t>(b) * a.nb + blk] = val;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     __threadfence_block();
     int32_t* out = block_idx + static_cast<int64_t>(b) * C;
     if (a.nb <= kSelectLds) {
@@ -226,44 +285,54 @@ __global__ __launch_bounds__(256) void block_select_kernel(const BlockArgs a, in
     }
 }
 
+int host_parts(int Gq, int nq_max) {
+    const int64_t parts = (static_cast<int64_t>(Gq) * nq_max + kPartRows - 1) / kPartRows;
+    return static_cast<int>(parts < 1 ? 1 : parts > kMaxParts ? kMaxParts : parts);
+}
+
 }  // namespace
 
-size_t block_workspace_bytes(int B, int Hkv, int P, int d, int bs) {
+size_t block_workspace_bytes(int B, int Hq, int Hkv, int P, int d, int bs, int nq_max) {
     const int64_t nb = (static_cast<int64_t>(P) + bs - 1) / bs;
-    return static_cast<size_t>(B) * Hkv * d * sizeof(double) +      // qsum
-           static_cast<size_t>(B) * Hkv * nb * sizeof(double) +     // per-head partials
-           static_cast<size_t>(B) * nb * sizeof(double);            // R
+    const int parts = host_parts(Hq / Hkv, nq_max);
+    return round_up(static_cast<size_t>(B) * Hkv * parts * nb * sizeof(double), 256) +   // partial R
+           round_up(static_cast<size_t>(B) * nb * sizeof(double), 256) +                 // R
+           static_cast<size_t>(B) * Hkv * nb * d * sizeof(float);                        // block means
+}
+
+hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStream_t stream) {
+    const int chunks = (a.nb + kMeansBlocks - 1) / kMeansBlocks;
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * chunks));
+#define FDL_MEANS(T, DD) hipLaunchKernelGGL((block_means_kernel<T, DD>), grid, dim3(kThreads), 0, stream, a)
+    if (dtype == FDL_BF16) { if (d == 128) FDL_MEANS(uint16_t, 128); else FDL_MEANS(uint16_t, 64); }
+    else { if (d == 128) FDL_MEANS(float, 128); else FDL_MEANS(float, 64); }
+#undef FDL_MEANS
+    return hipGetLastError();
 }
 
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream) {
-    a.qsum = static_cast<double*>(ws);
-    a.rpart = a.qsum + static_cast<int64_t>(a.B) * a.Hkv * d;
-    a.rfull = a.rpart + static_cast<int64_t>(a.B) * a.Hkv * a.nb;
-    a.blocks_per_wg = 2;
-    a.scan_chunks = (a.nb + a.blocks_per_wg - 1) / a.blocks_per_wg;
-    const bool bf = dtype == FDL_BF16;
-    const dim3 qgrid(a.B * a.Hkv);
-#define FDL_QSUM(T, DD) hipLaunchKernelGGL((block_qsum_kernel<T, DD>), qgrid, dim3(kQsumThreads), 0, stream, a)
-    if (bf) { if (d == 128) FDL_QSUM(uint16_t, 128); else FDL_QSUM(uint16_t, 64); }
-    else { if (d == 128) FDL_QSUM(float, 128); else FDL_QSUM(float, 64); }
-#undef FDL_QSUM
+    a.nparts = host_parts(a.Gq, a.nq_max);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    a.rpart = reinterpret_cast<double*>(w);
+    w += round_up(static_cast<size_t>(a.B) * a.Hkv * a.nparts * a.nb * sizeof(double), 256);
+    a.rfull = reinterpret_cast<double*>(w);
+    w += round_up(static_cast<size_t>(a.B) * a.nb * sizeof(double), 256);
+    if (a.k) {
+        // means from the keys first: into the caller's kbar when given, else the workspace
+        if (!a.kbar) a.kbar = reinterpret_cast<float*>(w);
+        hipError_t err = launch_block_means(dtype, d, a, stream);
+        if (err != hipSuccess) return err;
+    }
+    a.kbar_in = a.kbar;
+    const dim3 rgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * a.nparts));
+#define FDL_REL(T, DD) hipLaunchKernelGGL((block_relevance_kernel<T, DD>), rgrid, dim3(kThreads), 0, stream, a)
+    if (dtype == FDL_BF16) { if (d == 128) FDL_REL(uint16_t, 128); else FDL_REL(uint16_t, 64); }
+    else { if (d == 128) FDL_REL(float, 128); else FDL_REL(float, 64); }
+#undef FDL_REL
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 sgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * a.scan_chunks));
-#define FDL_SCAN(T, DD, KB) hipLaunchKernelGGL((block_scan_kernel<T, DD, KB>), sgrid, dim3(kScanThreads), 0, stream, a)
-    const bool kb = a.kbar != nullptr;
-    if (bf) {
-        if (d == 128) { if (kb) FDL_SCAN(uint16_t, 128, true); else FDL_SCAN(uint16_t, 128, false); }
-        else { if (kb) FDL_SCAN(uint16_t, 64, true); else FDL_SCAN(uint16_t, 64, false); }
-    } else {
-        if (d == 128) { if (kb) FDL_SCAN(float, 128, true); else FDL_SCAN(float, 128, false); }
-        else { if (kb) FDL_SCAN(float, 64, true); else FDL_SCAN(float, 64, false); }
-    }
-#undef FDL_SCAN
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(256), 0, stream, a, C, block_idx, R_out);
+    hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(kSelectThreads), 0, stream, a, C, block_idx, R_out);
     return hipGetLastError();
 }
 

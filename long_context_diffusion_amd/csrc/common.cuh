@@ -16,6 +16,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// x rounded up to a multiple of m (host-side workspace layout).
+inline size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
 // ------------------------------------------------------------------ bf16 helpers
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -31,11 +31,11 @@ struct BlockArgs {
     int64_t ksb, ksh, ksr;
     int B, Hq, Hkv, P, Gq, bs, nb;
     float scale;
-    float* kbar;      // [B, Hkv, nb, d] or NULL
-    double* qsum;     // [B, Hkv, d]
-    double* rpart;    // [B, Hkv, nb]
-    double* rfull;    // [B, nb]
-    int blocks_per_wg, scan_chunks;
+    float* kbar;            // [B, Hkv, nb, d] block means written by block_means, or NULL
+    const float* kbar_in;   // [B, Hkv, nb, d] block means the relevance is scored against
+    double* rpart;          // [B, Hkv, nparts, nb] partial relevance per query slice
+    double* rfull;          // [B, nb]
+    int nparts;             // query slices per (sequence, KV head)
 };
 
 hipError_t launch_pcgi_select(const float* conf, const uint8_t* mask, int B, int L, int k, int w,
@@ -47,7 +47,8 @@ size_t sink_workspace_bytes(int B, int Hkv, int L);
 hipError_t launch_sink_identify(fdl_dtype dtype, int d, SinkArgs a, int n_sinks, int32_t* sink_idx,
                                 float* user_scores, void* ws, hipStream_t stream);
 
-size_t block_workspace_bytes(int B, int Hkv, int P, int d, int bs);
+size_t block_workspace_bytes(int B, int Hq, int Hkv, int P, int d, int bs, int nq_max);
+hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStream_t stream);
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream);
 

@@ -8,7 +8,7 @@ the caller passes none).  A missing library, or a status other than FDL_OK,
 raises FdlError: there is no fallback path.
 
 Entry points (same names as the C functions without the fdl_ prefix):
-  pcgi_select, dense_attention, sink_identify, block_score_topc, sparse_attention.
+  pcgi_select, dense_attention, sink_identify, block_means, block_score_topc, sparse_attention.
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ EXPORTS = (
     "fdl_pcgi_select",
     "fdl_dense_attention_workspace_bytes", "fdl_dense_attention",
     "fdl_sink_identify_workspace_bytes", "fdl_sink_identify",
-    "fdl_block_score_topc_workspace_bytes", "fdl_block_score_topc",
+    "fdl_block_means", "fdl_block_score_topc_workspace_bytes", "fdl_block_score_topc",
     "fdl_sparse_attention_workspace_bytes", "fdl_sparse_attention",
 )
 
@@ -59,7 +59,8 @@ _SIGS = {
     "fdl_sink_identify_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "fdl_sink_identify": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F, _P, _I,
                                _P, _P, _P, _SZ, _P]),
-    "fdl_block_score_topc_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "fdl_block_means": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _I, _P, _P]),
+    "fdl_block_score_topc_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fdl_block_score_topc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
                                   _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "fdl_sparse_attention_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
@@ -236,26 +237,48 @@ def sink_identify(q, k, lse, n_sinks: int, *, q_idx=None, n_q=None, nq_max=None,
     return out[:, :n_sinks], scores
 
 
+def block_means(k, P: int, bs: int, *, out=None, stream=None):
+    """Mean key of every prompt block (fdl_block_means): [B, Hkv, nb, d] fp32."""
+    B, Hkv, L, d = k.shape
+    nb = -(-P // bs)
+    if out is None:
+        out = torch.empty((B, Hkv, nb, d), dtype=torch.float32, device=k.device)
+    if tuple(out.shape) != (B, Hkv, nb, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise FdlError(2, "block means: expected a contiguous [B, Hkv, nb, d] fp32 output")
+    st = lib().fdl_block_means(_dtype_code(k), B, Hkv, L, P, d, _ptr(k), _strides4(k), int(bs), _ptr(out),
+                               _stream(stream))
+    _check(st, "fdl_block_means")
+    return out
+
+
 def block_score_topc(q, k, P: int, bs: int, C: int, *, q_idx=None, n_q=None, nq_max=None,
-                     scale: float = 0.0, out=None, want_R=False, want_kbar=False, workspace=None,
-                     stream=None):
+                     scale: float = 0.0, out=None, want_R=False, want_kbar=False, kbar=None, L=None,
+                     workspace=None, stream=None):
     """Top-C prompt blocks by relevance to the active queries (fdl_block_score_topc).
 
+    k None: kbar must hold the block means (block_means) and L the sequence length.
     Returns (block_idx [B, C] int32, R [B, nb] fp64 or None, kbar [B, Hkv, nb, d] fp32 or None).
     """
     B, Hq, _, d = q.shape
-    Hkv, L = k.shape[1], k.shape[2]
+    if k is not None:
+        Hkv, L = k.shape[1], k.shape[2]
+    else:
+        if kbar is None or L is None:
+            raise FdlError(1, "block_score_topc without keys needs kbar and L")
+        Hkv = kbar.shape[1]
     qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
     dt = _dtype_code(q)
     nb = -(-P // bs)
     if out is None:
         out = torch.empty((B, max(C, 1)), dtype=torch.int32, device=q.device)
     R = torch.empty((B, nb), dtype=torch.float64, device=q.device) if want_R else None
-    kbar = torch.empty((B, Hkv, nb, d), dtype=torch.float32, device=q.device) if want_kbar else None
-    nbytes = int(lib().fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs))
+    if kbar is None and want_kbar:
+        kbar = torch.empty((B, Hkv, nb, d), dtype=torch.float32, device=q.device)
+    nbytes = int(lib().fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs, nq_max))
     ws, ws_n = _ws(workspace, q.device).get(nbytes)
+    ks = _strides4(k) if k is not None else Strides(0, 0, d)
     st = lib().fdl_block_score_topc(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
-                                    _ptr(k), _strides4(k), float(scale), int(bs), int(C), _ptr(out),
+                                    _ptr(k), ks, float(scale), int(bs), int(C), _ptr(out),
                                     _ptr(R), _ptr(kbar), ws, ws_n, _stream(stream))
     _check(st, "fdl_block_score_topc")
     return out[:, :C], R, kbar

@@ -6,9 +6,13 @@ in every layer); any other step runs (1) PCGI, (2) windows, (3) dense layers
 1..l_dense on the active rows with sinks taken from layer l_dense, then (4)
 block top-C and (5) sparse attention in every deeper layer, reusing the sinks.
 
-StepRunner only sequences the library's entry points on one stream with
-buffers allocated once, so a whole step can be captured in a HIP graph and
-replayed; it performs no arithmetic of its own.
+StepRunner only sequences the library's entry points with buffers allocated
+once, so a whole step can be captured in a HIP graph and replayed; it performs
+no arithmetic of its own.  The block means of step (4) depend on the prompt keys
+only; with overlap_means a sparse step computes them for every sparse layer on a
+second stream, one event per layer, while the layers before it attend on the
+caller's stream, and each layer's scoring waits for its own means.  Without it,
+each layer computes its means right before scoring them.
 """
 from __future__ import annotations
 
@@ -19,7 +23,7 @@ from . import fdl as F
 
 class StepRunner:
     def __init__(self, *, B, L, P, Hq, Hkv, d, dtype, n_t, rho, w, bs, C, n_sinks, layers, l_dense,
-                 scale=0.0, device="cuda"):
+                 scale=0.0, device="cuda", overlap_means=True):
         self.B, self.L, self.P, self.Hq, self.Hkv, self.d = B, L, P, Hq, Hkv, d
         self.n_t, self.rho, self.w, self.bs, self.C, self.n_sinks = n_t, rho, w, bs, C, n_sinks
         self.layers, self.l_dense, self.scale = layers, l_dense, scale
@@ -33,6 +37,12 @@ class StepRunner:
         self.n_active = torch.empty((B,), **i32)
         self.sinks = torch.empty((B, max(n_sinks, 1)), **i32)
         self.blocks = [torch.empty((B, max(C, 1)), **i32) for _ in range(layers)]
+        self.nb = -(-P // bs)
+        sparse_layers = range(l_dense, layers) if C else range(0)
+        self.kbar = {l: torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev) for l in sparse_layers}
+        self.overlap_means = overlap_means
+        self.side = torch.cuda.Stream(device=dev) if dev.type == "cuda" and overlap_means else None
+        self.means_done = {l: torch.cuda.Event() for l in sparse_layers}
         self.out = [torch.empty((B, Hq, self.nq_max, d), dtype=dtype, device=dev) for _ in range(layers)]
         self.lse = torch.empty((B, Hq, self.nq_max), dtype=torch.float32, device=dev)
         self.workspace = F.Workspace(dev)
@@ -42,7 +52,7 @@ class StepRunner:
         need = max(
             lib.fdl_dense_attention_workspace_bytes(dt, B, Hq, Hkv, L, d, self.nq_max),
             lib.fdl_sink_identify_workspace_bytes(dt, B, Hq, Hkv, L, d, self.nq_max),
-            lib.fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs),
+            lib.fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs, self.nq_max),
             lib.fdl_sparse_attention_workspace_bytes(dt, B, Hq, Hkv, L, P, d, self.nq_max, n_sinks, C, bs),
         )
         self.workspace.get(need)
@@ -63,6 +73,7 @@ class StepRunner:
             F.sink_identify(q, k, self.lse, self.n_sinks, out=self.sinks, **self._rows())
 
     def sparse_layer(self, l, q, k, v):
+        """Block top-C (block means from the keys) and sparse attention of one layer."""
         sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
         blocks = self.blocks[l][:, : self.C] if self.C else None
         if self.C:
@@ -72,9 +83,9 @@ class StepRunner:
     def sparse_step(self, conf, mask, qs, ks, vs, hooks=None):
         """A non-block-entry step; qs/ks/vs are per-layer [B, H, L, d] tensors.
 
-        `hooks` (optional) maps a stage name ("pcgi", "dense", "sinks", "blocks",
-        "sparse") to a (before, after) pair of callables run around each call of
-        that stage, e.g. to record events."""
+        `hooks` (optional) maps a stage name ("pcgi", "dense", "sinks", "means",
+        "blocks", "sparse") to a (before, after) pair of callables run around each
+        call of that stage on the stream it runs on, e.g. to record events."""
         def run(name, fn):
             h = hooks.get(name) if hooks else None
             if h:
@@ -82,6 +93,15 @@ class StepRunner:
             fn()
             if h:
                 h[1]()
+        main = torch.cuda.current_stream()
+        overlap = bool(self.kbar) and self.overlap_means
+        if overlap:
+            # block means of every sparse layer, on the second stream
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                for l, kb in self.kbar.items():
+                    run("means", lambda: F.block_means(ks[l], self.P, self.bs, out=kb))
+                    self.means_done[l].record(self.side)
         run("pcgi", lambda: self.pcgi(conf, mask))
         for l in range(self.layers):
             q, k, v = qs[l], ks[l], vs[l]
@@ -91,12 +111,18 @@ class StepRunner:
                     run("sinks", lambda: self.sinks_at(q, k))
             else:
                 if self.C:
-                    run("blocks", lambda: F.block_score_topc(q, k, self.P, self.bs, self.C,
-                                                            out=self.blocks[l], **self._rows()))
+                    if overlap:
+                        main.wait_event(self.means_done[l])
+                    else:
+                        run("means", lambda: F.block_means(k, self.P, self.bs, out=self.kbar[l]))
+                    run("blocks", lambda: F.block_score_topc(q, None, self.P, self.bs, self.C, kbar=self.kbar[l],
+                                                            L=self.L, out=self.blocks[l], **self._rows()))
                 sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
                 blocks = self.blocks[l][:, : self.C] if self.C else None
                 run("sparse", lambda: F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs,
                                                         out=self.out[l], **self._rows()))
+        if overlap:
+            main.wait_stream(self.side)
 
     def dense_refresh(self, qs, ks, vs, outs):
         """A block-entry step: every query row of every layer attends to all L keys."""

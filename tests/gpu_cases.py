@@ -60,6 +60,10 @@ def one_layer_step(wl, layer=0, step=0, device="cuda", check_refresh_rows=64, se
     Od, lse = F.dense_attention(Q, K, V, **kw)
     sinks, scores = F.sink_identify(Q, K, lse, wl.n_sinks, want_scores=True, **kw)
     blocks, R, kbar = F.block_score_topc(Q, K, wl.P, wl.bs, wl.C, want_R=True, want_kbar=True, **kw)
+    # the same scoring from means computed ahead by fdl_block_means (no keys passed)
+    kbar_ahead = F.block_means(K, wl.P, wl.bs)
+    blocks_ahead, R_ahead, _ = F.block_score_topc(Q, None, wl.P, wl.bs, wl.C, kbar=kbar_ahead, L=wl.L,
+                                                  want_R=True, **kw)
     Os, lse_s = F.sparse_attention(Q, K, V, wl.P, sinks, blocks, wl.bs, want_lse=True, **kw)
     refresh = None
     if check_refresh_rows:
@@ -67,6 +71,8 @@ def one_layer_step(wl, layer=0, step=0, device="cuda", check_refresh_rows=64, se
     torch.cuda.synchronize()
 
     actives = check_pcgi(wl, conf, mask, focus, n_focus, active, n_active)
+    assert torch.equal(kbar_ahead, kbar) and torch.equal(R_ahead, R) and torch.equal(blocks_ahead, blocks), \
+        "scoring from precomputed block means differs"
     Kf, Vf, Qf = synth.to_f64(K), synth.to_f64(V), synth.to_f64(Q)
     res = {"max_err": 0.0, "max_rel": 0.0, "set_swaps": 0}
     n_act = n_active.cpu().numpy()

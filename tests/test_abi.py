@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = F.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert sorted(F.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -73,12 +73,18 @@ def test_workspace_sizes():
                                                      1024, 16, 64, 128) > 0
     assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024) == \
         (32 * 32768 + 32768) * 4
+    # block scoring: relevance partials per (KV head, slice of <= 128 active rows, block), R, and
+    # room for the block means when they are computed from the keys
     nb = 252
-    assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32256, 128, 128) == \
-        (32 * 128 + 32 * nb + nb) * 8
+
+    def r256(x):
+        return -(-x // 256) * 256
+    for nq_max, parts in ((1024, 8), (100, 1), (1 << 20, 64)):
+        assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32256, 128, 128, nq_max) == \
+            r256(32 * parts * nb * 8) + r256(nb * 8) + 32 * nb * 128 * 4
     # invalid shapes report 0
     assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 5, 1024, 128, 64) == 0
-    assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 4, 4, 0, 64, 64) == 0
+    assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 4, 4, 0, 64, 64, 16) == 0
 
 
 def _pcgi(**kw):
@@ -159,3 +165,13 @@ def test_sparse_and_sink_and_block_validation():
                                        (192, 64, 4, 8, 5)]:
         assert lib.fdl_block_score_topc(F.FDL_BF16, 1, 4, 4, 256, P, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
                                         0.0, bs, C, FAKE, NULL, NULL, FAKE, ws_bytes, None) == status
+    # blocks without keys need the precomputed means
+    assert lib.fdl_block_score_topc(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, NULL, st,
+                                    0.0, 64, 4, FAKE, NULL, NULL, FAKE, 1 << 20, None) == 1
+    # block means: output required, P within [1, L], bs >= 1, aligned keys
+    for kw_, status in [(dict(kbar=NULL), 1), (dict(P=0), 2), (dict(P=257), 2), (dict(bs=0), 2),
+                        (dict(k=MISALIGNED), 4), (dict(k=NULL), 1), (dict(Hkv=0), 2)]:
+        a = dict(B=1, Hkv=4, L=256, P=192, d=128, k=FAKE, bs=64, kbar=FAKE)
+        a.update(kw_)
+        assert lib.fdl_block_means(F.FDL_BF16, a["B"], a["Hkv"], a["L"], a["P"], a["d"], a["k"], st, a["bs"],
+                                   a["kbar"], None) == status, kw_

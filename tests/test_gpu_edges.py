@@ -259,6 +259,8 @@ def test_graph_replays_match_eager():
         for o in run.out:             # eager work between replays: scribble over the outputs
             o.fill_(7.0)
         run.sinks.fill_(-5)
+        for kb in run.kbar.values():  # and over the block means the second stream writes
+            kb.fill_(3.0)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
