@@ -289,7 +289,19 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         float l_run = 0.0f;
 
         if (t_begin < t_end) {
-            // prologue: K and V of tiles t0 .. t0+2; those of t0 and t0+1 must land
+            // Ping-pong schedule.  Every wave runs the element sequence
+            //   M(-1) | V(0) | M(0) | V(1) | M(1) | ... | M(n-1)
+            // with a workgroup barrier after each element, where for tile t = t0 + j
+            //   V(j): softmax of S(t) -> P(t); K and V of this wave's 8 rows of tile t+2
+            //         are loaded; this wave's rows of V(t+1) are transposed into V^T(t+1)
+            //   M(j): O += V(t) P(t) from V^T(t); S(t+1) = K(t+1) Q^T
+            // Waves 4..7 run one element behind waves 0..3 (one extra barrier up front,
+            // waves 0..3 take theirs at the end).  Wave w and wave w+4 share a SIMD, so
+            // while one of them is in an MFMA element the other is in a VALU element.
+            // A wave only ever transposes the rows it loaded itself, so its loads need
+            // no barrier before its transposes; three stages of every buffer keep each
+            // tile until both halves of the workgroup are done with it.
+            const bool late = wv >= 4;
             int kn[2];
             keys2(t_begin, kn);
             issue_k(kn, s_k0);
@@ -297,27 +309,21 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             keys2(t_begin + 1, kn);
             issue_k(kn, s_k1);
             issue_v(kn, s_v1);
-            keys2(t_begin + 2, kn);
-            issue_k(kn, s_k2);
-            issue_v(kn, s_v2);
-            barrier_keep<4>();   // K(t0+2) and V(t0+2) may still be in flight
+            __builtin_amdgcn_s_waitcnt(0);
             transpose_v(s_v0, s_t0);
-            f32x16 st[2];
-            qk(s_k0, st);
-            barrier_keep<4>();   // V^T(t0) is complete; s_k0, s_v0 are free for tile t0+3
+            __syncthreads();   // K(t0), K(t0+1), V(t0+1) and V^T(t0) are complete
+            if (late) barrier_keep<0>();
 
-            // Iteration for tile t (stage j = (t - t0) % 3): K and V of tile t+3 go to
-            // stage j, V(t+1) becomes V^T(t+1), S(t+1) is computed from K(t+1), and the
-            // softmax of S(t) and O += V(t) P(t) run on stage j.
-            auto iteration = [&](int t, const uint8_t* kread, uint8_t* kdma, uint8_t* vdma, const uint8_t* vnext,
-                                 uint8_t* tnext, const uint8_t* tread) __attribute__((always_inline)) {
-                keys2(t + 3, kn);
+            f32x16 st[2];
+            bf16x8 pf[4];
+            qk(s_k0, st);     // M(-1)
+            barrier_keep<0>();
+
+            auto elem_v = [&](int t, uint8_t* kdma, uint8_t* vdma, const uint8_t* vnext, uint8_t* tnext)
+                __attribute__((always_inline)) {
+                keys2(t + 2, kn);
                 issue_k(kn, kdma);
                 issue_v(kn, vdma);
-                transpose_v(vnext, tnext);
-
-                f32x16 sn[2];
-                qk(kread, sn);
                 const int valid_here = n_keys - t * 64;
                 if (valid_here < 64) {
 #pragma unroll
@@ -348,7 +354,6 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 }
                 const float mneg = -m_run;
                 float psum = 0.0f;
-                bf16x8 pf[4];
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -358,7 +363,11 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                         pf[kc][j] = static_cast<__bf16>(pv);
                     }
                 l_run += psum;
-
+                // this wave's rows of V(t+1) landed by the end of its previous M element
+                transpose_v(vnext, tnext);
+                barrier_keep<4>();   // the loads of tile t+2 may stay in flight
+            };
+            auto elem_m = [&](const uint8_t* tread, const uint8_t* kread) __attribute__((always_inline)) {
                 // O^T += V^T P^T, the 4 fragments of a key chunk read before its MFMAs
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc) {
@@ -370,17 +379,23 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                     for (int db = 0; db < NDB; ++db)
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[kc], acc[db], 0, 0, 0);
                 }
-                // this iteration's 4 loads may stay in flight; every older one has landed
-                barrier_keep<4>();
-                st[0] = sn[0];
-                st[1] = sn[1];
+                qk(kread, st);
+                barrier_keep<0>();   // this wave's loads of the next tile have landed
             };
-            // tile t_begin + j: K in s_k[j % 3], V in s_v[j % 3], V^T in s_t[j % 3]
+            // tile t0 + j: K in s_k[j % 3], V in s_v[j % 3], V^T in s_t[j % 3]
             for (int t = t_begin; t < t_end; t += 3) {
-                iteration(t, s_k1, s_k0, s_v0, s_v1, s_t1, s_t0);
-                if (t + 1 < t_end) iteration(t + 1, s_k2, s_k1, s_v1, s_v2, s_t2, s_t1);
-                if (t + 2 < t_end) iteration(t + 2, s_k0, s_k2, s_v2, s_v0, s_t0, s_t2);
+                elem_v(t, s_k2, s_v2, s_v1, s_t1);
+                elem_m(s_t0, s_k1);
+                if (t + 1 < t_end) {
+                    elem_v(t + 1, s_k0, s_v0, s_v2, s_t2);
+                    elem_m(s_t1, s_k2);
+                }
+                if (t + 2 < t_end) {
+                    elem_v(t + 2, s_k1, s_v1, s_v0, s_t0);
+                    elem_m(s_t2, s_k0);
+                }
             }
+            if (!late) barrier_keep<0>();
             __builtin_amdgcn_s_waitcnt(0);   // drain the loads past the split before LDS is reused
         }
 
