@@ -270,15 +270,22 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         // ---- V tile -> V^T: lane (k, c8) moves rows 2k, 2k+1 x d = 8c8 .. 8c8+7
         const int tr_c8 = tid & 15, tr_k = tid >> 4;
         const int tr_s = vt_row(2 * tr_k);   // slots of rows 2k, 2k+1: tr_s, tr_s + 1
-        auto transpose_v = [&](const uint8_t* vraw, uint8_t* vt) __attribute__((always_inline)) {
-            const u32x4 ra = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k) * kRowB + 16 * tr_c8);
-            const u32x4 rb = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k + 1) * kRowB + 16 * tr_c8);
+        auto transpose_load = [&](const uint8_t* vraw, u32x4& ra, u32x4& rb) __attribute__((always_inline)) {
+            ra = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k) * kRowB + 16 * tr_c8);
+            rb = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k + 1) * kRowB + 16 * tr_c8);
+        };
+        auto transpose_store = [&](const u32x4& ra, const u32x4& rb, uint8_t* vt) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t x = ra[e >> 1], y = rb[e >> 1];
                 const uint32_t w = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
                 *reinterpret_cast<uint32_t*>(vt + vt_off(8 * tr_c8 + e, tr_s)) = w;
             }
+        };
+        auto transpose_v = [&](const uint8_t* vraw, uint8_t* vt) __attribute__((always_inline)) {
+            u32x4 ra, rb;
+            transpose_load(vraw, ra, rb);
+            transpose_store(ra, rb, vt);
         };
         f32x16 acc[NDB];
 #pragma unroll
@@ -321,6 +328,10 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
 
             auto elem_v = [&](int t, uint8_t* kdma, uint8_t* vdma, const uint8_t* vnext, uint8_t* tnext)
                 __attribute__((always_inline)) {
+                // this wave's rows of V(t+1) (landed by the end of its previous M element) are
+                // read first, so the LDS round trip hides behind the softmax
+                u32x4 ra, rb;
+                transpose_load(vnext, ra, rb);
                 keys2(t + 2, kn);
                 issue_k(kn, kdma);
                 issue_v(kn, vdma);
@@ -334,11 +345,15 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                             if (row_pos(r) >= valid_here) st[kb][i] = -INFINITY;
                         }
                 }
-                float mx = fmaxf(st[0][0], st[0][1]);
+                // max and sum as 4 independent chains each (short dependency chains)
+                float mq[4];
 #pragma unroll
-                for (int i = 2; i < 16; ++i) mx = fmaxf(mx, st[0][i]);
+                for (int c = 0; c < 4; ++c) {
+                    mq[c] = fmaxf(st[c >> 1][8 * (c & 1)], st[c >> 1][8 * (c & 1) + 1]);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[1][i]);
+                    for (int j = 2; j < 8; ++j) mq[c] = fmaxf(mq[c], st[c >> 1][8 * (c & 1) + j]);
+                }
+                float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
                 mx = fmaxf(mx, xhalf(mx));
                 const float mc = mx * a.sl2;
                 const bool need = mc > m_run + kSlack;
@@ -353,18 +368,17 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                     m_run = m_new;
                 }
                 const float mneg = -m_run;
-                float psum = 0.0f;
+                float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const float pv = fast_exp2(fmaf(st[kc >> 1][8 * (kc & 1) + j], a.sl2, mneg));
-                        psum += pv;
+                        ps[kc] += pv;
                         pf[kc][j] = static_cast<__bf16>(pv);
                     }
-                l_run += psum;
-                // this wave's rows of V(t+1) landed by the end of its previous M element
-                transpose_v(vnext, tnext);
+                l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                transpose_store(ra, rb, tnext);
                 barrier_keep<4>();   // the loads of tile t+2 may stay in flight
             };
             auto elem_m = [&](const uint8_t* tread, const uint8_t* kread) __attribute__((always_inline)) {
