@@ -693,10 +693,11 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     // groups of q_tiles consecutive slots per XCD: round the group count up to a multiple of 8
     const int64_t groups = static_cast<int64_t>(a.B) * a.Hkv * pl.n_splits;
     const dim3 grid(static_cast<unsigned>((groups + 7) / 8 * 8 * pl.q_tiles));
-    if (d128) launch_attn_bf16_d128(a, stream);
+    hipError_t err = hipSuccess;
+    if (d128) err = launch_attn_bf16_d128(a, stream);
     else if (d == 128) launch_kernel<128>(dtype, a, grid, stream);
     else launch_kernel<64>(dtype, a, grid, stream);
-    hipError_t err = hipGetLastError();
+    if (err == hipSuccess) err = hipGetLastError();
     if (err != hipSuccess || pl.n_splits == 1) return err;
     const int64_t n_rows = static_cast<int64_t>(a.B) * a.Hq * a.nq_max;
     const int64_t rows_per_wg = 256 / (d / kMergeEpt);

@@ -238,7 +238,6 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         auto issue_v = [&](const int (&key)[2], uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int r = 8 * wv + 4 * i + g4;
                 const uint16_t* src = vbase + static_cast<int64_t>(key[i]) * vsr + 8 * (lane & 15);
                 __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * (2 * wv + i)), 16, 0, 0);
             }

@@ -9,16 +9,19 @@
 // The block means depend on the prompt keys only, so they are a separate pass
 // (block_means) that a caller can run for every layer ahead of the layer that
 // needs them, e.g. on a second stream while earlier layers attend.  Scoring is
-// then a small pass over the means:
-//   block_means      one streaming read of the prompt keys, 16 bytes per lane,
-//                    fp64 sums (exact for bf16/fp32 inputs), one rounding of the
-//                    mean to fp32.
-//   block_relevance  R is linear in the queries: qsum = sum of the query rows of a
-//                    slice of the active rows of one KV head's query heads (fp64),
-//                    then that slice's partial R_b = qsum . kbar_b for every block.
-//   block_select     sums the partials in a fixed order (KV head, then slice),
-//                    scales by scale, and keeps the top-C blocks (lower block index
-//                    first among equal scores), ascending.
+// then three small passes; the two that read the queries and the means are spread
+// over many workgroups (a single CU pulls only about 20 GB/s from memory, so a
+// pass that one workgroup runs is bound by it):
+//   block_means        one streaming read of the prompt keys, 16 bytes per lane,
+//                      fp64 sums (exact for bf16/fp32 inputs), one rounding of the
+//                      mean to fp32.
+//   block_qsum         R is linear in the queries: the sum of the query rows of
+//                      every 64-row chunk of one KV head's query heads (fp64).
+//   block_dots         per (KV head, 32 blocks): the chunk sums added in chunk
+//                      order give qsum_g, and qsum_g . kbar_gb is that head's part of R_b.
+//   block_select       one workgroup per sequence adds the head parts in head order,
+//                      scales by `scale`, and keeps the top-C blocks (lower block
+//                      index first among equal scores), ascending.
 
 #include "ops.cuh"
 
@@ -27,8 +30,8 @@ namespace fdl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPartRows = 128;     // active rows per relevance slice (at most kMaxParts slices)
-constexpr int kMaxParts = 64;
+constexpr int kQsumRows = 64;      // packed query rows per query-sum workgroup
+constexpr int kDotBlocks = 32;     // blocks per dot-product workgroup
 constexpr int kMeansBlocks = 2;    // blocks per block_means workgroup
 
 template <typename T>
@@ -45,12 +48,6 @@ template <>
 __device__ __forceinline__ void unpack16<float>(const u32x4& x, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(x[i]);
-}
-
-// Relevance slices of sequence b: as many kPartRows-row slices as its active rows
-// need, at most a.nparts (the grid's bound); rows are split evenly between them.
-__device__ __forceinline__ int relevance_parts(const BlockArgs& a, int rows) {
-    return max(1, min(a.nparts, (rows + kPartRows - 1) / kPartRows));
 }
 
 // kbar[b][g][blk][e] = mean of K[b][g][blk*bs .. min((blk+1)*bs, P))[e], one rounding.
@@ -118,109 +115,105 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
     }
 }
 
-// rpart[b][g][part][blk] = qsum_part . kbar[b][g][blk], qsum_part = sum of the query rows of
-// slice `part` of the Gq*nq packed rows of KV head g (packed row p: head g*Gq + p%Gq, row p/Gq).
+// qpart[b][g][c][e] = sum over the packed rows [64c, 64c + 64) of KV head g of q[..][e] in
+// fp64 (packed row p: query head g*Gq + p%Gq, active row p/Gq); zeros past the rows.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void block_relevance_kernel(const BlockArgs a) {
-    constexpr int EPP = 16 / sizeof(T);
-    constexpr int NP = D / EPP;
-    constexpr int RG = kThreads / NP;
-    constexpr int kBatch = 8;
-    constexpr int LPB = 4;                  // lanes per block in the dot products
-    constexpr int EPL = D / LPB;            // kbar elements per lane
+__global__ __launch_bounds__(kThreads) void block_qsum_kernel(const BlockArgs a) {
+    constexpr int EPP = 16 / sizeof(T);     // elements per 16-byte piece
+    constexpr int NP = D / EPP;             // pieces per row
+    constexpr int RG = kThreads / NP;       // row groups
+    constexpr int RPT = kQsumRows / RG;     // rows per thread
+    static_assert(RPT * RG == kQsumRows, "row split");
     __shared__ double s_q[RG][D];
-    __shared__ double s_qsum[D];
     const int tid = threadIdx.x;
-    const int part = blockIdx.x % a.nparts;
-    const int bg = blockIdx.x / a.nparts;
+    const int c = blockIdx.x % a.nchunks;
+    const int bg = blockIdx.x / a.nchunks;
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
     const int rows = a.Gq * nq;
-    const int parts = relevance_parts(a, rows);
-    if (part >= parts) return;
-    const int rpp = (rows + parts - 1) / parts;
-    const int p_lo = part * rpp, p_hi = min(rows, p_lo + rpp);
-
-    // the block means of the first pass go out before the queries: both round trips overlap
-    const float* kb = a.kbar_in + (static_cast<int64_t>(b) * a.Hkv + g) * a.nb * D;
-    const int sub = tid % LPB;
-    f32x4 kx[EPL / 4];
-    {
-        const int blk = min(tid / LPB, a.nb - 1);
-        const float* row = kb + static_cast<int64_t>(blk) * D + sub * EPL;
-#pragma unroll
-        for (int i = 0; i < EPL / 4; ++i) kx[i] = *reinterpret_cast<const f32x4*>(row + 4 * i);
-    }
-
-    // ---- qsum of this slice (fp64)
     const int piece = tid % NP, rg = tid / NP;
+    u32x4 x[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const int p = c * kQsumRows + rg + RG * u;
+        x[u] = u32x4{0u, 0u, 0u, 0u};
+        if (p < rows) {
+            const int r = p / a.Gq, hh = p % a.Gq;
+            const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
+            x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + b * a.qsb + (g * a.Gq + hh) * a.qsh +
+                                                   static_cast<int64_t>(phys) * a.qsr + piece * EPP);
+        }
+    }
     double acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
-    // packed row p = r * Gq + hh (query head g*Gq + hh, row r); this thread's rows advance by RG
-    const int step_r = RG / a.Gq, step_h = RG % a.Gq;
-    int r_cur = (p_lo + rg) / a.Gq, h_cur = (p_lo + rg) % a.Gq;
-    for (int p0 = p_lo + rg; p0 < p_hi; p0 += RG * kBatch) {
-        int64_t off[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const bool in = p0 + u * RG < p_hi;
-            const int r = in ? r_cur : 0, hh = in ? h_cur : 0;
-            const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
-            off[u] = b * a.qsb + (g * a.Gq + hh) * a.qsh + static_cast<int64_t>(phys) * a.qsr + piece * EPP;
-            r_cur += step_r;
-            h_cur += step_h;
-            if (h_cur >= a.Gq) { h_cur -= a.Gq; ++r_cur; }
-        }
-        u32x4 x[kBatch];
+    for (int u = 0; u < RPT; ++u) {
+        float v[EPP];
+        unpack16<T>(x[u], v);
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + off[u]);
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            if (p0 + u * RG >= p_hi) continue;
-            float v[EPP];
-            unpack16<T>(x[u], v);
-#pragma unroll
-            for (int e = 0; e < EPP; ++e) acc[e] += static_cast<double>(v[e]);
-        }
+        for (int e = 0; e < EPP; ++e) acc[e] += static_cast<double>(v[e]);
     }
 #pragma unroll
     for (int e = 0; e < EPP; ++e) s_q[rg][piece * EPP + e] = acc[e];
     __syncthreads();
+    double* out = a.qpart + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nchunks + c) * D;
     for (int e = tid; e < D; e += kThreads) {
-        double s = 0.0;
-        for (int r = 0; r < RG; ++r) s += s_q[r][e];
-        s_qsum[e] = s;
+        double t = 0.0;
+        for (int r = 0; r < RG; ++r) t += s_q[r][e];
+        out[e] = t;
+    }
+}
+
+// rpart[b][g][blk] = qsum_g . kbar[b][g][blk] for the kDotBlocks blocks of this workgroup,
+// qsum_g being the chunk sums added in chunk order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void block_dots_kernel(const BlockArgs a) {
+    constexpr int LPB = kThreads / kDotBlocks;   // lanes per block
+    constexpr int EPL = D / LPB;                 // kbar elements per lane
+    static_assert(EPL % 4 == 0, "16-byte kbar pieces");
+    __shared__ double s_qsum[D];
+    const int tid = threadIdx.x;
+    const int nbc = (a.nb + kDotBlocks - 1) / kDotBlocks;
+    const int bc = blockIdx.x % nbc;
+    const int bg = blockIdx.x / nbc;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    // this workgroup's block means go out first; qsum_g meanwhile
+    const int blk = bc * kDotBlocks + tid / LPB, sub = tid % LPB;
+    const float* krow = a.kbar_in + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nb + min(blk, a.nb - 1)) * D + sub * EPL;
+    f32x4 kx[EPL / 4];
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) kx[i] = *reinterpret_cast<const f32x4*>(krow + 4 * i);
+    const double* qp = a.qpart + (static_cast<int64_t>(b) * a.Hkv + g) * a.nchunks * D;
+    for (int e = tid; e < D; e += kThreads) {
+        double t = 0.0;
+        int c = 0;
+        for (; c + 8 <= a.nchunks; c += 8) {
+            double y[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) y[u] = qp[(c + u) * D + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t += y[u];
+        }
+        for (; c < a.nchunks; ++c) t += qp[c * D + e];
+        s_qsum[e] = t;
     }
     __syncthreads();
-
-    // ---- partial relevance of every block: LPB consecutive lanes share a block
-    double* rp = a.rpart + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nparts + part) * a.nb;
-    for (int blk = tid / LPB; blk < a.nb; blk += kThreads / LPB) {
-        f32x4 x[EPL / 4];
-        if (blk < kThreads / LPB) {
+    double s = 0.0;
 #pragma unroll
-            for (int i = 0; i < EPL / 4; ++i) x[i] = kx[i];
-        } else {
-            const float* row = kb + static_cast<int64_t>(blk) * D + sub * EPL;
+    for (int i = 0; i < EPL / 4; ++i)
 #pragma unroll
-            for (int i = 0; i < EPL / 4; ++i) x[i] = *reinterpret_cast<const f32x4*>(row + 4 * i);
-        }
-        double s = 0.0;
+        for (int j = 0; j < 4; ++j) s = fma(static_cast<double>(kx[i][j]), s_qsum[sub * EPL + 4 * i + j], s);
 #pragma unroll
-        for (int i = 0; i < EPL / 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s = fma(static_cast<double>(x[i][j]), s_qsum[sub * EPL + 4 * i + j], s);
-        s += __shfl_xor(s, 1, 64);   // (s0 + s1) + (s2 + s3) in every lane of the four
-        s += __shfl_xor(s, 2, 64);
-        if (sub == 0) rp[blk] = s;
-    }
+    for (int off = 1; off < LPB; off <<= 1) s += __shfl_xor(s, off, kWave);   // every lane of the block
+    if (sub == 0 && blk < a.nb) a.rpart[(static_cast<int64_t>(b) * a.Hkv + g) * a.nb + blk] = s;
 }
 
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectLds = 2048;   // blocks ranked in LDS
-constexpr int kSlices = 4;         // threads summing the partials of one block
+constexpr int kSlices = 4;         // threads summing the head parts of one block
 
+// R_b = scale * sum over g of rpart[b][g][blk] (KV heads in order), then the top-C blocks.
 __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const BlockArgs a, int C,
                                                                        int32_t* block_idx, double* R_out) {
     __shared__ SelectSmem sm;
@@ -228,35 +221,23 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
     __shared__ double s_slice[kSlices][kSelectThreads / kSlices];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
-    const int parts = relevance_parts(a, a.Gq * nq);
-    // thread slice `slice` sums KV heads [slice*per, (slice+1)*per) x every slice of rows
+    // thread slice `slice` sums KV heads [slice*per, (slice+1)*per)
     const int per = (a.Hkv + kSlices - 1) / kSlices;
     double* R = a.rfull + static_cast<int64_t>(b) * a.nb;
-    const double* rp = a.rpart + static_cast<int64_t>(b) * a.Hkv * a.nparts * a.nb;
+    const double* rp = a.rpart + static_cast<int64_t>(b) * a.Hkv * a.nb;
     const int slice = tid / (kSelectThreads / kSlices), lb = tid % (kSelectThreads / kSlices);
     const int g0 = slice * per, g1 = min(a.Hkv, g0 + per);
-    const int terms = max(g1 - g0, 0) * parts;
     for (int blk0 = 0; blk0 < a.nb; blk0 += kSelectThreads / kSlices) {
         const int blk = blk0 + lb;
         double s = 0.0;
         if (blk < a.nb) {
-            // term t: KV head g0 + t / parts, row slice t % parts; addresses advance without a division
-            int g = g0, pi = 0;
-            for (int t = 0; t < terms; t += 16) {
+            // 16 loads in flight; head g's part is nb doubles after head g-1's
+            for (int g = g0; g < g1; g += 16) {
                 double x[16];
-                int gg = g, pp = pi;
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const bool in = t + u < terms;
-                    const double y = rp[(static_cast<int64_t>(in ? gg : g0) * a.nparts + (in ? pp : 0)) * a.nb + blk];
-                    x[u] = in ? y : 0.0;
-                    if (++pp == parts) { pp = 0; ++gg; }
-                }
+                for (int u = 0; u < 16; ++u) x[u] = g + u < g1 ? rp[static_cast<int64_t>(g + u) * a.nb + blk] : 0.0;
 #pragma unroll
                 for (int u = 0; u < 16; ++u) s += x[u];
-                g = gg;
-                pi = pp;
             }
         }
         s_slice[slice][lb] = s;
@@ -285,19 +266,20 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
     }
 }
 
-int host_parts(int Gq, int nq_max) {
-    const int64_t parts = (static_cast<int64_t>(Gq) * nq_max + kPartRows - 1) / kPartRows;
-    return static_cast<int>(parts < 1 ? 1 : parts > kMaxParts ? kMaxParts : parts);
+int host_chunks(int Gq, int nq_max) {
+    const int64_t c = (static_cast<int64_t>(Gq) * nq_max + kQsumRows - 1) / kQsumRows;
+    return static_cast<int>(c < 1 ? 1 : c);
 }
 
 }  // namespace
 
 size_t block_workspace_bytes(int B, int Hq, int Hkv, int P, int d, int bs, int nq_max) {
     const int64_t nb = (static_cast<int64_t>(P) + bs - 1) / bs;
-    const int parts = host_parts(Hq / Hkv, nq_max);
-    return round_up(static_cast<size_t>(B) * Hkv * parts * nb * sizeof(double), 256) +   // partial R
-           round_up(static_cast<size_t>(B) * nb * sizeof(double), 256) +                 // R
-           static_cast<size_t>(B) * Hkv * nb * d * sizeof(float);                        // block means
+    const int chunks = host_chunks(Hq / Hkv, nq_max);
+    return round_up(static_cast<size_t>(B) * Hkv * chunks * d * sizeof(double), 256) +   // query chunk sums
+           round_up(static_cast<size_t>(B) * Hkv * nb * sizeof(double), 256) +          // per-head R parts
+           round_up(static_cast<size_t>(B) * nb * sizeof(double), 256) +                // R
+           static_cast<size_t>(B) * Hkv * nb * d * sizeof(float);                       // block means
 }
 
 hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStream_t stream) {
@@ -312,10 +294,12 @@ hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStr
 
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream) {
-    a.nparts = host_parts(a.Gq, a.nq_max);
+    a.nchunks = host_chunks(a.Gq, a.nq_max);
     uint8_t* w = static_cast<uint8_t*>(ws);
+    a.qpart = reinterpret_cast<double*>(w);
+    w += round_up(static_cast<size_t>(a.B) * a.Hkv * a.nchunks * d * sizeof(double), 256);
     a.rpart = reinterpret_cast<double*>(w);
-    w += round_up(static_cast<size_t>(a.B) * a.Hkv * a.nparts * a.nb * sizeof(double), 256);
+    w += round_up(static_cast<size_t>(a.B) * a.Hkv * a.nb * sizeof(double), 256);
     a.rfull = reinterpret_cast<double*>(w);
     w += round_up(static_cast<size_t>(a.B) * a.nb * sizeof(double), 256);
     if (a.k) {
@@ -325,12 +309,18 @@ hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, i
         if (err != hipSuccess) return err;
     }
     a.kbar_in = a.kbar;
-    const dim3 rgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * a.nparts));
-#define FDL_REL(T, DD) hipLaunchKernelGGL((block_relevance_kernel<T, DD>), rgrid, dim3(kThreads), 0, stream, a)
-    if (dtype == FDL_BF16) { if (d == 128) FDL_REL(uint16_t, 128); else FDL_REL(uint16_t, 64); }
-    else { if (d == 128) FDL_REL(float, 128); else FDL_REL(float, 64); }
-#undef FDL_REL
+    const dim3 qgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * a.nchunks));
+#define FDL_QSUM(T, DD) hipLaunchKernelGGL((block_qsum_kernel<T, DD>), qgrid, dim3(kThreads), 0, stream, a)
+    if (dtype == FDL_BF16) { if (d == 128) FDL_QSUM(uint16_t, 128); else FDL_QSUM(uint16_t, 64); }
+    else { if (d == 128) FDL_QSUM(float, 128); else FDL_QSUM(float, 64); }
+#undef FDL_QSUM
     hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nbc = (a.nb + kDotBlocks - 1) / kDotBlocks;
+    const dim3 dgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * nbc));
+    if (d == 128) hipLaunchKernelGGL(block_dots_kernel<128>, dgrid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(block_dots_kernel<64>, dgrid, dim3(kThreads), 0, stream, a);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(kSelectThreads), 0, stream, a, C, block_idx, R_out);
     return hipGetLastError();

@@ -80,27 +80,25 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 
 // Exclusive prefix sum over the block (blockDim.x a multiple of 64, <= 1024).
 // `s_tmp` holds >= 17 ints.  Returns the exclusive prefix; *total gets the block sum.
+// Every thread reads the per-wave totals itself (broadcast LDS reads), so there is no
+// serial pass over the waves.
 __device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
-    int inc = wave_inclusive_sum(x);
+    const int inc = wave_inclusive_sum(x);
     if (lane == kWave - 1) s_tmp[wv] = inc;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int i = 0; i < nw; ++i) {
-            int t = s_tmp[i];
-            s_tmp[i] = run;
-            run += t;
-        }
-        s_tmp[16] = run;
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = i < nw ? s_tmp[i] : 0;
+        before += i < wv ? t : 0;
+        tot += t;
     }
-    __syncthreads();
-    int excl = s_tmp[wv] + inc - x;
-    *total = s_tmp[16];
-    __syncthreads();
-    return excl;
+    *total = tot;
+    __syncthreads();   // s_tmp is free for the next call
+    return before + inc - x;
 }
 
 // ------------------------------------------------------------------ top-k selection
@@ -146,6 +144,25 @@ __device__ __forceinline__ void for_each_key(int lo, int hi, KeyFn key_of, Body 
     }
 }
 
+// hist[digit] += 1 for every lane of the wave with `on`.  Skewed keys put most of a
+// wave on one or two digits, and same-address LDS atomics serialise, so the lanes that
+// share a leader lane's digit are counted with one atomic, for up to 4 leaders; the
+// lanes left over (many distinct digits, hence few conflicts) add their own.
+__device__ __forceinline__ void wave_count(int* hist, int digit, bool on) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t pending = __ballot(on);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        if (pending == 0) break;   // the same on every lane
+        const int leader = __builtin_ctzll(pending);
+        const int dl = __shfl(digit, leader, kWave);
+        const uint64_t same = __ballot(on && digit == dl) & pending;
+        if (lane == leader) atomicAdd(&hist[dl], static_cast<int>(__popcll(same)));
+        pending &= ~same;
+    }
+    if ((pending >> lane) & 1ull) atomicAdd(&hist[digit], 1);
+}
+
 // Radix select: the k-th largest ordered key among the valid entries of [0, n)
 // (1 <= k <= number of valid entries).  Every thread of the block must call it.
 template <typename U, typename KeyFn>
@@ -161,7 +178,7 @@ __device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
         for (int i = threadIdx.x; i < nw * 256; i += blockDim.x) sm->hist[i / 256][i % 256] = 0;
         __syncthreads();
         for_each_key<U>(lo, hi, key_of, [&](int, U kj) {
-            if ((kj & prefix_mask) == prefix) atomicAdd(&sm->hist[wv][static_cast<int>((kj >> shift) & 0xff)], 1);
+            wave_count(sm->hist[wv], static_cast<int>((kj >> shift) & 0xff), (kj & prefix_mask) == prefix);
         });
         __syncthreads();
         if (threadIdx.x < kWave) {
@@ -212,9 +229,12 @@ __device__ int block_emit_topk(int n, int k, KeyFn key_of, IdxFn idx_of, int32_t
     if (!take_all && nsel > 0) thr = block_kth_largest<U>(n, nsel, key_of, sm);
     int gt = 0, eq = 0;
     if (nsel > 0) {
+        // counted without branches: a conditional increment of one of two counters
+        // makes the compiler keep them in an indexed stack array (scratch memory)
         for_each_key<U>(lo, hi, key_of, [&](int, U kj) {
-            if (take_all || kj > thr) ++gt;
-            else if (kj == thr) ++eq;
+            const bool above = take_all || kj > thr;
+            gt += above ? 1 : 0;
+            eq += (!above && kj == thr) ? 1 : 0;
         });
     }
     int gt_total, eq_total;
@@ -223,60 +243,58 @@ __device__ int block_emit_topk(int n, int k, KeyFn key_of, IdxFn idx_of, int32_t
     const int ties_taken = nsel - gt_total;  // lowest-index ties fill the rest
     if (nsel > 0) {
         for_each_key<U>(lo, hi, key_of, [&](int j, U kj) {
-            if (take_all || kj > thr) {
-                out[gt_before + min(eq_before, ties_taken)] = idx_of(j);
-                ++gt_before;
-            } else if (kj == thr) {
-                if (eq_before < ties_taken) out[gt_before + eq_before] = idx_of(j);
-                ++eq_before;
-            }
+            const bool above = take_all || kj > thr;
+            const bool tie = !above && kj == thr;
+            if (above) out[gt_before + min(eq_before, ties_taken)] = idx_of(j);
+            if (tie && eq_before < ties_taken) out[gt_before + eq_before] = idx_of(j);
+            gt_before += above ? 1 : 0;
+            eq_before += tie ? 1 : 0;
         });
     }
     for (int i = nsel + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
     return nsel;
 }
 
-// Selection over keys already in LDS (every entry valid).  Up to 2048 entries each
-// thread ranks its own entries against all others; larger sets use the radix select.
+// Selection over keys already in LDS (every entry valid).  Up to blockDim.x entries are
+// ranked directly: G = blockDim.x / n (a power of two, at most 64) consecutive threads
+// share entry j, each counts the entries i = part, part + G, ... that beat it (larger
+// key, or equal key and lower index), and a shuffle adds the G counts.  Larger sets use
+// the radix select.
 template <typename U, typename IdxFn>
 __device__ int block_topk_lds(int n, int k, const U* keys, IdxFn idx_of, int32_t* out, int cap,
                               SelectSmem* sm) {
     const int nsel = min(max(k, 0), n);
-    if (n > 2048 || blockDim.x * 32 < static_cast<unsigned>(n)) {
+    if (n > static_cast<int>(blockDim.x)) {
         auto key_of = [&](int j, U* key) -> bool {
             *key = keys[j];
             return true;
         };
         return block_emit_topk<U>(n, k, key_of, idx_of, out, cap, sm);
     }
-    int lo, hi;
-    thread_chunk(n, &lo, &hi);
-    uint32_t sel = 0;
-    int cnt = 0;
-    for (int j = lo; j < hi; ++j) {
+    int G = 1;
+    while (G < kWave && 2 * G * n <= static_cast<int>(blockDim.x)) G *= 2;
+    const int j = static_cast<int>(threadIdx.x) / G;
+    const int part = static_cast<int>(threadIdx.x) % G;
+    int beat = 0;
+    if (j < n) {
         const U kj = keys[j];
-        int rank = 0;
-        int i = 0;
-        for (; i + 8 <= n; i += 8) {   // eight independent LDS reads in flight
-            U ki[8];
+        constexpr int kBatch = 8;
+        for (int i0 = part; i0 < n; i0 += kBatch * G) {
+            U ki[kBatch];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) ki[u] = keys[i + u];
+            for (int u = 0; u < kBatch; ++u) ki[u] = keys[min(i0 + u * G, n - 1)];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) rank += (ki[u] > kj || (ki[u] == kj && i + u < j)) ? 1 : 0;
-        }
-        for (; i < n; ++i) {
-            const U ki = keys[i];
-            rank += (ki > kj || (ki == kj && i < j)) ? 1 : 0;
-        }
-        if (rank < nsel) {
-            sel |= 1u << (j - lo);
-            ++cnt;
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = i0 + u * G;
+                beat += (i < n && (ki[u] > kj || (ki[u] == kj && i < j))) ? 1 : 0;
+            }
         }
     }
+    for (int off = G >> 1; off > 0; off >>= 1) beat += __shfl_xor(beat, off, kWave);
+    const int take = (j < n && part == 0 && beat < nsel) ? 1 : 0;
     int total;
-    int off = block_exclusive_sum(cnt, sm->tmp, &total);
-    for (int j = lo; j < hi; ++j)
-        if ((sel >> (j - lo)) & 1u) out[off++] = idx_of(j);
+    const int pos = block_exclusive_sum(take, sm->tmp, &total);   // thread order is entry order
+    if (take) out[pos] = idx_of(j);
     for (int i = nsel + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
     return nsel;
 }

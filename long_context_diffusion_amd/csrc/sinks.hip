@@ -15,7 +15,9 @@
 //                 the KV head) in a fixed order.  Q rows stream through LDS in
 //                 blocks of 32.
 //   sink_reduce   adds the per-KV-head partials in head order (deterministic).
-//   sink_select   radix top-n over the L scores of each sequence, ascending output.
+//   sink_select   top-n over the L scores of each sequence, ascending output: a
+//                 threshold from the per-thread maxima, then an exact rank of the
+//                 few scores above it (a radix select when there are many).
 
 #include "ops.cuh"
 
@@ -212,26 +214,137 @@ __global__ __launch_bounds__(256) void sink_reduce_kernel(const SinkArgs a) {
     a.scores[i] = s;
 }
 
-constexpr int kSinkLdsKeys = 32768;   // scores kept in LDS by the selection (128 KB)
+constexpr int kSelThreads = 1024;
+constexpr int kSelPerThread = 32;    // scores per thread held in registers (L <= 32768)
+constexpr int kSelCand = 1024;       // candidates ranked exactly in LDS
 
-__global__ __launch_bounds__(1024) void sink_select_kernel(const float* __restrict__ scores, int L,
-                                                           int n_sinks, int32_t* __restrict__ sink_idx) {
+// Unique ordered key of score x at position j: the ordered score in the high word and
+// the complement of j in the low word, so the larger score wins and, among equal
+// scores, the lower position.  Valid keys are never 0.
+__device__ __forceinline__ uint64_t sink_key(float x, int j) {
+    return (static_cast<uint64_t>(okey32(x)) << 32) | static_cast<uint32_t>(~j);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), mask, kWave));
+    const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), mask, kWave));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Top-n_sinks positions of each sequence's scores, ascending.  Every thread holds a
+// contiguous run of at most 32 scores in registers.  The n-th largest of the 1024
+// per-thread maxima, T, is at most the n-th largest score (the n largest maxima are n
+// distinct scores), so every selected score is >= T, and at most n threads hold one.
+// The scores >= T (at most 32 n of them, in position order) are ranked exactly in
+// LDS.  More than 32768 scores, or more than 1024 candidates, take the radix select.
+__global__ __launch_bounds__(kSelThreads) void sink_select_kernel(const float* __restrict__ scores, int L,
+                                                                 int n_sinks, int32_t* __restrict__ sink_idx) {
     __shared__ SelectSmem sm;
-    extern __shared__ uint32_t s_keys[];
+    __shared__ uint64_t s_lm[kSelThreads];
+    __shared__ uint64_t s_cand[kSelCand];
+    __shared__ uint64_t s_T;
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
     const float* s = scores + static_cast<int64_t>(b) * L;
     int32_t* out = sink_idx + static_cast<int64_t>(b) * n_sinks;
-    if (L <= kSinkLdsKeys) {
-        for (int j = threadIdx.x; j < L; j += blockDim.x) s_keys[j] = okey32(s[j]);
-        __syncthreads();
-        block_topk_lds<uint32_t>(L, n_sinks, s_keys, [](int j) { return j; }, out, n_sinks, &sm);
-    } else {
+    auto radix = [&]() {
         auto key_of = [&](int j, uint32_t* key) -> bool {
             *key = okey32(s[j]);
             return true;
         };
         block_emit_topk<uint32_t>(L, n_sinks, key_of, [](int j) { return j; }, out, n_sinks, &sm);
+    };
+    if (n_sinks <= 0) return;
+    if (L > kSelThreads * kSelPerThread) {
+        radix();
+        return;
     }
+    const int chunk = (L + kSelThreads - 1) / kSelThreads;
+    const int lo = min(L, tid * chunk);
+    const int cnt = min(L, lo + chunk) - lo;
+    uint64_t key[kSelPerThread];
+    if (chunk == kSelPerThread && cnt == kSelPerThread && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
+        f32x4 v[kSelPerThread / 4];
+#pragma unroll
+        for (int q = 0; q < kSelPerThread / 4; ++q) v[q] = *reinterpret_cast<const f32x4*>(s + lo + 4 * q);
+#pragma unroll
+        for (int u = 0; u < kSelPerThread; ++u) key[u] = sink_key(v[u / 4][u % 4], lo + u);
+    } else {
+        float x[kSelPerThread];
+#pragma unroll
+        for (int u = 0; u < kSelPerThread; ++u) x[u] = s[u < cnt ? lo + u : 0];
+#pragma unroll
+        for (int u = 0; u < kSelPerThread; ++u) key[u] = u < cnt ? sink_key(x[u], lo + u) : 0;
+    }
+    uint64_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kSelPerThread; ++u) m = key[u] > m ? key[u] : m;
+    // bitonic sort of the wave's 64 maxima, descending across the lanes
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint64_t p = shfl_xor_u64(m, stride);
+            const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+            const bool take_max = desc == lower;
+            m = take_max ? (p > m ? p : m) : (p < m ? p : m);
+        }
+    s_lm[tid] = m;
+    if (tid == 0) s_T = 0;
+    __syncthreads();
+    if (m != 0) {
+        // rank among all maxima = entries greater than m, by binary search in each sorted wave
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < kSelThreads / kWave; ++w) {
+            int a0 = 0, a1 = kWave;
+#pragma unroll
+            for (int it = 0; it < 6; ++it) {
+                const int mid = (a0 + a1) >> 1;
+                if (s_lm[w * kWave + mid] > m) a0 = mid + 1;
+                else a1 = mid;
+            }
+            rank += a0;
+        }
+        if (rank == n_sinks - 1) s_T = m;
+    }
+    __syncthreads();
+    // fewer than n_sinks threads with scores leave T = 0: every score is a candidate
+    const uint64_t T = s_T;
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kSelPerThread; ++u) c += (key[u] != 0 && key[u] >= T) ? 1 : 0;
+    int total;
+    int off = block_exclusive_sum(c, sm.tmp, &total);
+    if (total > kSelCand) {
+        radix();
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < kSelPerThread; ++u)
+        if (key[u] != 0 && key[u] >= T) s_cand[off++] = key[u];
+    __syncthreads();
+    int sel = 0;
+    uint64_t mine = 0;
+    if (tid < total) {
+        mine = s_cand[tid];
+        int r = 0;
+        int i = 0;
+        for (; i + 8 <= total; i += 8) {
+            uint64_t y[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) y[u] = s_cand[i + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) r += y[u] > mine ? 1 : 0;
+        }
+        for (; i < total; ++i) r += s_cand[i] > mine ? 1 : 0;
+        sel = r < n_sinks ? 1 : 0;
+    }
+    int nsel;
+    const int pos = block_exclusive_sum(sel, sm.tmp, &nsel);
+    if (sel) out[pos] = static_cast<int32_t>(~static_cast<uint32_t>(mine));
+    for (int i = nsel + tid; i < n_sinks; i += blockDim.x) out[i] = -1;
 }
 
 }  // namespace
@@ -259,8 +372,7 @@ hipError_t launch_sink_identify(fdl_dtype dtype, int d, SinkArgs a, int n_sinks,
     hipLaunchKernelGGL(sink_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds = a.L <= kSinkLdsKeys ? static_cast<size_t>(a.L) * sizeof(uint32_t) : 0;
-    hipLaunchKernelGGL(sink_select_kernel, dim3(a.B), dim3(1024), lds, stream, a.scores, a.L, n_sinks, sink_idx);
+    hipLaunchKernelGGL(sink_select_kernel, dim3(a.B), dim3(kSelThreads), 0, stream, a.scores, a.L, n_sinks, sink_idx);
     return hipGetLastError();
 }
 

@@ -72,12 +72,15 @@ class StepRunner:
         if self.n_sinks:
             F.sink_identify(q, k, self.lse, self.n_sinks, out=self.sinks, **self._rows())
 
-    def sparse_layer(self, l, q, k, v):
-        """Block top-C (block means from the keys) and sparse attention of one layer."""
+    def score_blocks(self, l, q):
+        """Block top-C of one sparse layer from its block means (already in self.kbar[l])."""
+        F.block_score_topc(q, None, self.P, self.bs, self.C, kbar=self.kbar[l], L=self.L, out=self.blocks[l],
+                           **self._rows())
+
+    def attend(self, l, q, k, v):
+        """Sparse attention of one layer over the step's sinks and the layer's selected blocks."""
         sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
         blocks = self.blocks[l][:, : self.C] if self.C else None
-        if self.C:
-            F.block_score_topc(q, k, self.P, self.bs, self.C, out=self.blocks[l], **self._rows())
         F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs, out=self.out[l], **self._rows())
 
     def sparse_step(self, conf, mask, qs, ks, vs, hooks=None):
@@ -115,12 +118,8 @@ class StepRunner:
                         main.wait_event(self.means_done[l])
                     else:
                         run("means", lambda: F.block_means(k, self.P, self.bs, out=self.kbar[l]))
-                    run("blocks", lambda: F.block_score_topc(q, None, self.P, self.bs, self.C, kbar=self.kbar[l],
-                                                            L=self.L, out=self.blocks[l], **self._rows()))
-                sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
-                blocks = self.blocks[l][:, : self.C] if self.C else None
-                run("sparse", lambda: F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs,
-                                                        out=self.out[l], **self._rows()))
+                    run("blocks", lambda: self.score_blocks(l, q))
+                run("sparse", lambda: self.attend(l, q, k, v))
         if overlap:
             main.wait_stream(self.side)
 
