@@ -186,9 +186,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
                 const int64_t idx = base + s * step;
                 m[s] = a.part_ml[2 * idx];
                 l[s] = a.part_ml[2 * idx + 1];
-                const float* po = a.part_o + idx * D + kMergeEpt * sub;
-                x[s][0] = *reinterpret_cast<const f32x4*>(po);
-                x[s][1] = *reinterpret_cast<const f32x4*>(po + 4);
+                if (a.dyn) {
+                    // the persistent bf16 kernel stores its partial rows in bf16
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const uint16_t*>(a.part_o) + idx * D + kMergeEpt * sub);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        x[s][0][2 * e] = bf16lo(w[e]);
+                        x[s][0][2 * e + 1] = bf16hi(w[e]);
+                        x[s][1][2 * e] = bf16lo(w[2 + e]);
+                        x[s][1][2 * e + 1] = bf16hi(w[2 + e]);
+                    }
+                } else {
+                    const float* po = a.part_o + idx * D + kMergeEpt * sub;
+                    x[s][0] = *reinterpret_cast<const f32x4*>(po);
+                    x[s][1] = *reinterpret_cast<const f32x4*>(po + 4);
+                }
             }
         }
 #pragma unroll

@@ -127,6 +127,23 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         const int nq = a.n_q ? a.n_q[b] : a.nq_max;
         const int rows_valid = a.Gq * nq;
 
+        // ---- Q fragments (B operand of S^T = K Q^T): d = 16c + 8hf .. +7 of the row.  Their
+        // loads go out before the key map is built, so both round trips overlap.
+        const int p = u.qt * kD128Rows + wv * 32 + col;   // 8 waves x 32 rows
+        const bool row_ok = p < rows_valid;
+        bf16x8 qf[NQC];
+        {
+            const int rr = row_ok ? p / a.Gq : 0;
+            const int hh = row_ok ? g * a.Gq + p % a.Gq : g * a.Gq;
+            int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + rr] : rr;
+            phys = max(phys, 0);
+            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh +
+                                   static_cast<int64_t>(phys) * a.qsr;
+#pragma unroll
+            for (int c = 0; c < NQC; ++c)
+                qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf));
+        }
+
         // ---- key set of this sequence: n_keys positions; blocks first, then [P, L),
         // then the sinks no selected block holds
         int n_keys = a.L, n_blk = 0, sink0 = a.L;
@@ -181,8 +198,28 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         const int t_begin = u.split * tps;
         const int t_end = min(n_tiles, t_begin + tps);
 
-        // rows of this lane's 2 key positions of tile t (row 0 past the split or the key set)
-        auto keys2 = [&](int t, int (&key)[2]) __attribute__((always_inline)) {
+        // Rows of this lane's 2 key positions of tile t (row 0 past the split or the key
+        // set), in two halves one element apart: keys_fetch reads what the key map holds
+        // for them (LDS, or the key list in global memory), keys_finish forms the rows.
+        // The fetch is issued a whole element before its use, so no wave waits on it.
+        auto keys_fetch = [&](int t, int (&kr)[6]) __attribute__((always_inline)) {
+            const int q0 = t * 64 + 8 * wv + 2 * g4;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int q = q0 + i;
+                if (MODE == kSparseList) {
+                    kr[3 * i] = (t < t_end && q < n_keys) ? klist[q] : 0;
+                } else if (MODE == kSparseLds) {
+                    // both LDS lookups use in-range indices
+                    const int qb = q < n_blk ? q : 0;
+                    const int c = div_magic(qb, a.bs, a.bs_magic);
+                    kr[3 * i] = s_blk[c];
+                    kr[3 * i + 1] = s_unc[min(max(q - sink0, 0), kMapSinks - 1)];
+                    kr[3 * i + 2] = qb - c * a.bs;
+                }
+            }
+        };
+        auto keys_finish = [&](int t, const int (&kr)[6], int (&key)[2]) __attribute__((always_inline)) {
             const int q0 = t * 64 + 8 * wv + 2 * g4;
             const bool live = t < t_end;
 #pragma unroll
@@ -193,35 +230,20 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 if (MODE == kDense) {
                     k = q;
                 } else if (MODE == kSparseList) {
-                    k = ok ? klist[q] : 0;
+                    k = kr[3 * i];
                 } else {
-                    // branch-free: both LDS lookups use in-range indices
-                    const bool in_blk = q < n_blk;
-                    const int qb = in_blk ? q : 0;
-                    const int c = div_magic(qb, a.bs, a.bs_magic);
-                    const int kb = min(max(s_blk[c] * a.bs + (qb - c * a.bs), 0), a.L - 1);
-                    const int ku = s_unc[min(max(q - sink0, 0), kMapSinks - 1)];
-                    k = in_blk ? kb : (q < sink0 ? a.P + (q - n_blk) : ku);
+                    const int kb = min(max(kr[3 * i] * a.bs + kr[3 * i + 2], 0), a.L - 1);
+                    k = q < n_blk ? kb : (q < sink0 ? a.P + (q - n_blk) : kr[3 * i + 1]);
                 }
                 key[i] = ok ? k : 0;
             }
         };
+        auto keys2 = [&](int t, int (&key)[2]) __attribute__((always_inline)) {
+            int kr[6] = {0, 0, 0, 0, 0, 0};
+            keys_fetch(t, kr);
+            keys_finish(t, kr, key);
+        };
 
-        // ---- Q fragments (B operand of S^T = K Q^T): d = 16c + 8hf .. +7 of the row
-        const int p = u.qt * kD128Rows + wv * 32 + col;   // 8 waves x 32 rows
-        const bool row_ok = p < rows_valid;
-        bf16x8 qf[NQC];
-        {
-            const int rr = row_ok ? p / a.Gq : 0;
-            const int hh = row_ok ? g * a.Gq + p % a.Gq : g * a.Gq;
-            int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + rr] : rr;
-            phys = max(phys, 0);
-            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh +
-                                   static_cast<int64_t>(phys) * a.qsr;
-#pragma unroll
-            for (int c = 0; c < NQC; ++c)
-                qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf));
-        }
         const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + g * a.ksh;
         const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.vsb + g * a.vsh;
         const int ksr = static_cast<int>(a.ksr), vsr = static_cast<int>(a.vsr);
@@ -315,6 +337,8 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             keys2(t_begin + 1, kn);
             issue_k(kn, s_k1);
             issue_v(kn, s_v1);
+            int kr[6] = {0, 0, 0, 0, 0, 0};   // map lookups of the next tile to load
+            keys_fetch(t_begin + 2, kr);
             __builtin_amdgcn_s_waitcnt(0);
             transpose_v(s_v0, s_t0);
             __syncthreads();   // K(t0), K(t0+1), V(t0+1) and V^T(t0) are complete
@@ -327,13 +351,17 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
 
             auto elem_v = [&](int t, uint8_t* kdma, uint8_t* vdma, const uint8_t* vnext, uint8_t* tnext)
                 __attribute__((always_inline)) {
-                // this wave's rows of V(t+1) (landed by the end of its previous M element) are
-                // read first, so the LDS round trip hides behind the softmax
-                u32x4 ra, rb;
-                transpose_load(vnext, ra, rb);
-                keys2(t + 2, kn);
+                // rows of tile t+2 from the lookups fetched one element ago; the lookups of
+                // tile t+3 go out before the loads of tile t+2, so those stay the newest
+                // memory operations (barrier_keep<4> leaves exactly them in flight).  This
+                // wave's rows of V(t+1) (landed by the end of its previous M element) are
+                // read early, so the LDS round trip hides behind the softmax.
+                keys_finish(t + 2, kr, kn);
+                keys_fetch(t + 3, kr);
                 issue_k(kn, kdma);
                 issue_v(kn, vdma);
+                u32x4 ra, rb;
+                transpose_load(vnext, ra, rb);
                 const int valid_here = n_keys - t * 64;
                 if (valid_here < 64) {
 #pragma unroll
@@ -437,15 +465,19 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 write_zero_row<uint16_t>(a, b, h, r, 128);
             }
         } else if (row_ok) {
+            // unnormalised partial row in bf16 (half the bytes of fp32; one more rounding of
+            // the output at most), running max and sum in fp32
             const int64_t idx = d128_part_index(a, nqt_max, n_splits, b, g, u.split, p);
-            float* po = a.part_o + idx * 128;
+            uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + idx * 128;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
                     const int d0 = db * 32 + 8 * qd + 4 * hf;
-                    f32x4 w = {acc[db][4 * qd + 0], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
-                    *reinterpret_cast<f32x4*>(po + d0) = w;
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[db][4 * qd + 0], acc[db][4 * qd + 1]);
+                    w[1] = pack_bf16x2(acc[db][4 * qd + 2], acc[db][4 * qd + 3]);
+                    *reinterpret_cast<u32x2*>(po + d0) = w;
                 }
             if (hf == 0) {
                 a.part_ml[idx * 2 + 0] = m_run;
