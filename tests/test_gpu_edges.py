@@ -212,6 +212,30 @@ def test_sinks_and_blocks_small(L):
             assert np.all(blocks[b, min(C, nb):C].cpu().numpy() == -1)
 
 
+@pytest.mark.parametrize("L,n_sinks", [(2000, 5), (32768, 16), (32768, 300), (33000, 7)])
+def test_uniform_scores_pick_the_lowest_indices(L, n_sinks):
+    """Zero queries give every key the same attention mass and every block the same
+    relevance (exact ties): both selections must return the lowest positions.  The cases
+    take the per-thread-maximum sink select (L <= 32768), its radix fallback when too
+    many scores tie at the threshold (300 sinks), and the radix select (L > 32768)."""
+    B, Hq, Hkv, d = 1, 4, 2, 64
+    P, bs, C = L - 48, 64, 6
+    _, k, _ = rand_qkv(11, B, Hq, Hkv, L, d, torch.bfloat16)
+    q = torch.zeros((B, Hq, 8, d), dtype=torch.bfloat16, device=DEV)
+    rows = torch.tensor([[0, 1, 2, 3, 4, 5, 6, 7]], dtype=torch.int32, device=DEV)
+    n_rows = torch.tensor([8], dtype=torch.int32, device=DEV)
+    # lse of zero queries: log(L) for every row
+    lse = torch.full((B, Hq, 8), math.log(L), dtype=torch.float32, device=DEV)
+    sinks, scores = F().sink_identify(q, k, lse, n_sinks, q_idx=rows, n_q=n_rows, nq_max=8, want_scores=True)
+    blocks, R, _ = F().block_score_topc(q, k, P, bs, C, q_idx=rows, n_q=n_rows, nq_max=8, want_R=True)
+    torch.cuda.synchronize()
+    sc = scores[0].cpu().numpy()
+    assert np.all(sc == sc[0])
+    assert list(sinks[0].cpu().numpy()) == list(range(n_sinks))
+    assert np.all(R[0].cpu().numpy() == 0.0)
+    assert list(blocks[0].cpu().numpy()) == list(range(C))
+
+
 # ------------------------------------------------------------------ determinism and graphs
 
 def _small_step(runner, conf, mask, qs, ks, vs):
