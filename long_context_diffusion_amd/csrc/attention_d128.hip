@@ -202,8 +202,27 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         // set), in two halves one element apart: keys_fetch reads what the key map holds
         // for them (LDS, or the key list in global memory), keys_finish forms the rows.
         // The fetch is issued a whole element before its use, so no wave waits on it.
-        auto keys_fetch = [&](int t, int (&kr)[6]) __attribute__((always_inline)) {
+        // A tile that lies inside one selected block (block sizes that are multiples of
+        // 64) or inside [P, L) maps position q to base + q: one broadcast lookup (or
+        // none) for the whole tile; only tiles that straddle a boundary map key by key.
+        // kr[6] is that base, or kNoBase.
+        constexpr int kNoBase = -0x40000000;
+        const bool bs64 = a.bs % 64 == 0;
+        auto keys_fetch = [&](int t, int (&kr)[7]) __attribute__((always_inline)) {
             const int q0 = t * 64 + 8 * wv + 2 * g4;
+            kr[6] = kNoBase;
+            if (MODE == kSparseLds) {
+                const int t0q = t * 64;
+                if (bs64 && t0q + 64 <= n_blk) {
+                    const int c = div_magic(t0q, a.bs, a.bs_magic);
+                    kr[6] = s_blk[c] * a.bs - c * a.bs;
+                    return;
+                }
+                if (t0q >= n_blk && t0q + 64 <= sink0) {
+                    kr[6] = a.P - n_blk;
+                    return;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int q = q0 + i;
@@ -219,9 +238,10 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 }
             }
         };
-        auto keys_finish = [&](int t, const int (&kr)[6], int (&key)[2]) __attribute__((always_inline)) {
+        auto keys_finish = [&](int t, const int (&kr)[7], int (&key)[2]) __attribute__((always_inline)) {
             const int q0 = t * 64 + 8 * wv + 2 * g4;
             const bool live = t < t_end;
+            const bool whole = MODE == kSparseLds && kr[6] != kNoBase;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int q = q0 + i;
@@ -231,6 +251,8 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                     k = q;
                 } else if (MODE == kSparseList) {
                     k = kr[3 * i];
+                } else if (whole) {
+                    k = kr[6] + q;
                 } else {
                     const int kb = min(max(kr[3 * i] * a.bs + kr[3 * i + 2], 0), a.L - 1);
                     k = q < n_blk ? kb : (q < sink0 ? a.P + (q - n_blk) : kr[3 * i + 1]);
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             }
         };
         auto keys2 = [&](int t, int (&key)[2]) __attribute__((always_inline)) {
-            int kr[6] = {0, 0, 0, 0, 0, 0};
+            int kr[7] = {0, 0, 0, 0, 0, 0, 0};
             keys_fetch(t, kr);
             keys_finish(t, kr, key);
         };
@@ -337,7 +359,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             keys2(t_begin + 1, kn);
             issue_k(kn, s_k1);
             issue_v(kn, s_v1);
-            int kr[6] = {0, 0, 0, 0, 0, 0};   // map lookups of the next tile to load
+            int kr[7] = {0, 0, 0, 0, 0, 0, 0};   // map lookups of the next tile to load
             keys_fetch(t_begin + 2, kr);
             __builtin_amdgcn_s_waitcnt(0);
             transpose_v(s_v0, s_t0);
