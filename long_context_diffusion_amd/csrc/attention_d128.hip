@@ -431,18 +431,34 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 barrier_keep<4>();   // the loads of tile t+2 may stay in flight
             };
             auto elem_m = [&](const uint8_t* tread, const uint8_t* kread) __attribute__((always_inline)) {
-                // O^T += V^T P^T, the 4 fragments of a key chunk read before its MFMAs
+                // O^T += V^T P^T, then S(t+1) = K(t+1) Q^T, as one stream of 32 MFMAs whose
+                // LDS fragments (16 of V^T, then 16 of K) are read through a rolling window of
+                // 4: each read is issued 4 MFMAs ahead of the one it feeds
+                auto frag = [&](int j) __attribute__((always_inline)) {
+                    if (j < 16) {   // V^T fragment: key chunk j / 4, head-dim block j % 4
+                        return *reinterpret_cast<const bf16x8*>(tread + (j & 3) * 4096 + (tofs ^ (32 * (j >> 2))));
+                    }
+                    const int c = j - 16;   // K fragment: key block c / 8, head-dim chunk c % 8
+                    return *reinterpret_cast<const bf16x8*>(kread + (c >> 3) * 32 * kRowB + (kofs ^ (32 * (c & 7))));
+                };
+                bf16x8 w[4];
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    const int o = tofs ^ (32 * kc);
-                    bf16x8 vf[NDB];
+                for (int j = 0; j < 4; ++j) w[j] = frag(j);
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) vf[db] = *reinterpret_cast<const bf16x8*>(tread + db * 4096 + o);
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf[kc], acc[db], 0, 0, 0);
+                    for (int i = 0; i < 16; ++i) st[kb][i] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const bf16x8 cur = w[j & 3];
+                    if (j + 4 < 32) w[j & 3] = frag(j + 4);
+                    if (j < 16) {
+                        acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[j >> 2], acc[j & 3], 0, 0, 0);
+                    } else {
+                        const int c = j - 16;
+                        st[c >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[c & 7], st[c >> 3], 0, 0, 0);
+                    }
                 }
-                qk(kread, st);
                 barrier_keep<0>();   // this wave's loads of the next tile have landed
             };
             // tile t0 + j: K in s_k[j % 3], V in s_v[j % 3], V^T in s_t[j % 3]
