@@ -141,8 +141,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d,
 }
 
 // Merge of the key-range splits.  Each thread owns 8 elements of one output row
-// (b, h, r); its loads of the running maxima/sums and of the partial outputs are
-// independent, so a row costs one memory round trip.  Valid rows get
+// (b, h, r); it takes the splits four at a time, and the loads of a group's running
+// maxima/sums and partial outputs are independent, so a group costs one memory round
+// trip.  Valid rows get
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s in split order; padding rows
 // (r >= n_q[b]) are written as zero with lse = -inf.
 constexpr int kMergeEpt = 8;
@@ -178,44 +179,57 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
             base = d128_part_index(a, nqt_max, ns, b, g, 0, p);
             step = static_cast<int64_t>(nqt_max) * kD128Rows;
         }
-        float m[kMaxSplits], l[kMaxSplits];
-        f32x4 x[kMaxSplits][2];
+        // splits in groups of 4: the 4 partials of a group are loaded together, then folded
+        // into the running (max, sum, row) with one rescale per group (few registers, so
+        // many rows are in flight)
+        constexpr int kGroup = 4;
+        for (int s0 = 0; s0 < ns; s0 += kGroup) {
+            float m[kGroup], l[kGroup];
+            f32x4 x[kGroup][2];
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-            if (s < ns) {
-                const int64_t idx = base + s * step;
-                m[s] = a.part_ml[2 * idx];
-                l[s] = a.part_ml[2 * idx + 1];
-                if (a.dyn) {
-                    // the persistent bf16 kernel stores its partial rows in bf16
-                    const u32x4 w = *reinterpret_cast<const u32x4*>(
-                        reinterpret_cast<const uint16_t*>(a.part_o) + idx * D + kMergeEpt * sub);
+            for (int j = 0; j < kGroup; ++j) {
+                m[j] = kNegBig;
+                l[j] = 0.0f;
+                x[j][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                x[j][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (s0 + j < ns) {
+                    const int64_t idx = base + (s0 + j) * step;
+                    m[j] = a.part_ml[2 * idx];
+                    l[j] = a.part_ml[2 * idx + 1];
+                    if (a.dyn) {
+                        // the persistent bf16 kernel stores its partial rows in bf16
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(
+                            reinterpret_cast<const uint16_t*>(a.part_o) + idx * D + kMergeEpt * sub);
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        x[s][0][2 * e] = bf16lo(w[e]);
-                        x[s][0][2 * e + 1] = bf16hi(w[e]);
-                        x[s][1][2 * e] = bf16lo(w[2 + e]);
-                        x[s][1][2 * e + 1] = bf16hi(w[2 + e]);
+                        for (int e = 0; e < 2; ++e) {
+                            x[j][0][2 * e] = bf16lo(w[e]);
+                            x[j][0][2 * e + 1] = bf16hi(w[e]);
+                            x[j][1][2 * e] = bf16lo(w[2 + e]);
+                            x[j][1][2 * e + 1] = bf16hi(w[2 + e]);
+                        }
+                    } else {
+                        const float* po = a.part_o + idx * D + kMergeEpt * sub;
+                        x[j][0] = *reinterpret_cast<const f32x4*>(po);
+                        x[j][1] = *reinterpret_cast<const f32x4*>(po + 4);
                     }
-                } else {
-                    const float* po = a.part_o + idx * D + kMergeEpt * sub;
-                    x[s][0] = *reinterpret_cast<const f32x4*>(po);
-                    x[s][1] = *reinterpret_cast<const f32x4*>(po + 4);
                 }
             }
-        }
+            float Mg = M;
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s)
-            if (s < ns) M = fmaxf(M, m[s]);
+            for (int j = 0; j < kGroup; ++j) Mg = fmaxf(Mg, m[j]);
+            const float r0 = exp2f(M - Mg);
+            Lsum *= r0;
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-            if (s < ns) {
-                const float w = exp2f(m[s] - M);
-                Lsum = fmaf(l[s], w, Lsum);
+            for (int e = 0; e < kMergeEpt; ++e) o[e] *= r0;
+            M = Mg;
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const float w = exp2f(m[j] - M);
+                Lsum = fmaf(l[j], w, Lsum);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    o[e] = fmaf(x[s][0][e], w, o[e]);
-                    o[4 + e] = fmaf(x[s][1][e], w, o[4 + e]);
+                    o[e] = fmaf(x[j][0][e], w, o[e]);
+                    o[4 + e] = fmaf(x[j][1][e], w, o[4 + e]);
                 }
             }
         }
