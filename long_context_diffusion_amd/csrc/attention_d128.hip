@@ -478,46 +478,66 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             __builtin_amdgcn_s_waitcnt(0);   // drain the loads past the split before LDS is reused
         }
 
-        // ---- epilogue: normalised rows (one split) or unnormalised partials
-        const int r = p / a.Gq;
-        const int h = g * a.Gq + p % a.Gq;
+        // ---- epilogue: normalised rows (one split) or unnormalised partials, in bf16.
+        // Each wave stages its 32 rows in LDS (row i at 256 i, 16-byte chunk c at slot
+        // c ^ (i & 15): conflict-free both ways), then stores whole rows, 4 rows (1 KB)
+        // per instruction.  Stored straight from the accumulator layout, every
+        // instruction would write 16-byte pieces of 32 different rows, which drains
+        // several times slower.  The loop ended on a barrier that every wave reached
+        // with its loads landed, so no tile buffer is in use any more.
         const float l_tot = l_run + xhalf(l_run);
-        if (n_splits == 1) {
-            if (row_ok) {
-                uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + h * a.osh + static_cast<int64_t>(r) * a.osr;
-                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const int d0 = db * 32 + 8 * qd + 4 * hf;
-                        u32x2 w;
-                        w[0] = pack_bf16x2(acc[db][4 * qd + 0] * inv, acc[db][4 * qd + 1] * inv);
-                        w[1] = pack_bf16x2(acc[db][4 * qd + 2] * inv, acc[db][4 * qd + 3] * inv);
-                        *reinterpret_cast<u32x2*>(orow + d0) = w;
-                    }
-                if (a.lse && hf == 0)
-                    a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] =
-                        l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-            } else if (hf == 0 && p < rows_all) {
-                write_zero_row<uint16_t>(a, b, h, r, 128);
-            }
-        } else if (row_ok) {
-            // unnormalised partial row in bf16 (half the bytes of fp32; one more rounding of
-            // the output at most), running max and sum in fp32
-            const int64_t idx = d128_part_index(a, nqt_max, n_splits, b, g, u.split, p);
-            uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + idx * 128;
+        {
+            uint8_t* stage = (wv < 2 ? s_t0 : wv < 4 ? s_t1 : wv < 6 ? s_t2 : s_v0) + (wv & 1) * 8192;
+            const float sc = n_splits > 1 ? 1.0f : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+            // The lane id goes through an empty asm, so the per-lane offsets below are formed
+            // here rather than hoisted above the tile loop (where they would stay live and spill).
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            // chunk c of row i at 256 i + 16 (c ^ (i & 15)) = (256 i + 16 (i & 15)) ^ 16 c
+            const int wbase = (el & 31) * 256 + 16 * (el & 15) + 8 * (el >> 5);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd) {
-                    const int d0 = db * 32 + 8 * qd + 4 * hf;
+                    // d = 32 db + 8 qd + 4 hf .. +3: half of 16-byte chunk 4 db + qd
                     u32x2 w;
-                    w[0] = pack_bf16x2(acc[db][4 * qd + 0], acc[db][4 * qd + 1]);
-                    w[1] = pack_bf16x2(acc[db][4 * qd + 2], acc[db][4 * qd + 3]);
-                    *reinterpret_cast<u32x2*>(po + d0) = w;
+                    w[0] = pack_bf16x2(acc[db][4 * qd + 0] * sc, acc[db][4 * qd + 1] * sc);
+                    w[1] = pack_bf16x2(acc[db][4 * qd + 2] * sc, acc[db][4 * qd + 3] * sc);
+                    *reinterpret_cast<u32x2*>(stage + (wbase ^ (16 * (4 * db + qd)))) = w;
                 }
-            if (hf == 0) {
+            const int cc = el & 15;
+            const int row0 = u.qt * kD128Rows + wv * 32;   // logical row of this wave's row 0
+            const int64_t pidx0 = n_splits > 1 ? d128_part_index(a, nqt_max, n_splits, b, g, u.split, row0) : 0;
+            // row i = 4k + lane/16: (i & 15) = 4 (k & 3) + lane/16
+            const int rbase = 256 * (el >> 4) + ((16 * cc) ^ (16 * (el >> 4)));
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = 4 * k + (el >> 4);
+                const int pr = row0 + i;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024 * k + (rbase ^ (64 * (k & 3))));
+                if (n_splits == 1) {
+                    if (pr < rows_all) {
+                        const int rr = pr / a.Gq;
+                        const int hh = g * a.Gq + pr % a.Gq;
+                        uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + hh * a.osh + static_cast<int64_t>(rr) * a.osr;
+                        *reinterpret_cast<u32x4*>(orow + 8 * cc) = pr < rows_valid ? v : u32x4{0u, 0u, 0u, 0u};
+                    }
+                } else if (pr < rows_valid) {
+                    uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (pidx0 + i) * 128;
+                    *reinterpret_cast<u32x4*>(po + 8 * cc) = v;
+                }
+            }
+        }
+        // softmax statistics, one lane per row
+        const int r = p / a.Gq;
+        const int h = g * a.Gq + p % a.Gq;
+        if (hf == 0) {
+            if (n_splits == 1) {
+                if (a.lse && p < rows_all)
+                    a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] =
+                        row_ok && l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+            } else if (row_ok) {
+                const int64_t idx = d128_part_index(a, nqt_max, n_splits, b, g, u.split, p);
                 a.part_ml[idx * 2 + 0] = m_run;
                 a.part_ml[idx * 2 + 1] = l_tot;
             }
