@@ -213,6 +213,14 @@ constexpr int kSelectThreads = 1024;
 constexpr int kSelectLds = 2048;   // blocks ranked in LDS
 constexpr int kSlices = 4;         // threads summing the head parts of one block
 
+// Up to kSelectThreads blocks are ranked by a distinct 64-bit key: the order-preserving
+// image of R_b with its low 11 bits replaced by (2047 - b).  Scores within 2^-41 of each
+// other (relative) therefore count as equal, and the lower block index wins, as it does
+// for exactly equal scores.
+__device__ __forceinline__ uint64_t distinct_key(double r, int blk) {
+    return (okey64(r) & ~uint64_t(0x7ff)) | static_cast<uint64_t>(0x7ff - blk);
+}
+
 // R_b = scale * sum over g of rpart[b][g][blk] (KV heads in order), then the top-C blocks.
 __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const BlockArgs a, int C,
                                                                        int32_t* block_idx, double* R_out) {
@@ -247,7 +255,8 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
 #pragma unroll
             for (int i = 0; i < kSlices; ++i) tot += s_slice[i][lb];
             const double val = tot * static_cast<double>(a.scale);
-            if (a.nb <= kSelectLds) s_key[blk] = okey64(val);
+            if (a.nb <= kSelectThreads) s_key[blk] = distinct_key(val, blk);
+            else if (a.nb <= kSelectLds) s_key[blk] = okey64(val);
             else R[blk] = val;
             if (R_out) R_out[static_cast<int64_t>(b) * a.nb + blk] = val;
         }
@@ -255,8 +264,14 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
     }
     __threadfence_block();
     int32_t* out = block_idx + static_cast<int64_t>(b) * C;
-    if (a.nb <= kSelectLds) {
-        block_topk_lds<uint64_t>(a.nb, C, s_key, [](int j) { return j; }, out, C, &sm);
+    if (a.nb <= kSelectThreads) {
+        block_topk_distinct(a.nb, C, [&](int j) { return s_key[j]; }, [](int j) { return j; }, out, C, &sm);
+    } else if (a.nb <= kSelectLds) {
+        auto key_of = [&](int j, uint64_t* key) -> bool {
+            *key = s_key[j];
+            return true;
+        };
+        block_emit_topk<uint64_t>(a.nb, C, key_of, [](int j) { return j; }, out, C, &sm);
     } else {
         auto key_of = [&](int j, uint64_t* key) -> bool {
             *key = okey64(R[j]);

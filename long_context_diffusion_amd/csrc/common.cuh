@@ -112,7 +112,7 @@ __device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
 // (skewed keys would otherwise pile every atomic onto one or two LDS words).
 constexpr int kMaxWaves = 16;
 struct SelectSmem {
-    int hist[kMaxWaves][256];
+    alignas(16) int hist[kMaxWaves][256];
     int tmp[17];
     int digit;
     int remaining;
@@ -255,48 +255,101 @@ __device__ int block_emit_topk(int n, int k, KeyFn key_of, IdxFn idx_of, int32_t
     return nsel;
 }
 
-// Selection over keys already in LDS (every entry valid).  Up to blockDim.x entries are
-// ranked directly: G = blockDim.x / n (a power of two, at most 64) consecutive threads
-// share entry j, each counts the entries i = part, part + G, ... that beat it (larger
-// key, or equal key and lower index), and a shuffle adds the G counts.  Larger sets use
-// the radix select.
-template <typename U, typename IdxFn>
-__device__ int block_topk_lds(int n, int k, const U* keys, IdxFn idx_of, int32_t* out, int cap,
-                              SelectSmem* sm) {
+// Top-k of n <= blockDim.x entries with distinct 64-bit keys, key_of(j) (read once per
+// entry), so the order is total: rank(j) = #{i : key_i > key_j}, and j is taken when
+// rank(j) < k.  A thread holds 4 consecutive entries in registers and compares them with
+// one slice of the keys (S slices of `span` keys, S a power of two <= 64: one LDS read
+// serves 4 comparisons, each a single 64-bit compare); the S partial counts of a group
+// sit in adjacent lanes and add with shuffles.  The keys are copied into sm->hist with
+// two spare slots after every slice, so the slices start on different LDS banks (slices
+// starting 16 or 32 keys apart would otherwise all read the same two banks).  The taken
+// entries are then written in index order from per-wave ballots.
+template <typename KeyFn, typename IdxFn>
+__device__ int block_topk_distinct(int n, int k, KeyFn key_of, IdxFn idx_of, int32_t* out, int cap,
+                                   SelectSmem* sm) {
     const int nsel = min(max(k, 0), n);
+    constexpr int kPer = 4;
+    const int ngroups = (n + kPer - 1) / kPer;
+    int S = 1;
+    while (S < kWave && 2 * S * ngroups <= static_cast<int>(blockDim.x)) S *= 2;
+    const int span = max((n + S - 1) / S, 1);
+    uint64_t* pk = reinterpret_cast<uint64_t*>(&sm->hist[0][0]);        // <= 1152 keys: 9 KB
+    int* s_rank = &sm->hist[10][0];                                      // <= 1024 ranks
+    uint64_t* s_mask = reinterpret_cast<uint64_t*>(&sm->hist[15][0]);    // one per wave
+    for (int i = threadIdx.x; i < n; i += blockDim.x) pk[i + 2 * (i / span)] = key_of(i);
+    __syncthreads();
+    const int jg = static_cast<int>(threadIdx.x) / S;
+    const int sl = static_cast<int>(threadIdx.x) % S;
+    if (jg < ngroups) {
+        const int j0 = kPer * jg;
+        uint64_t kj[kPer];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int jj = min(j0 + r, n - 1);
+            kj[r] = pk[jj + 2 * (jj / span)];
+        }
+        int cnt[kPer] = {0, 0, 0, 0};
+        const int i0 = min(n, sl * span), i1 = min(n, i0 + span);
+        const uint64_t* ps = pk + 2 * sl;   // key i of this slice at ps[i]
+        constexpr int kBatch = 8;
+        int ib = i0;
+        for (; ib + kBatch <= i1; ib += kBatch) {
+            uint64_t ki[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) ki[u] = ps[ib + u];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+                for (int r = 0; r < kPer; ++r) cnt[r] += ki[u] > kj[r] ? 1 : 0;
+        }
+        for (; ib < i1; ++ib) {
+            const uint64_t ki = ps[ib];
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) cnt[r] += ki > kj[r] ? 1 : 0;
+        }
+        for (int off = 1; off < S; off <<= 1)
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) cnt[r] += __shfl_xor(cnt[r], off, kWave);
+        if (sl == 0) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r)
+                if (j0 + r < n) s_rank[j0 + r] = cnt[r];
+        }
+    }
+    __syncthreads();
+    const int j = static_cast<int>(threadIdx.x);
+    const int lane = j & (kWave - 1), wv = j / kWave;
+    const bool take = j < n && s_rank[j] < nsel;
+    const uint64_t m = __ballot(take);
+    if (lane == 0) s_mask[wv] = m;
+    __syncthreads();
+    if (take) {
+        int pos = __popcll(m & ((uint64_t(1) << lane) - 1));
+        for (int w = 0; w < wv; ++w) pos += __popcll(s_mask[w]);
+        out[pos] = idx_of(j);
+    }
+    for (int i = nsel + j; i < cap; i += blockDim.x) out[i] = -1;
+    __syncthreads();   // the output (LDS or global) is complete and the scratch free
+    return nsel;
+}
+
+// Selection over 32-bit keys already in LDS (every entry valid), the lower index first
+// among equal keys.  Up to blockDim.x entries: ranked by the distinct 64-bit keys
+// (key << 32 | ~index), same order; larger sets use the radix select.
+template <typename IdxFn>
+__device__ int block_topk_lds(int n, int k, const uint32_t* keys, IdxFn idx_of, int32_t* out, int cap,
+                              SelectSmem* sm) {
     if (n > static_cast<int>(blockDim.x)) {
-        auto key_of = [&](int j, U* key) -> bool {
+        auto key_of = [&](int j, uint32_t* key) -> bool {
             *key = keys[j];
             return true;
         };
-        return block_emit_topk<U>(n, k, key_of, idx_of, out, cap, sm);
+        return block_emit_topk<uint32_t>(n, k, key_of, idx_of, out, cap, sm);
     }
-    int G = 1;
-    while (G < kWave && 2 * G * n <= static_cast<int>(blockDim.x)) G *= 2;
-    const int j = static_cast<int>(threadIdx.x) / G;
-    const int part = static_cast<int>(threadIdx.x) % G;
-    int beat = 0;
-    if (j < n) {
-        const U kj = keys[j];
-        constexpr int kBatch = 8;
-        for (int i0 = part; i0 < n; i0 += kBatch * G) {
-            U ki[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) ki[u] = keys[min(i0 + u * G, n - 1)];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int i = i0 + u * G;
-                beat += (i < n && (ki[u] > kj || (ki[u] == kj && i < j))) ? 1 : 0;
-            }
-        }
-    }
-    for (int off = G >> 1; off > 0; off >>= 1) beat += __shfl_xor(beat, off, kWave);
-    const int take = (j < n && part == 0 && beat < nsel) ? 1 : 0;
-    int total;
-    const int pos = block_exclusive_sum(take, sm->tmp, &total);   // thread order is entry order
-    if (take) out[pos] = idx_of(j);
-    for (int i = nsel + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
-    return nsel;
+    auto key_of = [&](int j) {
+        return (static_cast<uint64_t>(keys[j]) << 32) | (0xffffffffu - static_cast<uint32_t>(j));
+    };
+    return block_topk_distinct(n, k, key_of, idx_of, out, cap, sm);
 }
 
 }  // namespace fdl

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kPcgiThreads) void pcgi_select_kernel(
     if (n_masked <= kPcgiCap) {
         // selected into LDS (the windows read it there), then copied out
         const int n_sel = min(max(k, 0), n_masked);
-        nf = block_topk_lds<uint32_t>(n_masked, k, s_key, [&](int j) { return s_pos[j]; }, s_focus, n_sel, &sm);
+        nf = block_topk_lds(n_masked, k, s_key, [&](int j) { return s_pos[j]; }, s_focus, n_sel, &sm);
         __syncthreads();
         for (int i = tid; i < k_cap; i += blockDim.x) focus[i] = i < nf ? s_focus[i] : -1;
         fl = s_focus;
