@@ -173,7 +173,8 @@ fdl_status fdl_block_means(fdl_dtype dtype, int B, int Hkv, int L, int P, int d,
  *   block_idx  [B, C] out, ascending, -1 padded when C > nb
  *   R          [B, nb] fp64 out, or NULL
  *   kbar       [B, Hkv, nb, d] fp32 block means: out (k given) or in (k NULL), or NULL
- * The workspace size depends on nq_max (the query rows are scored in slices).
+ * The workspace holds each KV head's part of R, R, and the block means when k is
+ * given and kbar is NULL; its size does not depend on nq_max.
  */
 size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int P,
                                             int d, int bs, int nq_max);

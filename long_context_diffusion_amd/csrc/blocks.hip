@@ -9,16 +9,15 @@
 // The block means depend on the prompt keys only, so they are a separate pass
 // (block_means) that a caller can run for every layer ahead of the layer that
 // needs them, e.g. on a second stream while earlier layers attend.  Scoring is
-// then three small passes; the two that read the queries and the means are spread
-// over many workgroups (a single CU pulls only about 20 GB/s from memory, so a
-// pass that one workgroup runs is bound by it):
+// then two small passes; the one that reads the queries and the means is spread over
+// many workgroups (a single CU pulls only about 20 GB/s from memory, so a pass that
+// one workgroup runs is bound by it):
 //   block_means        one streaming read of the prompt keys, 16 bytes per lane,
 //                      fp64 sums (exact for bf16/fp32 inputs), one rounding of the
 //                      mean to fp32.
-//   block_qsum         R is linear in the queries: the sum of the query rows of
-//                      every 64-row chunk of one KV head's query heads (fp64).
-//   block_dots         per (KV head, 32 blocks): the chunk sums added in chunk
-//                      order give qsum_g, and qsum_g . kbar_gb is that head's part of R_b.
+//   block_dots         per (KV head g, 4096/d blocks): R is linear in the queries, so the
+//                      workgroup first sums the query rows of g's query heads (fp64),
+//                      qsum_g, and qsum_g . kbar_gb is that head's part of R_b.
 //   block_select       one workgroup per sequence adds the head parts in head order,
 //                      scales by `scale`, and keeps the top-C blocks (lower block
 //                      index first among equal scores), ascending.
@@ -30,8 +29,11 @@ namespace fdl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQsumRows = 64;      // packed query rows per query-sum workgroup
-constexpr int kDotBlocks = 32;     // blocks per dot-product workgroup
+constexpr int kQRows = 1024;       // packed query rows whose indices are staged in LDS at once
+constexpr int kDotThreads = 512;   // threads of a dot-product workgroup
+// blocks per dot-product workgroup: D / 16 lanes per block, 16 mean elements per lane (every
+// workgroup of a KV head sums the same query rows, so fewer, larger workgroups read less)
+__host__ __device__ constexpr int dot_blocks(int d) { return kDotThreads * 16 / d; }
 constexpr int kMeansBlocks = 2;    // blocks per block_means workgroup
 
 template <typename T>
@@ -115,87 +117,105 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
     }
 }
 
-// qpart[b][g][c][e] = sum over the packed rows [64c, 64c + 64) of KV head g of q[..][e] in
-// fp64 (packed row p: query head g*Gq + p%Gq, active row p/Gq); zeros past the rows.
+// rpart[b][g][blk] = qsum_g . kbar[b][g][blk] for the dot_blocks(D) blocks of this workgroup,
+// where qsum_g is the fp64 sum of the packed query rows p < Gq * nq of KV head g (query head
+// g*Gq + p%Gq, active row p/Gq).  Row group rg of the workgroup sums rows rg, rg + RG, ...
+// in order; the RG partial sums then add in row-group order.  The block means go out
+// first, the query-row indices of up to kQRows rows are staged in LDS, and each thread
+// keeps the loads of its next 8 rows in flight while it adds the previous 8 (one round of
+// loads covers 8 RG rows, and the next 8 RG go out before they are added: 512 rows for
+// bf16, d = 128).
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void block_qsum_kernel(const BlockArgs a) {
-    constexpr int EPP = 16 / sizeof(T);     // elements per 16-byte piece
-    constexpr int NP = D / EPP;             // pieces per row
-    constexpr int RG = kThreads / NP;       // row groups
-    constexpr int RPT = kQsumRows / RG;     // rows per thread
-    static_assert(RPT * RG == kQsumRows, "row split");
-    __shared__ double s_q[RG][D];
-    const int tid = threadIdx.x;
-    const int c = blockIdx.x % a.nchunks;
-    const int bg = blockIdx.x / a.nchunks;
-    const int g = bg % a.Hkv, b = bg / a.Hkv;
-    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
-    const int rows = a.Gq * nq;
-    const int piece = tid % NP, rg = tid / NP;
-    u32x4 x[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-        const int p = c * kQsumRows + rg + RG * u;
-        x[u] = u32x4{0u, 0u, 0u, 0u};
-        if (p < rows) {
-            const int r = p / a.Gq, hh = p % a.Gq;
-            const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
-            x[u] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.q) + b * a.qsb + (g * a.Gq + hh) * a.qsh +
-                                                   static_cast<int64_t>(phys) * a.qsr + piece * EPP);
-        }
-    }
-    double acc[EPP];
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-        float v[EPP];
-        unpack16<T>(x[u], v);
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) acc[e] += static_cast<double>(v[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) s_q[rg][piece * EPP + e] = acc[e];
-    __syncthreads();
-    double* out = a.qpart + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nchunks + c) * D;
-    for (int e = tid; e < D; e += kThreads) {
-        double t = 0.0;
-        for (int r = 0; r < RG; ++r) t += s_q[r][e];
-        out[e] = t;
-    }
-}
-
-// rpart[b][g][blk] = qsum_g . kbar[b][g][blk] for the kDotBlocks blocks of this workgroup,
-// qsum_g being the chunk sums added in chunk order.
-template <int D>
-__global__ __launch_bounds__(kThreads) void block_dots_kernel(const BlockArgs a) {
-    constexpr int LPB = kThreads / kDotBlocks;   // lanes per block
+__global__ __launch_bounds__(kDotThreads) void block_dots_kernel(const BlockArgs a) {
+    constexpr int EPP = 16 / sizeof(T);             // elements per 16-byte piece
+    constexpr int NP = D / EPP;                     // pieces per row
+    constexpr int RG = kDotThreads / NP;            // row groups
+    constexpr int kDotBlocks = dot_blocks(D);
+    constexpr int LPB = kDotThreads / kDotBlocks;   // lanes per block
     constexpr int EPL = D / LPB;                 // kbar elements per lane
+    constexpr int kBatch = 8;
     static_assert(EPL % 4 == 0, "16-byte kbar pieces");
+    __shared__ double s_q[RG][D + 2];            // padded rows: row groups start on different banks
     __shared__ double s_qsum[D];
+    __shared__ int s_phys[kQRows];
     const int tid = threadIdx.x;
     const int nbc = (a.nb + kDotBlocks - 1) / kDotBlocks;
     const int bc = blockIdx.x % nbc;
     const int bg = blockIdx.x / nbc;
     const int g = bg % a.Hkv, b = bg / a.Hkv;
-    // this workgroup's block means go out first; qsum_g meanwhile
     const int blk = bc * kDotBlocks + tid / LPB, sub = tid % LPB;
     const float* krow = a.kbar_in + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nb + min(blk, a.nb - 1)) * D + sub * EPL;
     f32x4 kx[EPL / 4];
 #pragma unroll
     for (int i = 0; i < EPL / 4; ++i) kx[i] = *reinterpret_cast<const f32x4*>(krow + 4 * i);
-    const double* qp = a.qpart + (static_cast<int64_t>(b) * a.Hkv + g) * a.nchunks * D;
-    for (int e = tid; e < D; e += kThreads) {
-        double t = 0.0;
-        int c = 0;
-        for (; c + 8 <= a.nchunks; c += 8) {
-            double y[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) y[u] = qp[(c + u) * D + e];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) t += y[u];
+
+    const int piece = tid % NP, rg = tid / NP;
+    const T* qhead = static_cast<const T*>(a.q) + b * a.qsb + static_cast<int64_t>(g) * a.Gq * a.qsh + piece * EPP;
+    // the row indices of a chunk are staged for up to Gq * nq_max rows, so the first chunk's
+    // index loads go out together with the row count instead of after it
+    const int rows_max = a.Gq * a.nq_max;
+    auto stage = [&](int c0) __attribute__((always_inline)) {
+        const int cn = min(kQRows, rows_max - c0);
+        for (int i = tid; i < cn; i += kDotThreads) {
+            const int r = (c0 + i) / a.Gq;
+            s_phys[i] = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
         }
-        for (; c < a.nchunks; ++c) t += qp[c * D + e];
+    };
+    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+    stage(0);
+    __syncthreads();
+    const int rows = min(a.Gq * nq, rows_max);
+    double acc[EPP];
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) acc[e] = 0.0;
+    for (int c0 = 0; c0 < rows; c0 += kQRows) {
+        if (c0 > 0) {
+            __syncthreads();   // the previous chunk's indices are no longer read
+            stage(c0);
+            __syncthreads();
+        }
+        const int cn = min(kQRows, rows - c0);
+        auto row_ptr = [&](int i) {   // row i of the chunk (i < cn)
+            const int hh = (c0 + i) % a.Gq;
+            return qhead + hh * a.qsh + static_cast<int64_t>(s_phys[i]) * a.qsr;
+        };
+        auto load = [&](int i0, u32x4 (&x)[kBatch]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = i0 + RG * u;
+                x[u] = i < cn ? *reinterpret_cast<const u32x4*>(row_ptr(i)) : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        auto add = [&](const u32x4 (&x)[kBatch], int i0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (i0 + RG * u >= cn) break;
+                float v[EPP];
+                unpack16<T>(x[u], v);
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) acc[e] += static_cast<double>(v[e]);
+            }
+        };
+        u32x4 xa[kBatch], xb[kBatch];
+        int i0 = rg;
+        load(i0, xa);
+        while (i0 < cn) {
+            const int i1 = i0 + RG * kBatch;
+            if (i1 < cn) load(i1, xb);
+            add(xa, i0);
+            if (i1 >= cn) break;
+            const int i2 = i1 + RG * kBatch;
+            if (i2 < cn) load(i2, xa);
+            add(xb, i1);
+            i0 = i2;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) s_q[rg][piece * EPP + e] = acc[e];
+    __syncthreads();
+    for (int e = tid; e < D; e += kDotThreads) {
+        double t = 0.0;
+        for (int r = 0; r < RG; ++r) t += s_q[r][e];
         s_qsum[e] = t;
     }
     __syncthreads();
@@ -281,18 +301,13 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
     }
 }
 
-int host_chunks(int Gq, int nq_max) {
-    const int64_t c = (static_cast<int64_t>(Gq) * nq_max + kQsumRows - 1) / kQsumRows;
-    return static_cast<int>(c < 1 ? 1 : c);
-}
-
 }  // namespace
 
 size_t block_workspace_bytes(int B, int Hq, int Hkv, int P, int d, int bs, int nq_max) {
+    (void)Hq;
+    (void)nq_max;
     const int64_t nb = (static_cast<int64_t>(P) + bs - 1) / bs;
-    const int chunks = host_chunks(Hq / Hkv, nq_max);
-    return round_up(static_cast<size_t>(B) * Hkv * chunks * d * sizeof(double), 256) +   // query chunk sums
-           round_up(static_cast<size_t>(B) * Hkv * nb * sizeof(double), 256) +          // per-head R parts
+    return round_up(static_cast<size_t>(B) * Hkv * nb * sizeof(double), 256) +          // per-head R parts
            round_up(static_cast<size_t>(B) * nb * sizeof(double), 256) +                // R
            static_cast<size_t>(B) * Hkv * nb * d * sizeof(float);                       // block means
 }
@@ -309,10 +324,7 @@ hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStr
 
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream) {
-    a.nchunks = host_chunks(a.Gq, a.nq_max);
     uint8_t* w = static_cast<uint8_t*>(ws);
-    a.qpart = reinterpret_cast<double*>(w);
-    w += round_up(static_cast<size_t>(a.B) * a.Hkv * a.nchunks * d * sizeof(double), 256);
     a.rpart = reinterpret_cast<double*>(w);
     w += round_up(static_cast<size_t>(a.B) * a.Hkv * a.nb * sizeof(double), 256);
     a.rfull = reinterpret_cast<double*>(w);
@@ -324,18 +336,13 @@ hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, i
         if (err != hipSuccess) return err;
     }
     a.kbar_in = a.kbar;
-    const dim3 qgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * a.nchunks));
-#define FDL_QSUM(T, DD) hipLaunchKernelGGL((block_qsum_kernel<T, DD>), qgrid, dim3(kThreads), 0, stream, a)
-    if (dtype == FDL_BF16) { if (d == 128) FDL_QSUM(uint16_t, 128); else FDL_QSUM(uint16_t, 64); }
-    else { if (d == 128) FDL_QSUM(float, 128); else FDL_QSUM(float, 64); }
-#undef FDL_QSUM
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int nbc = (a.nb + kDotBlocks - 1) / kDotBlocks;
+    const int nbc = (a.nb + dot_blocks(d) - 1) / dot_blocks(d);
     const dim3 dgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * nbc));
-    if (d == 128) hipLaunchKernelGGL(block_dots_kernel<128>, dgrid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(block_dots_kernel<64>, dgrid, dim3(kThreads), 0, stream, a);
-    err = hipGetLastError();
+#define FDL_DOTS(T, DD) hipLaunchKernelGGL((block_dots_kernel<T, DD>), dgrid, dim3(kDotThreads), 0, stream, a)
+    if (dtype == FDL_BF16) { if (d == 128) FDL_DOTS(uint16_t, 128); else FDL_DOTS(uint16_t, 64); }
+    else { if (d == 128) FDL_DOTS(float, 128); else FDL_DOTS(float, 64); }
+#undef FDL_DOTS
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(kSelectThreads), 0, stream, a, C, block_idx, R_out);
     return hipGetLastError();

@@ -33,10 +33,8 @@ struct BlockArgs {
     float scale;
     float* kbar;            // [B, Hkv, nb, d] block means written by block_means, or NULL
     const float* kbar_in;   // [B, Hkv, nb, d] block means the relevance is scored against
-    double* qpart;          // [B, Hkv, nchunks, d] sums of 64-row query chunks
     double* rpart;          // [B, Hkv, nb] each KV head's part of R
     double* rfull;          // [B, nb]
-    int nchunks;            // query chunks per (sequence, KV head)
 };
 
 hipError_t launch_pcgi_select(const float* conf, const uint8_t* mask, int B, int L, int k, int w,

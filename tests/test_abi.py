@@ -73,15 +73,15 @@ def test_workspace_sizes():
                                                      1024, 16, 64, 128) > 0
     assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024) == \
         (32 * 32768 + 32768) * 4
-    # block scoring: fp64 sums of 64-row query chunks per KV head, each KV head's part of R, R, and
-    # room for the block means when they are computed from the keys
+    # block scoring: each KV head's part of R, R, and room for the block means when they are
+    # computed from the keys; the number of query rows does not change it
     nb = 252
 
     def r256(x):
         return -(-x // 256) * 256
-    for nq_max, chunks in ((1024, 16), (100, 2), (1 << 20, 1 << 14)):
+    for nq_max in (1024, 100, 1 << 20):
         assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32256, 128, 128, nq_max) == \
-            r256(32 * chunks * 128 * 8) + r256(32 * nb * 8) + r256(nb * 8) + 32 * nb * 128 * 4
+            r256(32 * nb * 8) + r256(nb * 8) + 32 * nb * 128 * 4
     # invalid shapes report 0
     assert lib.fdl_dense_attention_workspace_bytes(F.FDL_BF16, 1, 32, 5, 1024, 128, 64) == 0
     assert lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 4, 4, 0, 64, 64, 16) == 0
