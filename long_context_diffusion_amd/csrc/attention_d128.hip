@@ -51,12 +51,12 @@ __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 // V^T tile: 128 rows (d) of 128 bytes.  Slot s (0..63) of row d holds V of LDS row
 // vt_row(s), which swaps bits 2 and 3 of s: the 8 slots of 16-byte chunk 2kc + hf then
 // hold S^T rows 16kc + 8(j/4) + 4hf + j%4, j = 0..7, the order a lane's P fragment
-// has.  Chunk c of row d sits at c ^ vt_swz(d): 16 consecutive rows read at one chunk
-// hit distinct banks, and the rows 8 apart that one transposing store instruction
-// writes spread over 8 chunk positions (a swizzle of bits 1-3 of d alone would put
-// them on 2).
+// has.  Chunk c of row d sits at c ^ vt_swz(d), chosen by measuring the LDS bank-conflict
+// counter over candidate swizzles on gfx950: the fragment reads are conflict-free and the
+// transposing stores (rows 8 apart in one instruction) 2-way; with bits 1-3 of d alone
+// the stores are 8-way.
 __device__ __forceinline__ int vt_row(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 7; }
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 __device__ __forceinline__ int vt_off(int d, int s) { return d * 128 + 16 * ((s >> 3) ^ vt_swz(d)) + 2 * (s & 7); }
 
 // key position (within the tile) held by LDS row r: rows 8w + 4i + g hold 8w + 2g + i
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         };
 
         // V^T operand of (kc, db): row d = 32db + col, chunk 2kc + hf, at
-        // 4096 db + (tofs ^ 64 (db & 1) ^ 32 kc), since vt_swz(32db + col) = vt_swz(col) ^ 4 (db & 1)
+        // 4096 db + (tofs ^ 32 (kc ^ db)), since vt_swz(32db + col) = vt_swz(col) ^ 2db
         const int tofs = col * 128 + ((16 * hf) ^ (16 * vt_swz(col)));
 
         // ---- V tile -> V^T: lane (k, c8) moves rows 2k, 2k+1 x d = 8c8 .. 8c8+7
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 // 4: each read is issued 4 MFMAs ahead of the one it feeds
                 auto frag = [&](int j) __attribute__((always_inline)) {
                     if (j < 16) {   // V^T fragment: key chunk j / 4, head-dim block j % 4
-                        return *reinterpret_cast<const bf16x8*>(tread + (j & 3) * 4096 + (tofs ^ (64 * (j & 1)) ^ (32 * (j >> 2))));
+                        return *reinterpret_cast<const bf16x8*>(tread + (j & 3) * 4096 + (tofs ^ (32 * ((j >> 2) ^ (j & 3)))));
                     }
                     const int c = j - 16;   // K fragment: key block c / 8, head-dim chunk c % 8
                     return *reinterpret_cast<const bf16x8*>(kread + (c >> 3) * 32 * kRowB + (kofs ^ (32 * (c & 7))));
