@@ -61,7 +61,9 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
     constexpr int NP = D / EPP;             // pieces per key row
     constexpr int RG = kThreads / NP;       // rows read together by the workgroup
     constexpr int kBatch = 8;               // loads per thread and block in flight
-    __shared__ double s_sum[kMeansBlocks][RG][D];
+    constexpr int kWaves = kThreads / kWave;
+    // one row of sums per wave, element-major: s_sum[c][w][e][piece]
+    __shared__ double s_sum[kMeansBlocks][kWaves][EPP][NP];
     const int tid = threadIdx.x;
     const int chunks = (a.nb + kMeansBlocks - 1) / kMeansBlocks;
     const int chunk = blockIdx.x % chunks;
@@ -103,24 +105,37 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
                 for (int e = 0; e < EPP; ++e) acc[c][e] += static_cast<double>(v[e]);
             }
     }
+    // the row groups of a wave (lanes NP apart) fold with shuffles; the fp64 sums of bf16 or
+    // fp32 keys are exact, so the order of the additions does not change them
 #pragma unroll
     for (int c = 0; c < kMeansBlocks; ++c)
 #pragma unroll
-        for (int e = 0; e < EPP; ++e) s_sum[c][rg][piece * EPP + e] = acc[c][e];
+        for (int e = 0; e < EPP; ++e)
+#pragma unroll
+            for (int off = NP; off < kWave; off <<= 1) acc[c][e] += __shfl_xor(acc[c][e], off, kWave);
+    const int wv = tid / kWave;
+    if ((tid % kWave) < NP) {
+#pragma unroll
+        for (int c = 0; c < kMeansBlocks; ++c)
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) s_sum[c][wv][e][piece] = acc[c][e];
+    }
     __syncthreads();
     for (int i = tid; i < kMeansBlocks * D; i += kThreads) {
-        const int c = i / D, e = i % D;
+        const int c = i / D, ep = i % D;   // ep = e * NP + piece: element piece * EPP + e
         if (blk0 + c >= a.nb) continue;
+        const int e = ep / NP, pc = ep % NP;
         double s = 0.0;
-        for (int r = 0; r < RG; ++r) s += s_sum[c][r][e];
-        out[static_cast<int64_t>(blk0 + c) * D + e] = static_cast<float>(s / static_cast<double>(hi[c] - lo[c]));
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += s_sum[c][w][e][pc];
+        out[static_cast<int64_t>(blk0 + c) * D + pc * EPP + e] = static_cast<float>(s / static_cast<double>(hi[c] - lo[c]));
     }
 }
 
 // rpart[b][g][blk] = qsum_g . kbar[b][g][blk] for the dot_blocks(D) blocks of this workgroup,
 // where qsum_g is the fp64 sum of the packed query rows p < Gq * nq of KV head g (query head
 // g*Gq + p%Gq, active row p/Gq).  Row group rg of the workgroup sums rows rg, rg + RG, ...
-// in order; the RG partial sums then add in row-group order.  The block means go out
+// in order; the row groups of a wave then fold with shuffles and the waves add in order.  The block means go out
 // first, the query-row indices of up to kQRows rows are staged in LDS, and each thread
 // keeps the loads of its next 8 rows in flight while it adds the previous 8 (one round of
 // loads covers 8 RG rows, and the next 8 RG go out before they are added: 512 rows for
@@ -135,7 +150,8 @@ __global__ __launch_bounds__(kDotThreads) void block_dots_kernel(const BlockArgs
     constexpr int EPL = D / LPB;                 // kbar elements per lane
     constexpr int kBatch = 8;
     static_assert(EPL % 4 == 0, "16-byte kbar pieces");
-    __shared__ double s_q[RG][D + 2];            // padded rows: row groups start on different banks
+    constexpr int kWaves = kDotThreads / kWave;
+    __shared__ double s_q[kWaves][EPP][NP];      // one row of sums per wave, element-major
     __shared__ double s_qsum[D];
     __shared__ int s_phys[kQRows];
     const int tid = threadIdx.x;
@@ -210,13 +226,22 @@ __global__ __launch_bounds__(kDotThreads) void block_dots_kernel(const BlockArgs
             i0 = i2;
         }
     }
+    // the row groups of a wave (lanes NP apart) fold with shuffles, then the waves in order
 #pragma unroll
-    for (int e = 0; e < EPP; ++e) s_q[rg][piece * EPP + e] = acc[e];
+    for (int e = 0; e < EPP; ++e)
+#pragma unroll
+        for (int off = NP; off < kWave; off <<= 1) acc[e] += __shfl_xor(acc[e], off, kWave);
+    if ((tid % kWave) < NP) {
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) s_q[tid / kWave][e][piece] = acc[e];
+    }
     __syncthreads();
-    for (int e = tid; e < D; e += kDotThreads) {
+    for (int ep = tid; ep < D; ep += kDotThreads) {   // ep = e * NP + piece: element piece * EPP + e
+        const int e = ep / NP, pc = ep % NP;
         double t = 0.0;
-        for (int r = 0; r < RG; ++r) t += s_q[r][e];
-        s_qsum[e] = t;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t += s_q[w][e][pc];
+        s_qsum[pc * EPP + e] = t;
     }
     __syncthreads();
     double s = 0.0;
