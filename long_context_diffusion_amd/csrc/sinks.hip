@@ -28,6 +28,7 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kSinkKeysPerWg = 256;  // 4 waves x 64 keys
+constexpr int kSinkRowsStaged = 1024;  // packed query rows resolved into LDS at once
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs a) {
@@ -36,7 +37,9 @@ __global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs
     constexpr int QP = D * 2 + 16;         // Q row pitch in LDS (bytes)
     constexpr int QPT = 32 * NCH / 256;    // 16-byte Q pieces staged per thread per block
     __shared__ __attribute__((aligned(16))) uint8_t s_q[2][32 * QP];
-    __shared__ float s_lse[2][32];
+    // per packed row of the current chunk: element offset of its Q row, its lse (log2)
+    __shared__ int64_t s_qoff[kSinkRowsStaged];
+    __shared__ float s_lse2[kSinkRowsStaged + 32];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, col = lane & 31;
     const int kt = blockIdx.x % a.key_tiles;
@@ -44,7 +47,6 @@ __global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int nq = a.n_q ? a.n_q[b] : a.nq_max;
     const int rows = a.Gq * nq;
-    const int n_blocks = (rows + 31) / 32;
     const int key0 = kt * kSinkKeysPerWg + wv * 64;
 
     // K fragments (B operand): key = key0 + 32*kg + col, d = 16c + 8hf .. +7
@@ -59,63 +61,48 @@ __global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs
                 bf16x8, *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * a.ksr + 16 * c + 8 * hf));
     }
 
-    // Staging of Q block i (packed rows 32i .. 32i+31): thread stages pieces (rr, ch).
-    // Physical row offsets are resolved one block ahead of the loads.
-    auto row_offset = [&](int i, int x) -> int64_t {   // element offset of the row of piece x
-        const int item = tid + 256 * x;
-        const int p = min(32 * i + item / NCH, max(rows - 1, 0));
-        const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
-        const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
-        return b * a.qsb + h * a.qsh + static_cast<int64_t>(phys) * a.qsr + 8 * ((tid + 256 * x) % NCH);
-    };
-    auto lse_of = [&](int i) -> float {   // lse (log2 units) of row 32i + tid % 32, +inf past the end
-        const int p = 32 * i + (tid & 31);
-        const int pc = min(p, rows - 1);
-        const int h = g * a.Gq + pc % a.Gq, r = pc / a.Gq;
-        const float v = a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] * kLog2e;
-        return p < rows ? v : INFINITY;
-    };
+    // The packed rows are resolved once per chunk of kSinkRowsStaged rows (query head,
+    // physical row through q_idx, lse), so a 32-row block costs each thread two table
+    // reads instead of divisions by Gq and dependent loads.  Q block i of the chunk (rows
+    // 32i .. 32i+31) is staged through registers into one of two LDS buffers while the
+    // previous block is computed.
     const uint16_t* qb = static_cast<const uint16_t*>(a.q);
-    u32x4 qreg[QPT];
-    int64_t off_next[QPT];
-    float lse_next = INFINITY;
-    auto load_block = [&](int64_t* off) {
-#pragma unroll
-        for (int x = 0; x < QPT; ++x) qreg[x] = *reinterpret_cast<const u32x4*>(qb + off[x]);
-    };
-    auto store_block = [&](int buf) {
-#pragma unroll
-        for (int x = 0; x < QPT; ++x) {
-            const int item = tid + 256 * x;
-            *reinterpret_cast<u32x4*>(&s_q[buf][(item / NCH) * QP + 16 * (item % NCH)]) = qreg[x];
-        }
-        if (tid < 32) s_lse[buf][tid] = lse_next;
-    };
-
+    const int pr = tid / NCH, pch = tid % NCH;   // piece x of a block: row pr + 256x/NCH, chunk pch
     float acc[2] = {0.0f, 0.0f};
-    if (n_blocks > 0) {
-        int64_t off0[QPT];
-#pragma unroll
-        for (int x = 0; x < QPT; ++x) {
-            off0[x] = row_offset(0, x);
-            off_next[x] = row_offset(1, x);
+    for (int c0 = 0; c0 < rows; c0 += kSinkRowsStaged) {
+        const int cn = min(kSinkRowsStaged, rows - c0);
+        const int nblk = (cn + 31) / 32;
+        __syncthreads();   // the previous chunk's tables and blocks are no longer read
+        for (int i = tid; i < 32 * nblk; i += 256) {
+            const int p = c0 + min(i, cn - 1);
+            const int h = g * a.Gq + p % a.Gq, r = p / a.Gq;
+            const int phys = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
+            if (i < kSinkRowsStaged) s_qoff[i] = b * a.qsb + h * a.qsh + static_cast<int64_t>(phys) * a.qsr;
+            s_lse2[i] = i < cn ? a.lse[(static_cast<int64_t>(b) * a.Hq + h) * a.nq_max + r] * kLog2e : INFINITY;
         }
-        lse_next = lse_of(0);
-        load_block(off0);
+        __syncthreads();
+        u32x4 qreg[QPT];
+        auto load_block = [&](int i) __attribute__((always_inline)) {   // rows clamped to the chunk
+#pragma unroll
+            for (int x = 0; x < QPT; ++x) {
+                const int row = min(32 * i + pr + x * (256 / NCH), cn - 1);
+                qreg[x] = *reinterpret_cast<const u32x4*>(qb + s_qoff[row] + 8 * pch);
+            }
+        };
+        auto store_block = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int x = 0; x < QPT; ++x)
+                *reinterpret_cast<u32x4*>(&s_q[buf][(pr + x * (256 / NCH)) * QP + 16 * pch]) = qreg[x];
+        };
+        load_block(0);
         store_block(0);
         __syncthreads();
-        for (int i = 0; i < n_blocks; ++i) {
+        for (int i = 0; i < nblk; ++i) {
             const int buf = i & 1;
-            // prefetch block i+1 (valid rows are clamped; past the end it is never used)
-            load_block(off_next);
-            const float lse_pref = lse_of(i + 1);
-            int64_t off_after[QPT];
-#pragma unroll
-            for (int x = 0; x < QPT; ++x) off_after[x] = row_offset(i + 2, x);
-
+            if (i + 1 < nblk) load_block(i + 1);
             float lrow[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) lrow[e] = s_lse[buf][8 * (e >> 2) + 4 * hf + (e & 3)];
+            for (int e = 0; e < 16; ++e) lrow[e] = s_lse2[32 * i + 8 * (e >> 2) + 4 * hf + (e & 3)];
             const uint8_t* qrow = &s_q[buf][col * QP + 16 * hf];
 #pragma unroll
             for (int kg = 0; kg < 2; ++kg) {
@@ -130,10 +117,7 @@ __global__ __launch_bounds__(256, 2) void sink_colsum_bf16_kernel(const SinkArgs
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[kg] += fast_exp2(fmaf(sc[e], a.sl2, -lrow[e]));
             }
-            lse_next = lse_pref;
-            store_block(buf ^ 1);
-#pragma unroll
-            for (int x = 0; x < QPT; ++x) off_next[x] = off_after[x];
+            if (i + 1 < nblk) store_block(buf ^ 1);
             __syncthreads();
         }
     }
