@@ -73,6 +73,7 @@ def test_pcgi_hand_fixture():
 
 @pytest.mark.parametrize("L,frac,n_t,rho,w", [
     (64, 0.5, 4, 2.0, 8),          # rank path, heavy ties
+    (1100, 0.9, 40, 2.0, 9),       # ~990 candidates: rank path with many keys per slice
     (3000, 0.9, 16, 2.0, 33),      # 2700 candidates: radix select over LDS keys
     (20000, 0.6, 20, 2.0, 8),      # 12000 candidates: radix select over global keys
     (5000, 0.001, 30, 2.0, 7),     # fewer masked slots than k
@@ -234,6 +235,36 @@ def test_uniform_scores_pick_the_lowest_indices(L, n_sinks):
     assert list(sinks[0].cpu().numpy()) == list(range(n_sinks))
     assert np.all(R[0].cpu().numpy() == 0.0)
     assert list(blocks[0].cpu().numpy()) == list(range(C))
+
+
+@pytest.mark.parametrize("nb", [1024, 1025, 2048, 2049, 3001])
+def test_block_select_size_regimes(nb):
+    """Block top-C at the edges of its three selection regimes: a rank over distinct keys
+    (nb <= 1024), a radix select over LDS keys (nb <= 2048) and over the relevance in global
+    memory (larger nb).  Random queries check the selection against the oracle; zero
+    queries tie every block at R = 0, where the lowest indices must win."""
+    B, Hq, Hkv, d, bs = 2, 4, 2, 64, 8
+    P = nb * bs - 3                           # ragged last block
+    L = P + 40
+    q, k, _ = rand_qkv(nb, B, Hq, Hkv, L, d, torch.bfloat16, sigma=1.0, q_rows=16)
+    rows = torch.tensor([[0, 3, 5, 9, 15], [2, 4, -1, -1, -1]], dtype=torch.int32, device=DEV)
+    n_rows = torch.tensor([5, 2], dtype=torch.int32, device=DEV)
+    qf, kf = f64(q), f64(k)
+    kb = [O.block_means(kf[b], P, bs) for b in range(B)]
+    for C in (1, 37, nb // 3, nb - 1):
+        blocks, R, _ = F().block_score_topc(q, k, P, bs, C, q_idx=rows, n_q=n_rows, nq_max=5, want_R=True)
+        torch.cuda.synchronize()
+        for b in range(B):
+            r = rows[b, :int(n_rows[b])].cpu().numpy()
+            Rr = O.block_relevance(qf[b][:, r], kb[b], 1 / math.sqrt(d))
+            assert_selection(blocks[b].cpu().numpy(), O.top_blocks(Rr, C), Rr, f"nb={nb} C={C} b={b}")
+    zq = torch.zeros_like(q)
+    for C in (1, nb // 2):
+        blocks, R, _ = F().block_score_topc(zq, k, P, bs, C, q_idx=rows, n_q=n_rows, nq_max=5, want_R=True)
+        torch.cuda.synchronize()
+        assert np.all(R.cpu().numpy() == 0.0)
+        for b in range(B):
+            assert list(blocks[b].cpu().numpy()) == list(range(C)), f"ties nb={nb} C={C} b={b}"
 
 
 # ------------------------------------------------------------------ determinism and graphs
