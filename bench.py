@@ -261,30 +261,43 @@ def main():
     if sinks_found != sorted(synth.sink_positions(wl, 0).tolist()):
         print(f"# warning: sinks {sinks_found} differ from the injected positions", file=sys.stderr)
 
-    def launch_timing(reps):
-        """Sparse attention of every sparse layer called back to back on one stream, one event
-        pair around each call.  One untimed call goes first, so the host stays ahead of the
-        GPU and the events time the kernels, not the launches.  Returns microseconds per call.
-        (A spin kernel ahead of the calls would give the host more lead, but the chip clocks
-        down while it spins and the launches after it measured 8-10 % slower.)"""
-        layers = range(wl.l_dense, wl.layers)
+    def eager_launches(reps):
+        """Sparse attention of every sparse layer called back to back on one stream: one
+        untimed call, then `reps` passes (the launches whose counters rocprofv3 reads)."""
         run.attend(wl.l_dense, qs[wl.l_dense], ks[wl.l_dense], vs[wl.l_dense])
-        evs = []
         for _ in range(reps):
-            for l in layers:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
+            for l in range(wl.l_dense, wl.layers):
                 run.attend(l, qs[l], ks[l], vs[l])
-                b.record(stream)
-                evs.append((a, b))
         torch.cuda.synchronize()
-        return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs), len(evs)
+        return reps * (wl.layers - wl.l_dense)
+
+    def launch_timing(reps):
+        """Average duration of one sparse-attention call (key list, attention, split merge):
+        one pass over every sparse layer is captured in a HIP graph and replayed `reps` times
+        back to back on this stream between two HIP events, after one untimed replay.  The
+        replays keep the host out of the timing (one launch per pass), also under a
+        profiler whose per-dispatch host cost can exceed a kernel's duration.  Returns
+        microseconds per call and the number of calls timed."""
+        layers = range(wl.l_dense, wl.layers)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in layers:
+                run.attend(l, qs[l], ks[l], vs[l])
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        n = reps * len(layers)
+        return 1000.0 * a.elapsed_time(b) / n, n
 
     if args.kernel_only:
-        us, n = launch_timing(args.kernel_reps)
-        print(json.dumps({"kernel": "fdl_sparse_attention", "launches": n, "us_per_launch": round(us, 2),
-                          "n_active": int(run.n_active[0]), "kernel_sources_sha256": kernel_sources_sha256()}),
-              flush=True)
+        n = eager_launches(args.kernel_reps)
+        print(json.dumps({"kernel": "fdl_sparse_attention", "launches": n, "n_active": int(run.n_active[0]),
+                          "kernel_sources_sha256": kernel_sources_sha256()}), flush=True)
         return
 
     # stage events: one pair around every entry-point call
