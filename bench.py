@@ -239,9 +239,11 @@ def main():
         ks.append(k)
         vs.append(v)
         qs.append(synth.make_q(wl, l, 0, dev))
+    # V with the keys contiguous, beside V: the attention loads runs of consecutive keys from it
+    vts = [F.transpose_v(v) for v in vs]
     torch.cuda.synchronize()
-    print(f"# inputs resident: {wl.layers} layers, {sum(t.numel() * 2 for t in qs + ks + vs) / 2**30:.1f} GiB "
-          f"in {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
+    print(f"# inputs resident: {wl.layers} layers, {sum(t.numel() * 2 for t in qs + ks + vs + vts) / 2**30:.1f} GiB "
+          f"(Q, K, V, V^T) in {time.time() - t_setup:.1f}s", file=sys.stderr, flush=True)
 
     run = StepRunner(B=wl.B, L=wl.L, P=wl.P, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, dtype=torch.bfloat16,
                      n_t=wl.n_t, rho=wl.rho, w=wl.w, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
@@ -250,7 +252,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(hooks=None):
-        run.sparse_step(conf, mask, qs, ks, vs, hooks=hooks)
+        run.sparse_step(conf, mask, qs, ks, vs, hooks=hooks, vts=vts)
 
     for _ in range(max(args.warmup, 1)):
         step()
@@ -264,10 +266,10 @@ def main():
     def eager_launches(reps):
         """Sparse attention of every sparse layer called back to back on one stream: one
         untimed call, then `reps` passes (the launches whose counters rocprofv3 reads)."""
-        run.attend(wl.l_dense, qs[wl.l_dense], ks[wl.l_dense], vs[wl.l_dense])
+        run.attend(wl.l_dense, qs[wl.l_dense], ks[wl.l_dense], vs[wl.l_dense], vts[wl.l_dense])
         for _ in range(reps):
             for l in range(wl.l_dense, wl.layers):
-                run.attend(l, qs[l], ks[l], vs[l])
+                run.attend(l, qs[l], ks[l], vs[l], vts[l])
         torch.cuda.synchronize()
         return reps * (wl.layers - wl.l_dense)
 
@@ -282,7 +284,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for l in layers:
-                run.attend(l, qs[l], ks[l], vs[l])
+                run.attend(l, qs[l], ks[l], vs[l], vts[l])
         g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -437,11 +439,11 @@ def main():
     if not args.no_refresh:
         # block-entry refresh of one layer: all 32768 rows attend to all keys
         out = torch.empty_like(qs[0])
-        F.dense_attention(qs[0], ks[0], vs[0], out=out, want_lse=False, scale=wl.scale)
+        F.dense_attention(qs[0], ks[0], vs[0], vt=vts[0], out=out, want_lse=False, scale=wl.scale)
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(args.refresh_reps):
-            F.dense_attention(qs[0], ks[0], vs[0], out=out, want_lse=False, scale=wl.scale)
+            F.dense_attention(qs[0], ks[0], vs[0], vt=vts[0], out=out, want_lse=False, scale=wl.scale)
         e1.record(stream)
         torch.cuda.synchronize()
         rms = e0.elapsed_time(e1) / args.refresh_reps

@@ -106,6 +106,15 @@ fdl_status fdl_pcgi_select(const float* conf, const uint8_t* mask, int B, int L,
  * (step (3)), there for the active rows only (q_idx = active_idx, n_q = n_active).
  *   q       [B, Hq, *, d] with strides qs; q_idx [B, nq_max] or NULL; n_q [B] or NULL
  *   k, v    [B, Hkv, L, d] with strides ks, vs
+ *   vt      NULL, or the same values as v laid out [B, Hkv, d, L] (keys contiguous) with
+ *           strides vts = (b, h, d): read only by the bf16 d = 128 path, which then
+ *           loads runs of 64 consecutive keys from it instead of transposing V rows
+ *           on chip (used when L is a multiple of 8; in fdl_sparse_attention also
+ *           bs a multiple of 64 and P a multiple of 8; otherwise ignored).  There the
+ *           pointer must be 16-byte aligned and vts.b, vts.h, vts.r multiples of 8
+ *           (FDL_ERR_ALIGN), with L <= vts.r < 2^24 (FDL_ERR_SHAPE).  The results are
+ *           the same with or without it.  Keeping it current (e.g. for the rows an
+ *           approximate KV cache refreshes) is the caller's part.
  *   o       [B, Hq, nq_max, d] out with strides os, in the input dtype
  *   lse     [B, Hq, nq_max] fp32 out (natural log of the softmax denominator) or NULL
  * Workspace: fdl_dense_attention_workspace_bytes (partial results of the key split).
@@ -116,6 +125,7 @@ fdl_status fdl_dense_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, i
                                const void* q, fdl_strides qs, const int32_t* q_idx,
                                const int32_t* n_q, int nq_max,
                                const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                               const void* vt, fdl_strides vts,
                                float scale, void* o, fdl_strides os, float* lse,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -191,7 +201,7 @@ fdl_status fdl_block_score_topc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
  * selected prompt blocks; this library also adds the generation region [P, L)
  * (without it, keeping every block could not reproduce dense attention).  Each
  * key of I_p is attended once, however many of the three sets hold it.
- *   q, q_idx, n_q, nq_max, k, ks, v, vs, scale, o, os, lse   as in fdl_dense_attention
+ *   q, q_idx, n_q, nq_max, k, ks, v, vs, vt, vts, scale, o, os, lse   as in fdl_dense_attention
  *   sink_idx   [B, n_sinks] ascending, -1 entries ignored (fdl_sink_identify output)
  *   block_idx  [B, C] ascending, -1 entries ignored (fdl_block_score_topc output)
  *   P, bs      prompt length and block size used to select block_idx
@@ -203,6 +213,7 @@ fdl_status fdl_sparse_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
                                 const void* q, fdl_strides qs, const int32_t* q_idx,
                                 const int32_t* n_q, int nq_max,
                                 const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                const void* vt, fdl_strides vts,
                                 const int32_t* sink_idx, int n_sinks,
                                 const int32_t* block_idx, int C, int bs,
                                 float scale, void* o, fdl_strides os, float* lse,

@@ -34,6 +34,15 @@ fdl_status check_tensor(const void* p, fdl_strides s, fdl_dtype dt, int d) {
     return FDL_OK;
 }
 
+// V^T (keys contiguous, rows indexed by d): read only by the bf16 d = 128 kernel, so it
+// is checked (and used) only there.
+fdl_status check_vt(const void* vt, fdl_strides s, fdl_dtype dt, int d, int L) {
+    if (!vt || dt != FDL_BF16 || d != 128) return FDL_OK;
+    if (!aligned16(vt) || s.b % 8 || s.h % 8 || s.r % 8) return FDL_ERR_ALIGN;
+    if (s.r < L || s.r >= (1ll << 24)) return FDL_ERR_SHAPE;
+    return FDL_OK;
+}
+
 fdl_status check_rows(int nq_max, int Gq) {
     if (nq_max < 0) return FDL_ERR_SHAPE;
     if (static_cast<int64_t>(nq_max) * Gq > (1ll << 30)) return FDL_ERR_SHAPE;
@@ -57,13 +66,15 @@ constexpr float kLog2eF = 1.44269504088896340736f;
 
 AttnArgs attn_args(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, const void* q, fdl_strides qs,
                    const int32_t* q_idx, const int32_t* n_q, int nq_max, const void* k, fdl_strides ks,
-                   const void* v, fdl_strides vs, float scale, int d, void* o, fdl_strides os, float* lse,
-                   void* ws) {
+                   const void* v, fdl_strides vs, const void* vt, fdl_strides vts, float scale, int d,
+                   void* o, fdl_strides os, float* lse, void* ws) {
     AttnArgs a{};
     a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
     a.q_idx = q_idx; a.n_q = n_q; a.nq_max = nq_max;
     a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
     a.v = v; a.vsb = vs.b; a.vsh = vs.h; a.vsr = vs.r;
+    a.vt = dt == FDL_BF16 && d == 128 ? vt : nullptr;
+    a.vtsb = vts.b; a.vtsh = vts.h; a.vtsd = static_cast<int>(vts.r);
     a.o = o; a.osb = os.b; a.osh = os.h; a.osr = os.r;
     a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.P = P; a.Gq = Hq / Hkv;
@@ -118,21 +129,22 @@ size_t fdl_dense_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv,
 
 fdl_status fdl_dense_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, const void* q,
                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
-                               const void* k, fdl_strides ks, const void* v, fdl_strides vs, float scale,
-                               void* o, fdl_strides os, float* lse, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+                               const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                               const void* vt, fdl_strides vts, float scale, void* o, fdl_strides os,
+                               float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
     fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
     if (st != FDL_OK) return st;
     if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
     if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
     if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
     if ((st = check_tensor(v, vs, dt, d)) != FDL_OK) return st;
+    if ((st = check_vt(vt, vts, dt, d, L)) != FDL_OK) return st;
     if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
     if (nq_max == 0) return FDL_OK;
     const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, L, false);
     if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
-    AttnArgs a = attn_args(dt, B, Hq, Hkv, L, L, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, scale, d, o, os,
-                           lse, ws);
+    AttnArgs a = attn_args(dt, B, Hq, Hkv, L, L, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, vt, vts, scale, d,
+                           o, os, lse, ws);
     a.sparse = 0;
     return hip_status(launch_attention(dt, d, a, pl, stream));
 }
@@ -224,6 +236,7 @@ size_t fdl_sparse_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv
 fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
                                 fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
                                 const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                const void* vt, fdl_strides vts,
                                 const int32_t* sink_idx, int n_sinks, const int32_t* block_idx, int C,
                                 int bs, float scale, void* o, fdl_strides os, float* lse, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
@@ -233,6 +246,7 @@ fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
     if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
     if ((st = check_tensor(v, vs, dt, d)) != FDL_OK) return st;
+    if ((st = check_vt(vt, vts, dt, d, L)) != FDL_OK) return st;
     if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
     if (P < 0 || P > L || bs < 1 || C < 0 || n_sinks < 0) return FDL_ERR_SHAPE;
     if ((n_sinks > 0 && !sink_idx) || (C > 0 && !block_idx)) return FDL_ERR_NULL;
@@ -241,8 +255,8 @@ fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if (nq_max == 0) return FDL_OK;
     const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, bound, true);
     if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
-    AttnArgs a = attn_args(dt, B, Hq, Hkv, L, P, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, scale, d, o, os,
-                           lse, ws);
+    AttnArgs a = attn_args(dt, B, Hq, Hkv, L, P, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, vt, vts, scale, d,
+                           o, os, lse, ws);
     a.sparse = 1;
     a.sink_idx = sink_idx;
     a.n_sinks = n_sinks;

@@ -15,6 +15,9 @@ struct AttnArgs {
     int64_t ksb, ksh, ksr;
     const void* v;
     int64_t vsb, vsh, vsr;
+    const void* vt;        // V with keys contiguous, [B, Hkv, d, L] by strides (b, h, d), or NULL
+    int64_t vtsb, vtsh;
+    int vtsd;
     void* o;
     int64_t osb, osh, osr;
     float* lse;            // [B, Hq, nq_max] or NULL

@@ -48,10 +48,12 @@ constexpr float kSlack = 8.0f;       // max growth (log2 units) tolerated before
 enum KeyMode { kDense = 0, kSparseLds = 1, kSparseList = 2 };
 
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
-// V^T tile: 128 rows (d) of 128 bytes.  Slot s (0..63) of row d holds V of LDS row
-// vt_row(s), which swaps bits 2 and 3 of s: the 8 slots of 16-byte chunk 2kc + hf then
-// hold S^T rows 16kc + 8(j/4) + 4hf + j%4, j = 0..7, the order a lane's P fragment
-// has.  Chunk c of row d sits at c ^ vt_swz(d), chosen by measuring the LDS bank-conflict
+// Row r of a K tile (and of the S^T accumulator) holds key position vt_row(r) of the
+// tile, where vt_row swaps bits 2 and 3.  A lane's P fragment for 16-key chunk kc holds
+// S^T rows 16kc + 8(j/4) + 4hf + j%4, j = 0..7, which are then key positions
+// 16kc + 8hf + j: so slot s (0..63) of a V^T row is simply key position s, and 8
+// consecutive keys of one d fill one 16-byte chunk.
+// V^T tile: 128 rows (d) of 128 bytes.  Chunk c of row d sits at c ^ vt_swz(d), chosen by measuring the LDS bank-conflict
 // counter over candidate swizzles on gfx950: the fragment reads are conflict-free and the
 // transposing stores (rows 8 apart in one instruction) 2-way; with bits 1-3 of d alone
 // the stores are 8-way.
@@ -59,8 +61,6 @@ __device__ __forceinline__ int vt_row(int s) { return (s & ~12) | ((s & 4) << 1)
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 __device__ __forceinline__ int vt_off(int d, int s) { return d * 128 + 16 * ((s >> 3) ^ vt_swz(d)) + 2 * (s & 7); }
 
-// key position (within the tile) held by LDS row r: rows 8w + 4i + g hold 8w + 2g + i
-__device__ __forceinline__ int row_pos(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
 
 // floor(n / d) for 0 <= n < 2^30 and d >= 1, with m = ceil(2^32 / d) for d >= 2.
 __device__ __forceinline__ int div_magic(int n, int d, uint32_t m) {
@@ -98,12 +98,12 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_t0[kTileB];   // V^T tiles
     __shared__ __attribute__((aligned(1024))) uint8_t s_t1[kTileB];
     __shared__ __attribute__((aligned(1024))) uint8_t s_t2[kTileB];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kTileB];   // row-major V tiles
-    __shared__ __attribute__((aligned(1024))) uint8_t s_v1[kTileB];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_v2[kTileB];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_t3[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kTileB];   // K tiles
     __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kTileB];
     __shared__ __attribute__((aligned(1024))) uint8_t s_k2[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_k3[kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kTileB];  // row-major V of a tile to transpose
     __shared__ int s_blk[MODE == kSparseLds ? kMapBlocks : 1];
     __shared__ int s_unc[MODE == kSparseLds ? kMapSinks : 1];
     __shared__ int s_tmp[17];
@@ -115,6 +115,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
     const int hf = lane >> 5;
     const int col = lane & 31;
     const int g4 = lane >> 4;
+    const int qlane = vt_row(8 * wv + g4);   // key position of this lane's first DMA row
 
     const int nqt_max = valid_q_tiles(a, kD128Rows);
     const int n_splits = dyn_splits(a, nqt_max);
@@ -201,8 +202,9 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         const int t_begin = u.split * tps;
         const int t_end = min(n_tiles, t_begin + tps);
 
-        // Rows of this lane's 2 key positions of tile t (row 0 past the split or the key
-        // set), in two halves one element apart: keys_fetch reads what the key map holds
+        // Rows of this lane's 2 key positions of tile t, qlane and qlane + 8 (LDS rows
+        // 8wv + g4 and 8wv + 4 + g4; row 0 past the split or the key set), in two halves
+        // one element apart: keys_fetch reads what the key map holds
         // for them (LDS, or the key list in global memory), keys_finish forms the rows.
         // The fetch is issued a whole element before its use, so no wave waits on it.
         // A tile that lies inside one selected block (block sizes that are multiples of
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         constexpr int kNoBase = -0x40000000;
         const bool bs64 = a.bs % 64 == 0;
         auto keys_fetch = [&](int t, int (&kr)[7]) __attribute__((always_inline)) {
-            const int q0 = t * 64 + 8 * wv + 2 * g4;
+            const int q0 = t * 64 + qlane;
             kr[6] = kNoBase;
             if (MODE == kSparseLds) {
                 const int t0q = t * 64;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int q = q0 + i;
+                const int q = q0 + 8 * i;
                 if (MODE == kSparseList) {
                     kr[3 * i] = (t < t_end && q < n_keys) ? klist[q] : 0;
                 } else if (MODE == kSparseLds) {
@@ -242,12 +244,12 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             }
         };
         auto keys_finish = [&](int t, const int (&kr)[7], int (&key)[2]) __attribute__((always_inline)) {
-            const int q0 = t * 64 + 8 * wv + 2 * g4;
+            const int q0 = t * 64 + qlane;
             const bool live = t < t_end;
             const bool whole = MODE == kSparseLds && kr[6] != kNoBase;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int q = q0 + i;
+                const int q = q0 + 8 * i;
                 const bool ok = live && q < n_keys;
                 int k;
                 if (MODE == kDense) {
@@ -263,11 +265,23 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 key[i] = ok ? k : 0;
             }
         };
-        auto keys2 = [&](int t, int (&key)[2]) __attribute__((always_inline)) {
-            int kr[7] = {0, 0, 0, 0, 0, 0, 0};
-            keys_fetch(t, kr);
-            keys_finish(t, kr, key);
+        // Tiles of 64 consecutive keys (every tile of a dense range; in I_p the tiles
+        // inside one selected block or inside [P, L), exactly those keys_fetch maps with
+        // one base) load V^T directly when the caller supplies it; the others load V
+        // rows and transpose them in LDS.  Both tests are uniform over the workgroup.
+        const bool use_vt = MODE != kSparseList && a.vt != nullptr;
+        const int n_blk_u = __builtin_amdgcn_readfirstlane(n_blk);
+        const int sink0_u = __builtin_amdgcn_readfirstlane(sink0);
+        auto whole_tile = [&](int t) __attribute__((always_inline)) {
+            if (MODE == kDense) return true;
+            if (MODE == kSparseList) return false;
+            const int t0q = t * 64;
+            return (bs64 && t0q + 64 <= n_blk_u) || (t0q >= n_blk_u && t0q + 64 <= sink0_u);
         };
+        auto tile_k0 = [&](int t, const int (&kr)[7]) __attribute__((always_inline)) {
+            return (MODE == kDense ? 0 : kr[6]) + t * 64;
+        };
+        bool raw_next = true;
 
         const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + g * a.ksh;
         const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.vsb + g * a.vsh;
@@ -286,6 +300,24 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const uint16_t* src = vbase + static_cast<int64_t>(key[i]) * vsr + 8 * (lane & 15);
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * (2 * wv + i)), 16, 0, 0);
+            }
+        };
+        // A tile of 64 consecutive keys k0 .. k0+63 (k0 a multiple of 8) straight from V^T
+        // in global memory into its swizzled LDS layout: instruction 2wv + i fills rows
+        // d = 16wv + 8i .. +7, lane l chunk l % 8 of row d, i.e. keys
+        // k0 + 8 ((l % 8) ^ vt_swz(d)) .. +7 (16 contiguous bytes).  Chunks at or past
+        // n_keys (only in the last tile of a dense key range; n_keys is a multiple of 8)
+        // read chunk 0 of the row instead, whose probabilities are zero.
+        const uint16_t* vtbase = static_cast<const uint16_t*>(a.vt) + b * a.vtsb + g * a.vtsh;
+        const int vtsd = a.vtsd;
+        auto issue_vt = [&](int k0, uint8_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int d = 16 * wv + 8 * i + (lane >> 3);
+                int kk = k0 + 8 * ((lane & 7) ^ vt_swz(d));
+                if (MODE == kDense) kk = kk < n_keys ? kk : 0;
+                const uint16_t* src = vtbase + d * vtsd + kk;
                 __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * (2 * wv + i)), 16, 0, 0);
             }
         };
@@ -314,18 +346,31 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         const int tofs = col * 128 + ((16 * hf) ^ (16 * vt_swz(col)));
 
         // ---- V tile -> V^T: lane (k, c8) moves rows 2k, 2k+1 x d = 8c8 .. 8c8+7
-        const int tr_c8 = tid & 15, tr_k = tid >> 4;
-        const int tr_s = vt_row(2 * tr_k);   // slots of rows 2k, 2k+1: tr_s, tr_s + 1
+        const int tr_c8 = tid & 15, tr_k = tid >> 4;   // rows 2k, 2k+1 go to slots vt_row(2k), +1
         auto transpose_load = [&](const uint8_t* vraw, u32x4& ra, u32x4& rb) __attribute__((always_inline)) {
             ra = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k) * kRowB + 16 * tr_c8);
             rb = *reinterpret_cast<const u32x4*>(vraw + (2 * tr_k + 1) * kRowB + 16 * tr_c8);
         };
         auto transpose_store = [&](const u32x4& ra, const u32x4& rb, uint8_t* vt) __attribute__((always_inline)) {
+            // vt_off(8 c8 + e, s) = A ^ (128 e + 16 (e / 2)), A formed here from a lane id
+            // that passes an empty asm, so the 8 addresses are not hoisted out of the tile
+            // loop (where they would stay live and spill).  The stores are written as asm:
+            // the compiler cannot tell this slot from the one a V^T load of the same
+            // element is filling (more tile buffers take LDS loads than it tracks apart)
+            // and would wait for that load first.  No load into this slot is in flight:
+            // the tile was loaded row-major, and the loads of older tiles landed before
+            // the previous barrier.
+            int el = tid;
+            asm volatile("" : "+v"(el));
+            const int c8 = el & 15, sl = vt_row(2 * (el >> 4));
+            const uint32_t A = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void*)vt)) + 1024 * c8 +
+                               2 * (sl & 7) + 16 * (((sl >> 3) ^ (4 * (c8 & 1)) ^ (c8 >> 1)) & 7);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t x = ra[e >> 1], y = rb[e >> 1];
                 const uint32_t w = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-                *reinterpret_cast<uint32_t*>(vt + vt_off(8 * tr_c8 + e, tr_s)) = w;
+                const uint32_t addr = A ^ (128 * e + 16 * (e >> 1));
+                asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(w) : "memory");
             }
         };
         auto transpose_v = [&](const uint8_t* vraw, uint8_t* vt) __attribute__((always_inline)) {
@@ -356,17 +401,26 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             // tile until both halves of the workgroup are done with it.
             const bool late = wv >= 4;
             int kn[2];
-            keys2(t_begin, kn);
-            issue_k(kn, s_k0);
-            issue_v(kn, s_v0);
-            keys2(t_begin + 1, kn);
-            issue_k(kn, s_k1);
-            issue_v(kn, s_v1);
             int kr[7] = {0, 0, 0, 0, 0, 0, 0};   // map lookups of the next tile to load
+            // V of tile t0: V^T straight into s_t0, or rows into s_t2 (free until tile
+            // t0+2 loads) transposed below; V of tile t0+1: V^T into s_t1 or rows into s_raw
+            keys_fetch(t_begin, kr);
+            const bool vt0 = use_vt && whole_tile(t_begin);
+            const int k00 = tile_k0(t_begin, kr);
+            keys_finish(t_begin, kr, kn);
+            issue_k(kn, s_k0);
+            if (vt0) issue_vt(k00, s_t0); else issue_v(kn, s_t2);
+            keys_fetch(t_begin + 1, kr);
+            const bool vt1 = use_vt && whole_tile(t_begin + 1);
+            const int k01 = tile_k0(t_begin + 1, kr);
+            keys_finish(t_begin + 1, kr, kn);
+            issue_k(kn, s_k1);
+            if (vt1) issue_vt(k01, s_t1); else issue_v(kn, s_raw);
+            raw_next = !vt1;
             keys_fetch(t_begin + 2, kr);
             __builtin_amdgcn_s_waitcnt(0);
-            transpose_v(s_v0, s_t0);
-            __syncthreads();   // K(t0), K(t0+1), V(t0+1) and V^T(t0) are complete
+            if (!vt0) transpose_v(s_t2, s_t0);
+            __syncthreads();   // K(t0), K(t0+1), V^T(t0) and V(t0+1) are complete
             if (late) barrier_keep<0>();
 
             f32x16 st[2];
@@ -374,19 +428,28 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             qk(s_k0, st);     // M(-1)
             barrier_keep<0>();
 
-            auto elem_v = [&](int t, uint8_t* kdma, uint8_t* vdma, const uint8_t* vnext, uint8_t* tnext)
-                __attribute__((always_inline)) {
+            auto elem_v = [&](int t, uint8_t* kdma, uint8_t* tdma, uint8_t* tnext) __attribute__((always_inline)) {
                 // rows of tile t+2 from the lookups fetched one element ago; the lookups of
                 // tile t+3 go out before the loads of tile t+2, so those stay the newest
                 // memory operations (barrier_keep<4> leaves exactly them in flight).  This
                 // wave's rows of V(t+1) (landed by the end of its previous M element) are
                 // read early, so the LDS round trip hides behind the softmax.
+                const bool vt2 = use_vt && whole_tile(t + 2);
+                const int k02 = tile_k0(t + 2, kr);
                 keys_finish(t + 2, kr, kn);
                 keys_fetch(t + 3, kr);
                 issue_k(kn, kdma);
-                issue_v(kn, vdma);
+                const bool raw1 = raw_next;   // V(t+1) sits row-major in s_raw
                 u32x4 ra, rb;
-                transpose_load(vnext, ra, rb);
+                if (raw1) transpose_load(s_raw, ra, rb);
+                if (vt2) {
+                    issue_vt(k02, tdma);
+                } else {
+                    // this wave's rows of s_raw are read before its DMA overwrites them
+                    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+                    issue_v(kn, s_raw);
+                }
+                raw_next = !vt2;
                 const int valid_here = n_keys - t * 64;
                 if (valid_here < 64) {
 #pragma unroll
@@ -394,7 +457,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             const int r = kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                            if (row_pos(r) >= valid_here) st[kb][i] = -INFINITY;
+                            if (vt_row(r) >= valid_here) st[kb][i] = -INFINITY;
                         }
                 }
                 // max and sum as 4 independent chains each (short dependency chains)
@@ -430,7 +493,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                         pf[kc][j] = static_cast<__bf16>(pv);
                     }
                 l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                transpose_store(ra, rb, tnext);
+                if (raw1) transpose_store(ra, rb, tnext);
                 barrier_keep<4>();   // the loads of tile t+2 may stay in flight
             };
             auto elem_m = [&](const uint8_t* tread, const uint8_t* kread) __attribute__((always_inline)) {
@@ -464,17 +527,21 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 }
                 barrier_keep<0>();   // this wave's loads of the next tile have landed
             };
-            // tile t0 + j: K in s_k[j % 3], V in s_v[j % 3], V^T in s_t[j % 3]
-            for (int t = t_begin; t < t_end; t += 3) {
-                elem_v(t, s_k2, s_v2, s_v1, s_t1);
+            // tile t0 + j: K in s_k[j % 4], V^T in s_t[j % 4]
+            for (int t = t_begin; t < t_end; t += 4) {
+                elem_v(t, s_k2, s_t2, s_t1);
                 elem_m(s_t0, s_k1);
                 if (t + 1 < t_end) {
-                    elem_v(t + 1, s_k0, s_v0, s_v2, s_t2);
+                    elem_v(t + 1, s_k3, s_t3, s_t2);
                     elem_m(s_t1, s_k2);
                 }
                 if (t + 2 < t_end) {
-                    elem_v(t + 2, s_k1, s_v1, s_v0, s_t0);
-                    elem_m(s_t2, s_k0);
+                    elem_v(t + 2, s_k0, s_t0, s_t3);
+                    elem_m(s_t2, s_k3);
+                }
+                if (t + 3 < t_end) {
+                    elem_v(t + 3, s_k1, s_t1, s_t0);
+                    elem_m(s_t3, s_k0);
                 }
             }
             if (!late) barrier_keep<0>();
@@ -490,7 +557,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         // with its loads landed, so no tile buffer is in use any more.
         const float l_tot = l_run + xhalf(l_run);
         {
-            uint8_t* stage = (wv < 2 ? s_t0 : wv < 4 ? s_t1 : wv < 6 ? s_t2 : s_v0) + (wv & 1) * 8192;
+            uint8_t* stage = (wv < 2 ? s_t0 : wv < 4 ? s_t1 : wv < 6 ? s_t2 : s_t3) + (wv & 1) * 8192;
             const float sc = n_splits > 1 ? 1.0f : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
             // The lane id goes through an empty asm, so the per-lane offsets below are formed
             // here rather than hoisted above the tile loop (where they would stay live and spill).
@@ -567,8 +634,16 @@ int d128_slots() {
     return cached[dev];
 }
 
-hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.slots));
+hipError_t launch_attn_bf16_d128(const AttnArgs& args, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(args.slots));
+    AttnArgs a = args;
+    // V^T serves the tiles of consecutive keys when every such tile starts on a 16-byte
+    // chunk: L a multiple of 8, and in I_p blocks of whole 64-key tiles and P a multiple
+    // of 8 (then the tiles of [P, L) start at P + 64 i too).  Otherwise V rows serve all.
+    if (a.vt) {
+        const bool ok = a.L % 8 == 0 && (!a.sparse || (sparse_map_in_lds(a) && a.bs % 64 == 0 && a.P % 8 == 0));
+        if (!ok) a.vt = nullptr;
+    }
     if (!a.sparse) hipLaunchKernelGGL(attn_d128_kernel<kDense>, grid, dim3(512), 0, stream, a);
     else if (sparse_map_in_lds(a)) hipLaunchKernelGGL(attn_d128_kernel<kSparseLds>, grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL(attn_d128_kernel<kSparseList>, grid, dim3(512), 0, stream, a);

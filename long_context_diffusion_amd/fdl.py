@@ -54,7 +54,7 @@ _SIGS = {
     "fdl_focus_count": (_I, [_I, _D]),
     "fdl_pcgi_select": (_I, [_P, _P, _I, _I, _I, _D, _I, _P, _P, _I, _P, _P, _I, _P]),
     "fdl_dense_attention_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
-    "fdl_dense_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P, Strides,
+    "fdl_dense_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P, Strides, _P, Strides,
                                  _F, _P, Strides, _P, _P, _SZ, _P]),
     "fdl_sink_identify_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "fdl_sink_identify": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F, _P, _I,
@@ -65,7 +65,7 @@ _SIGS = {
                                   _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "fdl_sparse_attention_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
-                                  Strides, _P, _I, _P, _I, _I, _F, _P, Strides, _P, _P, _SZ, _P]),
+                                  Strides, _P, Strides, _P, _I, _P, _I, _I, _F, _P, Strides, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -117,6 +117,27 @@ def _strides4(t: torch.Tensor) -> Strides:
     if t.dim() != 4 or t.stride(3) != 1:
         raise FdlError(2, "expected a [B, H, rows, d] tensor with a contiguous last axis")
     return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _vt(vt, v):
+    """Pointer and (b, h, d) strides of an optional [B, Hkv, d, L] V^T with contiguous keys."""
+    if vt is None:
+        return None, Strides(0, 0, 0)
+    B, H, L, d = v.shape
+    if tuple(vt.shape) != (B, H, d, L) or vt.dtype != v.dtype or vt.device != v.device:
+        raise FdlError(2, f"vt must be a [B, Hkv, d, L] tensor like v, got {tuple(vt.shape)}")
+    return _ptr(vt), _strides4(vt)
+
+
+def transpose_v(v: torch.Tensor) -> torch.Tensor:
+    """A [B, H, d, L] copy of v [B, H, L, d] with the keys contiguous (the vt argument).
+
+    The rows are padded to a multiple of 8 keys, so every stride is 16-byte aligned."""
+    B, H, L, d = v.shape
+    Lp = (L + 7) // 8 * 8
+    buf = torch.empty((B, H, d, Lp), dtype=v.dtype, device=v.device)
+    buf[..., :L].copy_(v.transpose(2, 3))
+    return buf[..., :L]
 
 
 def _stream(stream):
@@ -192,11 +213,12 @@ def dense_attention_workspace_bytes(dtype_code, B, Hq, Hkv, L, d, nq_max) -> int
     return int(lib().fdl_dense_attention_workspace_bytes(dtype_code, B, Hq, Hkv, L, d, nq_max))
 
 
-def dense_attention(q, k, v, *, q_idx=None, n_q=None, nq_max=None, scale: float = 0.0, out=None,
+def dense_attention(q, k, v, *, vt=None, q_idx=None, n_q=None, nq_max=None, scale: float = 0.0, out=None,
                     lse=None, want_lse=True, workspace=None, stream=None):
     """Full attention of the selected query rows over all keys (fdl_dense_attention).
 
-    q [B, Hq, rows, d]; k, v [B, Hkv, L, d].  Returns (o [B, Hq, nq_max, d], lse [B, Hq, nq_max] or None).
+    q [B, Hq, rows, d]; k, v [B, Hkv, L, d]; vt None or transpose_v(v).
+    Returns (o [B, Hq, nq_max, d], lse [B, Hq, nq_max] or None).
     """
     B, Hq, _, d = q.shape
     Hkv, L = k.shape[1], k.shape[2]
@@ -208,7 +230,7 @@ def dense_attention(q, k, v, *, q_idx=None, n_q=None, nq_max=None, scale: float 
         lse = torch.empty((B, Hq, nq_max), dtype=torch.float32, device=q.device)
     ws, ws_n = _ws(workspace, q.device).get(dense_attention_workspace_bytes(dt, B, Hq, Hkv, L, d, nq_max))
     st = lib().fdl_dense_attention(dt, B, Hq, Hkv, L, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
-                                   _ptr(k), _strides4(k), _ptr(v), _strides4(v), float(scale),
+                                   _ptr(k), _strides4(k), _ptr(v), _strides4(v), *_vt(vt, v), float(scale),
                                    _ptr(out), _strides4(out), _ptr(lse), ws, ws_n, _stream(stream))
     _check(st, "fdl_dense_attention")
     return out, lse
@@ -284,12 +306,13 @@ def block_score_topc(q, k, P: int, bs: int, C: int, *, q_idx=None, n_q=None, nq_
     return out[:, :C], R, kbar
 
 
-def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, q_idx=None, n_q=None,
+def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, vt=None, q_idx=None, n_q=None,
                      nq_max=None, scale: float = 0.0, out=None, lse=None, want_lse=False,
                      workspace=None, stream=None):
     """Attention of the active queries over I_p only (fdl_sparse_attention).
 
-    sink_idx [B, n_sinks] and block_idx [B, C] int32 (ascending, -1 padded) or None.
+    sink_idx [B, n_sinks] and block_idx [B, C] int32 (ascending, -1 padded) or None;
+    vt None or transpose_v(v).
     Returns (o [B, Hq, nq_max, d], lse or None).
     """
     B, Hq, _, d = q.shape
@@ -311,7 +334,7 @@ def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, q_idx=Non
     nbytes = int(lib().fdl_sparse_attention_workspace_bytes(dt, B, Hq, Hkv, L, P, d, nq_max, n_sinks, C, bs))
     ws, ws_n = _ws(workspace, q.device).get(nbytes)
     st = lib().fdl_sparse_attention(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
-                                    _ptr(k), _strides4(k), _ptr(v), _strides4(v), _ptr(sink_idx), n_sinks,
+                                    _ptr(k), _strides4(k), _ptr(v), _strides4(v), *_vt(vt, v), _ptr(sink_idx), n_sinks,
                                     _ptr(block_idx), C, int(bs), float(scale), _ptr(out), _strides4(out),
                                     _ptr(lse), ws, ws_n, _stream(stream))
     _check(st, "fdl_sparse_attention")

@@ -65,8 +65,8 @@ class StepRunner:
         F.pcgi_select(conf, mask, self.n_t, self.rho, self.w, k_cap=self.focus.shape[1], nq_max=self.nq_max,
                       out=(self.focus, self.n_focus, self.active, self.n_active))
 
-    def dense_layer(self, l, q, k, v):
-        F.dense_attention(q, k, v, out=self.out[l], lse=self.lse, **self._rows())
+    def dense_layer(self, l, q, k, v, vt=None):
+        F.dense_attention(q, k, v, vt=vt, out=self.out[l], lse=self.lse, **self._rows())
 
     def sinks_at(self, q, k):
         if self.n_sinks:
@@ -77,14 +77,15 @@ class StepRunner:
         F.block_score_topc(q, None, self.P, self.bs, self.C, kbar=self.kbar[l], L=self.L, out=self.blocks[l],
                            **self._rows())
 
-    def attend(self, l, q, k, v):
+    def attend(self, l, q, k, v, vt=None):
         """Sparse attention of one layer over the step's sinks and the layer's selected blocks."""
         sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
         blocks = self.blocks[l][:, : self.C] if self.C else None
-        F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs, out=self.out[l], **self._rows())
+        F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs, vt=vt, out=self.out[l], **self._rows())
 
-    def sparse_step(self, conf, mask, qs, ks, vs, hooks=None):
-        """A non-block-entry step; qs/ks/vs are per-layer [B, H, L, d] tensors.
+    def sparse_step(self, conf, mask, qs, ks, vs, hooks=None, vts=None):
+        """A non-block-entry step; qs/ks/vs are per-layer [B, H, L, d] tensors, vts None or
+        per-layer V^T copies (F.transpose_v) that the attention reads for runs of keys.
 
         `hooks` (optional) maps a stage name ("pcgi", "dense", "sinks", "means",
         "blocks", "sparse") to a (before, after) pair of callables run around each
@@ -108,8 +109,9 @@ class StepRunner:
         run("pcgi", lambda: self.pcgi(conf, mask))
         for l in range(self.layers):
             q, k, v = qs[l], ks[l], vs[l]
+            vt = vts[l] if vts is not None else None
             if l < self.l_dense:
-                run("dense", lambda: self.dense_layer(l, q, k, v))
+                run("dense", lambda: self.dense_layer(l, q, k, v, vt))
                 if l == self.l_dense - 1:
                     run("sinks", lambda: self.sinks_at(q, k))
             else:
@@ -119,12 +121,12 @@ class StepRunner:
                     else:
                         run("means", lambda: F.block_means(k, self.P, self.bs, out=self.kbar[l]))
                     run("blocks", lambda: self.score_blocks(l, q))
-                run("sparse", lambda: self.attend(l, q, k, v))
+                run("sparse", lambda: self.attend(l, q, k, v, vt))
         if overlap:
             main.wait_stream(self.side)
 
-    def dense_refresh(self, qs, ks, vs, outs):
+    def dense_refresh(self, qs, ks, vs, outs, vts=None):
         """A block-entry step: every query row of every layer attends to all L keys."""
         for l in range(self.layers):
-            F.dense_attention(qs[l], ks[l], vs[l], out=outs[l], want_lse=False, scale=self.scale,
-                              workspace=self.workspace)
+            F.dense_attention(qs[l], ks[l], vs[l], vt=vts[l] if vts is not None else None, out=outs[l],
+                              want_lse=False, scale=self.scale, workspace=self.workspace)

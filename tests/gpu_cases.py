@@ -57,18 +57,24 @@ def one_layer_step(wl, layer=0, step=0, device="cuda", check_refresh_rows=64, se
     Q = synth.make_q(wl, layer, step, device)
     focus, n_focus, active, n_active = gpu_select(wl, conf, mask, device)
     kw = dict(q_idx=active, n_q=n_active, nq_max=wl.nq_max, scale=wl.scale)
-    Od, lse = F.dense_attention(Q, K, V, **kw)
+    VT = F.transpose_v(V)   # read by the bf16 d = 128 path, ignored by the others
+    Od, lse = F.dense_attention(Q, K, V, vt=VT, **kw)
     sinks, scores = F.sink_identify(Q, K, lse, wl.n_sinks, want_scores=True, **kw)
     blocks, R, kbar = F.block_score_topc(Q, K, wl.P, wl.bs, wl.C, want_R=True, want_kbar=True, **kw)
     # the same scoring from means computed ahead by fdl_block_means (no keys passed)
     kbar_ahead = F.block_means(K, wl.P, wl.bs)
     blocks_ahead, R_ahead, _ = F.block_score_topc(Q, None, wl.P, wl.bs, wl.C, kbar=kbar_ahead, L=wl.L,
                                                   want_R=True, **kw)
-    Os, lse_s = F.sparse_attention(Q, K, V, wl.P, sinks, blocks, wl.bs, want_lse=True, **kw)
+    Os, lse_s = F.sparse_attention(Q, K, V, wl.P, sinks, blocks, wl.bs, vt=VT, want_lse=True, **kw)
     refresh = None
     if check_refresh_rows:
-        refresh, _ = F.dense_attention(Q, K, V, scale=wl.scale, want_lse=False)
+        refresh, _ = F.dense_attention(Q, K, V, vt=VT, scale=wl.scale, want_lse=False)
+    # without V^T every tile transposes V rows on chip: the same values reach the MFMAs
+    Od_rows, lse_rows = F.dense_attention(Q, K, V, **kw)
+    Os_rows, lse_s_rows = F.sparse_attention(Q, K, V, wl.P, sinks, blocks, wl.bs, want_lse=True, **kw)
     torch.cuda.synchronize()
+    assert torch.equal(Od, Od_rows) and torch.equal(lse, lse_rows), "dense attention differs without V^T"
+    assert torch.equal(Os, Os_rows) and torch.equal(lse_s, lse_s_rows), "sparse attention differs without V^T"
 
     actives = check_pcgi(wl, conf, mask, focus, n_focus, active, n_active)
     assert torch.equal(kbar_ahead, kbar) and torch.equal(R_ahead, R) and torch.equal(blocks_ahead, blocks), \

@@ -110,12 +110,13 @@ def test_pcgi_validation(kw, status):
 def _dense(**kw):
     a = dict(dt=F.FDL_BF16, B=1, Hq=4, Hkv=4, L=256, d=128, q=FAKE, qs=S(4 * 256 * 128, 256 * 128, 128),
              q_idx=NULL, n_q=NULL, nq_max=256, k=FAKE, ks=S(4 * 256 * 128, 256 * 128, 128), v=FAKE,
-             vs=S(4 * 256 * 128, 256 * 128, 128), scale=0.0, o=FAKE, os=S(4 * 256 * 128, 256 * 128, 128),
-             lse=NULL, ws=NULL, ws_bytes=0)
+             vs=S(4 * 256 * 128, 256 * 128, 128), vt=NULL, vts=S(0, 0, 0), scale=0.0, o=FAKE,
+             os=S(4 * 256 * 128, 256 * 128, 128), lse=NULL, ws=NULL, ws_bytes=0)
     a.update(kw)
     return F.lib().fdl_dense_attention(a["dt"], a["B"], a["Hq"], a["Hkv"], a["L"], a["d"], a["q"], a["qs"],
                                        a["q_idx"], a["n_q"], a["nq_max"], a["k"], a["ks"], a["v"], a["vs"],
-                                       a["scale"], a["o"], a["os"], a["lse"], a["ws"], a["ws_bytes"], None)
+                                       a["vt"], a["vts"], a["scale"], a["o"], a["os"], a["lse"], a["ws"],
+                                       a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -130,6 +131,14 @@ def _dense(**kw):
     (dict(nq_max=16, L=4096, ws=FAKE, ws_bytes=64), 5),
     (dict(nq_max=16, L=4096, ws=MISALIGNED, ws_bytes=1 << 30), 4),
     (dict(nq_max=0), 0),                                 # nothing to compute
+    # V^T: checked for the bf16 d = 128 path only, before anything runs
+    (dict(nq_max=0, vt=MISALIGNED, vts=S(0, 0, 256)), 4),
+    (dict(nq_max=0, vt=FAKE, vts=S(0, 0, 260)), 4),      # d-row stride not a multiple of 8
+    (dict(nq_max=0, vt=FAKE, vts=S(4, 0, 256)), 4),
+    (dict(nq_max=0, vt=FAKE, vts=S(0, 0, 248)), 2),      # d rows shorter than L
+    (dict(nq_max=0, vt=FAKE, vts=S(0, 0, 1 << 24)), 2),
+    (dict(nq_max=0, vt=FAKE, vts=S(128 * 256, 256, 256)), 0),
+    (dict(nq_max=0, dt=F.FDL_F32, vt=MISALIGNED, vts=S(0, 0, 3)), 0),   # fp32: V^T is not read or checked
 ])
 def test_dense_validation(kw, status):
     if status == 5 or status == 4 and "ws" in kw:
@@ -143,15 +152,15 @@ def test_sparse_and_sink_and_block_validation():
     st = S(4 * 256 * 128, 256 * 128, 128)
     # sparse: the key list always needs a workspace
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
-                                    FAKE, st, FAKE, 5000, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0,
+                                    FAKE, st, NULL, S(0, 0, 0), FAKE, 5000, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0,
                                     None) == 5
     # sparse: P > L, bs < 1, block list missing
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 300, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
-                                    FAKE, st, FAKE, 4, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
+                                    FAKE, st, NULL, S(0, 0, 0), FAKE, 4, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
-                                    FAKE, st, FAKE, 4, FAKE, 2, 0, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
+                                    FAKE, st, NULL, S(0, 0, 0), FAKE, 4, FAKE, 2, 0, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
-                                    FAKE, st, FAKE, 4, NULL, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 1
+                                    FAKE, st, NULL, S(0, 0, 0), FAKE, 4, NULL, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 1
     # sinks: lse and output required, n_sinks within [0, L], workspace
     assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
                                  NULL, 4, FAKE, NULL, FAKE, 1 << 20, None) == 1

@@ -177,6 +177,65 @@ def test_strided_query_layout():
     assert_close(f64(o[1]), ref, "bf16", "strided Q")
 
 
+def _vt_pair(call, v):
+    """The call with V^T and without it must give bit-identical results."""
+    o1, l1 = call(F().transpose_v(v))
+    o2, l2 = call(None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), f"outputs differ with V^T: max {float((o1.float() - o2.float()).abs().max())}"
+    assert torch.equal(l1, l2), "lse differs with V^T"
+    return o1, l1
+
+
+@pytest.mark.parametrize("L,nrows", [(1000, 37), (1000, 300), (1003, 37), (4096, 512)])
+def test_dense_with_vt(L, nrows):
+    """Dense key range from V^T (ragged last tile; L not a multiple of 8 ignores V^T)."""
+    B, Hq, Hkv, d = 2, 8, 2, 128
+    q, k, v = rand_qkv(L + nrows, B, Hq, Hkv, L, d, torch.bfloat16, sigma=1.0)
+    g = torch.Generator().manual_seed(nrows)
+    rows = torch.stack([torch.randperm(L, generator=g)[:nrows].sort().values for _ in range(B)]).to(torch.int32).to(DEV)
+    n_q = torch.tensor([nrows, nrows - 5], dtype=torch.int32, device=DEV)
+    o, lse = _vt_pair(lambda vt: F().dense_attention(q, k, v, vt=vt, q_idx=rows, n_q=n_q, nq_max=nrows), v)
+    ref, _ = O.dense_attention(f64(q)[1][:, rows[1, :nrows - 5].cpu().numpy()], f64(k)[1], f64(v)[1], 1 / math.sqrt(d))
+    assert_close(f64(o[1, :, :nrows - 5]), ref, "bf16", "dense with V^T")
+
+
+@pytest.mark.parametrize("P,bs,blk,snk", [
+    (4096, 128, [0, 3, 4, 17, 31], [3, 130, 1000, 4100]),     # whole tiles, a sinks tile
+    (4000, 128, [1, 2, 30, 31], [5, 3990, 4001]),               # ragged last block selected
+    (4000, 128, [0, 9], []),                                    # no sinks
+    (4096, 64, [0, 1, 2, 63], [100, 200, 300]),
+    (4032, 192, [0, 5, 20], [7]),
+    (4001, 128, [0, 31], [2]),                                  # P not a multiple of 8: V rows only
+])
+def test_sparse_with_vt(P, bs, blk, snk):
+    """Sparse key sets from V^T where tiles hold consecutive keys, V rows elsewhere."""
+    B, Hq, Hkv, d = 1, 8, 4, 128
+    L = P + 512
+    q, k, v = rand_qkv(P + bs, B, Hq, Hkv, L, d, torch.bfloat16, sigma=1.0, q_rows=64)
+    rows = torch.arange(0, 64, 2, dtype=torch.int32, device=DEV).reshape(1, -1)
+    blocks = torch.tensor([blk], dtype=torch.int32, device=DEV)
+    sinks = torch.tensor([snk], dtype=torch.int32, device=DEV) if snk else None
+    o, lse = _vt_pair(lambda vt: F().sparse_attention(q, k, v, P, sinks, blocks, bs, vt=vt, q_idx=rows,
+                                                      want_lse=True), v)
+    I_p = O.key_set(np.array(snk, dtype=np.int64), np.array(blk, dtype=np.int64), bs, P, L)
+    ref, _ = O.sparse_attention(f64(q)[0][:, rows[0].cpu().numpy()], f64(k)[0], f64(v)[0], I_p, 1 / math.sqrt(d))
+    assert_close(f64(o[0]), ref, "bf16", "sparse with V^T")
+
+
+def test_vt_strided_view():
+    """V^T as a view into a wider buffer (d-row stride above L)."""
+    B, Hq, Hkv, L, d = 1, 4, 4, 2048, 128
+    q, k, v = rand_qkv(5, B, Hq, Hkv, L, d, torch.bfloat16, sigma=1.0, q_rows=40)
+    wide = torch.zeros((B, Hkv, d, L + 64), dtype=torch.bfloat16, device=DEV)
+    wide[..., :L] = v.transpose(2, 3)
+    vt = wide[..., :L]
+    o1, _ = F().dense_attention(q, k, v, vt=vt)
+    o2, _ = F().dense_attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 # ------------------------------------------------------------------ sinks and blocks
 
 @pytest.mark.parametrize("L", [1000, 40000])   # LDS selection, and the global-memory fallback

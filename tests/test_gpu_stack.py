@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import long_context_diffusion_amd as F
 from workloads import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -98,8 +99,9 @@ def test_ctx32k_stack_sparse_step():
         ks.append(k)
         vs.append(v)
         qs.append(synth.make_q(wl, l, 0, dev))
+    vts = [F.transpose_v(v) for v in vs]
     run = _runner(wl, dev)
-    run.sparse_step(gpu_cases.to_dev(conf), gpu_cases.to_dev(mask), qs, ks, vs)
+    run.sparse_step(gpu_cases.to_dev(conf), gpu_cases.to_dev(mask), qs, ks, vs, vts=vts)
     torch.cuda.synchronize()
     gpu_cases.log("GPU step done; checking against the oracle")
     _check_block_form(wl, run)
@@ -116,7 +118,6 @@ def valid_sinks(run):
 
 def test_ctx32k_gqa_batch4_refresh():
     import gpu_cases
-    import long_context_diffusion_amd as F
     from oracle import focus_oracle as O
     from parity import assert_close
     wl = configs.CTX32K_GQA_B4
@@ -129,7 +130,8 @@ def test_ctx32k_gqa_batch4_refresh():
         k, v = synth.make_kv(wl, l, dev)
         q = q0[l]
         o = torch.empty_like(q)
-        F.dense_attention(q, k, v, out=o, want_lse=False, scale=wl.scale, workspace=run.workspace)
+        F.dense_attention(q, k, v, vt=F.transpose_v(v), out=o, want_lse=False, scale=wl.scale,
+                          workspace=run.workspace)
         if l in (0, wl.layers - 1):
             kept[l] = (q, k, v, o)
         else:
@@ -161,13 +163,14 @@ def test_ctx32k_gqa_batch4_sparse_steps():
 
     ks = [kvget(l)[0] for l in range(wl.layers)]
     vs = [kvget(l)[1] for l in range(wl.layers)]
+    vts = [F.transpose_v(v) for v in vs]
     for t in range(1, wl.steps):
         gpu_cases.log(f"case {wl.name}: sparse step {t}")
         states = [synth.scenario(wl, b)[t] for b in range(wl.B)]
         conf = np.stack([c for _, c in states])
         mask = np.stack([m.astype(np.uint8) for m, _ in states])
         qt = LazyQ(wl, t, dev)
-        run.sparse_step(gpu_cases.to_dev(conf), gpu_cases.to_dev(mask), qt, ks, vs)
+        run.sparse_step(gpu_cases.to_dev(conf), gpu_cases.to_dev(mask), qt, ks, vs, vts=vts)
         torch.cuda.synchronize()
         gpu_cases.check_pcgi(wl, conf, mask, run.focus, run.n_focus, run.active, run.n_active)
         _check_block_form(wl, run)
