@@ -10,21 +10,25 @@
 // items, and the number of key splits comes from the device-side row counts, so a
 // sparse step with few active rows still fills every CU.
 //   * K and V tiles go from global memory straight into LDS (global_load_lds, 16
-//     bytes per lane) through a 3-deep ring: while tile t is finished, K and V of
-//     tiles t+2 and t+3 are in flight, so every load has two iterations to land.
-//     Rows are 256 bytes, unpadded; 16-byte chunk c of LDS row r of K sits at slot
-//     c ^ (r & 15), which makes the 128-bit reads of S = K Q^T conflict-free.  One
-//     DMA instruction fills 4 LDS rows, and a lane's 2 rows of a tile hold 2
-//     consecutive key positions, so every lane maps its own keys: no index ring, no
-//     wave waiting on another.
-//   * Each V tile is transposed once, in LDS, one tile ahead of its use: every lane
-//     turns 2 rows x 8 d into 8 words of V^T.  P V then reads V^T with
-//     conflict-free 128-bit reads (transposing LDS reads of the row-major tile run
-//     at about a third of that rate on gfx950).
+//     bytes per lane) through 4-deep rings: while tile t is finished, the tiles t+1
+//     and t+2 are landing, so every load has a whole element to arrive.  K rows are
+//     256 bytes, unpadded; 16-byte chunk c of LDS row r of K sits at slot c ^ (r & 15),
+//     which makes the 128-bit reads of S = K Q^T conflict-free.  One DMA instruction
+//     fills 4 LDS rows, and a lane's 2 rows of a tile are fixed key positions, so every
+//     lane maps its own keys: no index ring, no wave waiting on another.
+//   * P V reads V^T (rows d, slots keys) with conflict-free 128-bit reads.  When the
+//     caller supplies V^T (keys contiguous), a tile of 64 consecutive keys (every tile
+//     of a dense range, the tiles inside a selected block or inside [P, L)) is loaded
+//     from it straight into the swizzled V^T layout.  Other tiles (sinks, tiles that
+//     straddle two parts of I_p, or no V^T given) load V rows into one staging buffer,
+//     and each lane turns 2 rows x 8 d into 8 words of V^T one element later
+//     (transposing LDS reads of the row-major tile run at about a third of the plain
+//     rate on gfx950).
 //   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16, keys on the M axis): one lane owns one
 //     query's softmax state.  S of tile t+1 is computed while tile t is finished.
-//   * O^T += V^T P^T, with the V^T slots ordered like the rows of the S^T
-//     accumulator, so P goes to the MFMA straight from the softmax registers.
+//   * O^T += V^T P^T.  Row r of a K tile holds key vt_row(r) of the tile, so the S^T
+//     rows a lane holds for one 16-key chunk are 8 consecutive keys: P goes to the
+//     MFMA straight from the softmax registers, and V^T slot s is simply key s.
 //   * The running max is only raised when a tile's max exceeds it by more than 2^8
 //     (exp2 units), so rescaling the accumulators is rare; the final
 //     normalisation is exact either way.
@@ -390,15 +394,16 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             // Ping-pong schedule.  Every wave runs the element sequence
             //   M(-1) | V(0) | M(0) | V(1) | M(1) | ... | M(n-1)
             // with a workgroup barrier after each element, where for tile t = t0 + j
-            //   V(j): softmax of S(t) -> P(t); K and V of this wave's 8 rows of tile t+2
-            //         are loaded; this wave's rows of V(t+1) are transposed into V^T(t+1)
+            //   V(j): softmax of S(t) -> P(t); this wave's share of K(t+2) and of V^T(t+2)
+            //         (or of the V rows of t+2, into the staging buffer) is loaded; if
+            //         V(t+1) was staged, this wave transposes its own rows into V^T(t+1)
             //   M(j): O += V(t) P(t) from V^T(t); S(t+1) = K(t+1) Q^T
             // Waves 4..7 run one element behind waves 0..3 (one extra barrier up front,
             // waves 0..3 take theirs at the end).  Wave w and wave w+4 share a SIMD, so
             // while one of them is in an MFMA element the other is in a VALU element.
-            // A wave only ever transposes the rows it loaded itself, so its loads need
-            // no barrier before its transposes; three stages of every buffer keep each
-            // tile until both halves of the workgroup are done with it.
+            // A wave reads the staging buffer's rows it loaded itself before loading the
+            // next staged tile over them, so staging needs no barrier; four stages of K and
+            // V^T keep each tile until both halves of the workgroup are done with it.
             const bool late = wv >= 4;
             int kn[2];
             int kr[7] = {0, 0, 0, 0, 0, 0, 0};   // map lookups of the next tile to load
