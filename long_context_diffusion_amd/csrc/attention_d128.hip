@@ -61,9 +61,30 @@ __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 // counter over candidate swizzles on gfx950: the fragment reads are conflict-free and the
 // transposing stores (rows 8 apart in one instruction) 2-way; with bits 1-3 of d alone
 // the stores are 8-way.
-__device__ __forceinline__ int vt_row(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
-__device__ __forceinline__ int vt_off(int d, int s) { return d * 128 + 16 * ((s >> 3) ^ vt_swz(d)) + 2 * (s & 7); }
+__host__ __device__ constexpr int vt_row(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+__host__ __device__ constexpr int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
+__host__ __device__ constexpr int vt_off(int d, int s) { return d * 128 + 16 * ((s >> 3) ^ vt_swz(d)) + 2 * (s & 7); }
+
+// The two writers of a V^T tile compute vt_off in closed forms; both are checked here
+// against it at compile time.  The V^T DMA: instruction m, lane l writes LDS bytes
+// 1024 m + 16 l, the chunk of row d = 8 m + l / 8 that holds slots 8 ((l % 8) ^ vt_swz(d)) + 0..7.
+// The transposing store of thread t: word e at A(t) ^ (128 e + 16 (e / 2)), d = 8 (t % 16) + e,
+// slot vt_row(2 (t / 16)).
+constexpr bool vt_writers_match_layout() {
+    for (int m = 0; m < 16; ++m)
+        for (int l = 0; l < 64; ++l) {
+            const int d = 8 * m + l / 8;
+            if (vt_off(d, 8 * ((l % 8) ^ vt_swz(d))) != 1024 * m + 16 * l) return false;
+        }
+    for (int t = 0; t < 512; ++t) {
+        const int c8 = t & 15, sl = vt_row(2 * (t >> 4));
+        const int A = 1024 * c8 + 2 * (sl & 7) + 16 * (((sl >> 3) ^ (4 * (c8 & 1)) ^ (c8 >> 1)) & 7);
+        for (int e = 0; e < 8; ++e)
+            if ((A ^ (128 * e + 16 * (e >> 1))) != vt_off(8 * c8 + e, sl)) return false;
+    }
+    return true;
+}
+static_assert(vt_writers_match_layout(), "V^T writers disagree with vt_off");
 
 
 // floor(n / d) for 0 <= n < 2^30 and d >= 1, with m = ceil(2^32 / d) for d >= 2.
