@@ -184,3 +184,22 @@ def test_sparse_and_sink_and_block_validation():
         a.update(kw_)
         assert lib.fdl_block_means(F.FDL_BF16, a["B"], a["Hkv"], a["L"], a["P"], a["d"], a["k"], st, a["bs"],
                                    a["kbar"], None) == status, kw_
+
+
+def test_vt_marshalling():
+    """The binding passes V^T as (pointer, (b, h, d) strides) and rejects a tensor that is
+    not V's [B, Hkv, d, L] transpose; transpose_v pads rows to 8 keys (aligned strides)."""
+    import torch
+    from long_context_diffusion_amd import fdl
+    v = torch.zeros((2, 3, 13, 128), dtype=torch.bfloat16)
+    vt = fdl.transpose_v(v)
+    assert tuple(vt.shape) == (2, 3, 128, 13) and vt.stride(3) == 1
+    assert vt.stride(2) == 16 and vt.stride(1) == 128 * 16 and vt.stride(0) == 3 * 128 * 16
+    assert torch.equal(vt, v.transpose(2, 3))
+    ptr, st = fdl._vt(vt, v)
+    assert ptr.value == vt.data_ptr() and (st.b, st.h, st.r) == (3 * 128 * 16, 128 * 16, 16)
+    assert fdl._vt(None, v)[0] is None
+    with pytest.raises(fdl.FdlError):
+        fdl._vt(v, v)                                   # not transposed
+    with pytest.raises(fdl.FdlError):
+        fdl._vt(vt.to(torch.float32), v)                # dtype differs
