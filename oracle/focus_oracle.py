@@ -38,7 +38,8 @@ reason in the design notes):
 Pins (tests marked "not gpu"): brute-force dominance and exhaustive subset
 checks for every selection, exact rational block means, closed-form and
 hand-worked attention fixtures, a library softmax/attention routine on small
-inputs, the sparse == dense reduction, and recovery of injected sinks.  The
+inputs, the sparse == dense reduction, recovery of injected sinks, and the KV
+refresh against the identity refresh and the incremental block-means formula.  The
 pages print no worked example, so no pin holds a value printed on a page.
 Parity of the readings R1, R3, R4, R5 against the authors' own code is
 unpinned: the pins fix the oracle to these readings, not the readings to the
@@ -185,6 +186,32 @@ def block_means(K, P: int, bs: int) -> np.ndarray:
         lo, hi = b * bs, min((b + 1) * bs, P)
         kbar[:, b] = K[:, lo:hi].sum(axis=1) / (hi - lo)
     return kbar
+
+
+def kv_refresh(K, V, rows, K_new, V_new):
+    """The approximate KV cache after one refresh: the rows of U(t) take their recomputed
+    keys and values, every other row keeps its cached ones.
+
+    Summary, "Prerequisites" (approximate KV cache): K_i = f_K(x^(t))_i for i in U(t),
+    otherwise the cached value; the same for V.  K, V [Hkv, L, d]; rows the positions of
+    U(t) (distinct; entries outside [0, L) are ignored); K_new, V_new [Hkv, len(rows), d],
+    column j holding the new row of position rows[j].  Returns new arrays.
+    """
+    K2 = np.array(K, dtype=np.float64, copy=True)
+    V2 = np.array(V, dtype=np.float64, copy=True)
+    L = K2.shape[1]
+    for j, r in enumerate(rows):
+        r = int(r)
+        if 0 <= r < L:
+            K2[:, r] = np.asarray(K_new, dtype=np.float64)[:, j]
+            V2[:, r] = np.asarray(V_new, dtype=np.float64)[:, j]
+    return K2, V2
+
+
+def refreshed_blocks(rows, P: int, bs: int) -> np.ndarray:
+    """The prompt blocks holding a refreshed row: the only block means a refresh can change
+    (Summary, "Method steps" (4): a block's representative is the mean of its own keys)."""
+    return np.array(sorted({int(r) // bs for r in rows if 0 <= int(r) < P}), dtype=np.int64)
 
 
 def block_relevance(Q_rows, kbar, scale: float) -> np.ndarray:

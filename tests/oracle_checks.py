@@ -404,11 +404,47 @@ def check_step_composition():
     _close(st.out[("sparse", 0)], out, 0.0, "driver sparse output")
 
 
+
+def check_kv_refresh(seed=11):
+    """The refreshed cache: new rows where U(t) says, cached rows elsewhere; refreshing
+    rows with their own values changes nothing; and the block means of the refreshed cache
+    equal the old means plus the incremental correction sum(new - old) / |block| of the
+    refreshed blocks only (an independent formula for the same result)."""
+    rng = np.random.default_rng(seed)
+    Hkv, L, d, P, bs = 2, 300, 16, 250, 16
+    K = _bf16_grid(rng, (Hkv, L, d))
+    V = _bf16_grid(rng, (Hkv, L, d))
+    rows = np.array([3, 4, 40, 47, 48, 199, 245, 249, 250, 290, -1])
+    valid = rows[rows >= 0]
+    Kn = _bf16_grid(rng, (Hkv, len(rows), d))
+    Vn = _bf16_grid(rng, (Hkv, len(rows), d))
+    K2, V2 = O.kv_refresh(K, V, rows, Kn, Vn)
+    for j, r in enumerate(rows):
+        if r >= 0:
+            assert np.array_equal(K2[:, r], Kn[:, j]) and np.array_equal(V2[:, r], Vn[:, j])
+    keep = np.setdiff1d(np.arange(L), valid)
+    assert np.array_equal(K2[:, keep], K[:, keep]) and np.array_equal(V2[:, keep], V[:, keep])
+    K3, V3 = O.kv_refresh(K, V, valid, K[:, valid], V[:, valid])
+    assert np.array_equal(K3, K) and np.array_equal(V3, V)
+    old, new = O.block_means(K, P, bs), O.block_means(K2, P, bs)
+    touched = O.refreshed_blocks(rows, P, bs)
+    assert list(touched) == sorted({r // bs for r in valid if r < P})
+    inc = old.copy()
+    for j, r in enumerate(rows):
+        if 0 <= r < P:
+            b = r // bs
+            size = min((b + 1) * bs, P) - b * bs
+            inc[:, b] += (Kn[:, j] - K[:, r]) / size
+    _close(new, inc, 1e-12, "incremental block means")
+    untouched = np.setdiff1d(np.arange(old.shape[1]), touched)
+    assert np.array_equal(new[:, untouched], old[:, untouched])
+
+
 ALL_CHECKS = [
     check_focus_count, check_pcgi_dominance, check_pcgi_exhaustive, check_pcgi_window_fixture,
     check_window_closed_forms, check_attention_closed_form, check_attention_vs_library,
     check_attention_invariants, check_sink_scores_vs_library, check_sink_select_dominance,
     check_sink_recovery, check_block_means_exact, check_relevance_bruteforce,
     check_block_fixture, check_key_set, check_sparse_equals_dense, check_sparse_vs_library,
-    check_step_composition,
+    check_step_composition, check_kv_refresh,
 ]
