@@ -12,6 +12,8 @@
  *   fdl_block_means       (4) mean key per prompt block (keys only: can run ahead)
  *   fdl_block_score_topc  (4) relevance R_b of the active queries, top-C blocks
  *   fdl_sparse_attention  (5) attention of the active queries over I_p only
+ *   fdl_kv_refresh        approximate KV cache: the rows of U(t) take new K/V (Prerequisites)
+ *   fdl_block_means_refresh  (4) the means of the blocks a refresh touched
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
@@ -218,6 +220,41 @@ fdl_status fdl_sparse_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
                                 const int32_t* block_idx, int C, int bs,
                                 float scale, void* o, fdl_strides os, float* lse,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fdl_kv_refresh - the approximate KV cache refresh of one step.
+ * Summary page, "Prerequisites" (approximate KV cache): the rows of the refresh set
+ * U(t) take freshly computed keys and values, every other row keeps its cached ones.
+ *   rows       [B, n_max] int32 positions of U(t) (distinct within a sequence; entries
+ *              outside [0, L) are skipped), e.g. active_idx; n_rows [B] or NULL (all n_max)
+ *   k_new, v_new  [B, Hkv, n_max, d] with strides kns, vns: row i belongs to rows[b][i]
+ *   k, v       [B, Hkv, L, d] caches with strides ks, vs, updated in place
+ *   vt, vts    NULL, or the caller's keys-contiguous copy of v (as in fdl_dense_attention),
+ *              updated too (stride checks as there)
+ * Pure data movement; rows repeated within a sequence race (which write lands is not
+ * defined).  Errors: as fdl_dense_attention for dtype, sizes and alignment; rows NULL
+ * with n_max > 0 is FDL_ERR_NULL.
+ */
+fdl_status fdl_kv_refresh(fdl_dtype dtype, int B, int Hkv, int L, int d, const int32_t* rows,
+                          const int32_t* n_rows, int n_max, const void* k_new, fdl_strides kns,
+                          const void* v_new, fdl_strides vns, void* k, fdl_strides ks, void* v,
+                          fdl_strides vs, void* vt, fdl_strides vts, hipStream_t stream);
+
+/*
+ * fdl_block_means_refresh - the block means after a KV refresh.
+ * Summary page, "Method steps" (4): a block's mean depends on its own keys only, so
+ * after fdl_kv_refresh only the blocks holding a refreshed prompt row (< P) change.
+ * This recomputes exactly those entries of kbar [B, Hkv, nb, d] (fp32, as
+ * fdl_block_means writes them, bit for bit) from the refreshed k, and leaves the
+ * others as they are.  rows, n_rows, n_max as in fdl_kv_refresh; an ascending row
+ * list recomputes each touched block once (any order gives the same result).
+ * Errors: dtype, sizes, alignment as fdl_block_means; kbar NULL, or rows NULL with
+ * n_max > 0, is FDL_ERR_NULL.
+ */
+fdl_status fdl_block_means_refresh(fdl_dtype dtype, int B, int Hkv, int L, int P, int d,
+                                   const void* k, fdl_strides ks, int bs, const int32_t* rows,
+                                   const int32_t* n_rows, int n_max, float* kbar,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

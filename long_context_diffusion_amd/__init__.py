@@ -5,6 +5,6 @@ The compute path is libfdl.so (hand-written HIP kernels, C ABI in include/fdl.h)
 """
 from . import fdl  # noqa: F401
 from .fdl import (  # noqa: F401
-    FdlError, Workspace, block_means, block_score_topc, dense_attention, focus_count, pcgi_select,
-    sink_identify, sparse_attention, transpose_v,
+    FdlError, Workspace, block_means, block_means_refresh, block_score_topc, dense_attention, focus_count, pcgi_select,
+    kv_refresh, sink_identify, sparse_attention, transpose_v,
 )

@@ -48,6 +48,26 @@ hipError_t launch_sink_identify(fdl_dtype dtype, int d, SinkArgs a, int n_sinks,
 
 size_t block_workspace_bytes(int B, int Hq, int Hkv, int P, int d, int bs, int nq_max);
 hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStream_t stream);
+
+// approximate KV cache refresh (cache.hip)
+struct CacheArgs {
+    int B, Hkv, L, P, d, bs, nb, n_max;
+    const int32_t* rows;     // [B, n_max] refreshed positions, -1 entries skipped
+    const int32_t* n_rows;   // [B] valid entries, or NULL (all n_max)
+    const void* k_new;
+    int64_t knb, knh, knr;
+    const void* v_new;
+    int64_t vnb, vnh, vnr;
+    void* k;
+    int64_t ksb, ksh, ksr;
+    void* v;
+    int64_t vsb, vsh, vsr;
+    void* vt;                // [B, Hkv, d, L] keys contiguous, or NULL
+    int64_t vtsb, vtsh, vtsd;
+    float* kbar;             // [B, Hkv, nb, d]
+};
+hipError_t launch_kv_scatter(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream);
+hipError_t launch_block_means_refresh(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream);
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream);
 

@@ -30,6 +30,7 @@ EXPORTS = (
     "fdl_sink_identify_workspace_bytes", "fdl_sink_identify",
     "fdl_block_means", "fdl_block_score_topc_workspace_bytes", "fdl_block_score_topc",
     "fdl_sparse_attention_workspace_bytes", "fdl_sparse_attention",
+    "fdl_kv_refresh", "fdl_block_means_refresh",
 )
 
 
@@ -64,6 +65,9 @@ _SIGS = {
     "fdl_block_score_topc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
                                   _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "fdl_sparse_attention_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "fdl_kv_refresh": (_I, [_I, _I, _I, _I, _I, _P, _P, _I, _P, Strides, _P, Strides, _P, Strides, _P, Strides,
+                            _P, Strides, _P]),
+    "fdl_block_means_refresh": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _I, _P, _P, _I, _P, _P]),
     "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
                                   Strides, _P, Strides, _P, _I, _P, _I, _I, _F, _P, Strides, _P, _P, _SZ, _P]),
 }
@@ -271,6 +275,36 @@ def block_means(k, P: int, bs: int, *, out=None, stream=None):
                                _stream(stream))
     _check(st, "fdl_block_means")
     return out
+
+
+def kv_refresh(rows, k_new, v_new, k, v, *, n_rows=None, vt=None, stream=None):
+    """Approximate KV cache refresh (fdl_kv_refresh): rows [B, n_max] int32 (-1 skipped),
+    k_new, v_new [B, Hkv, n_max, d] into the caches k, v [B, Hkv, L, d] (and vt, when given)."""
+    B, Hkv, L, d = k.shape
+    n_max = rows.shape[1]
+    if rows.dtype != torch.int32 or not rows.is_contiguous():
+        raise FdlError(2, "rows must be a contiguous int32 [B, n_max] tensor")
+    if tuple(k_new.shape) != (B, Hkv, n_max, d) or tuple(v_new.shape) != (B, Hkv, n_max, d):
+        raise FdlError(2, "k_new, v_new must be [B, Hkv, n_max, d]")
+    vtp, vts = _vt(vt, v)
+    st = lib().fdl_kv_refresh(_dtype_code(k), B, Hkv, L, d, _ptr(rows), _ptr(n_rows), n_max, _ptr(k_new),
+                              _strides4(k_new), _ptr(v_new), _strides4(v_new), _ptr(k), _strides4(k), _ptr(v),
+                              _strides4(v), vtp, vts, _stream(stream))
+    _check(st, "fdl_kv_refresh")
+
+
+def block_means_refresh(k, P: int, bs: int, rows, kbar, *, n_rows=None, stream=None):
+    """The block means a refresh touched (fdl_block_means_refresh), recomputed in kbar."""
+    B, Hkv, L, d = k.shape
+    nb = -(-P // bs)
+    if tuple(kbar.shape) != (B, Hkv, nb, d) or kbar.dtype != torch.float32 or not kbar.is_contiguous():
+        raise FdlError(2, "block means: expected a contiguous [B, Hkv, nb, d] fp32 kbar")
+    if rows.dtype != torch.int32 or not rows.is_contiguous():
+        raise FdlError(2, "rows must be a contiguous int32 [B, n_max] tensor")
+    st = lib().fdl_block_means_refresh(_dtype_code(k), B, Hkv, L, P, d, _ptr(k), _strides4(k), int(bs),
+                                       _ptr(rows), _ptr(n_rows), rows.shape[1], _ptr(kbar), _stream(stream))
+    _check(st, "fdl_block_means_refresh")
+    return kbar
 
 
 def block_score_topc(q, k, P: int, bs: int, C: int, *, q_idx=None, n_q=None, nq_max=None,

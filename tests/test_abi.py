@@ -31,7 +31,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = F.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert sorted(F.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -203,3 +203,33 @@ def test_vt_marshalling():
         fdl._vt(v, v)                                   # not transposed
     with pytest.raises(fdl.FdlError):
         fdl._vt(vt.to(torch.float32), v)                # dtype differs
+
+
+def test_kv_refresh_validation():
+    lib = F.lib()
+    st = S(4 * 256 * 128, 256 * 128, 128)
+    z = S(0, 0, 0)
+    # rows missing, sizes, dtype, alignment; nothing to do with n_max = 0
+    assert lib.fdl_kv_refresh(F.FDL_BF16, 1, 4, 256, 128, NULL, NULL, 8, FAKE, st, FAKE, st, FAKE, st, FAKE, st,
+                              NULL, z, None) == 1
+    assert lib.fdl_kv_refresh(F.FDL_BF16, 1, 4, 256, 128, FAKE, NULL, -1, FAKE, st, FAKE, st, FAKE, st, FAKE, st,
+                              NULL, z, None) == 2
+    assert lib.fdl_kv_refresh(F.FDL_BF16, 1, 4, 256, 96, FAKE, NULL, 8, FAKE, st, FAKE, st, FAKE, st, FAKE, st,
+                              NULL, z, None) == 7
+    assert lib.fdl_kv_refresh(F.FDL_BF16, 1, 4, 256, 128, FAKE, NULL, 8, FAKE, st, FAKE, st, MISALIGNED, st, FAKE,
+                              st, NULL, z, None) == 4
+    assert lib.fdl_kv_refresh(F.FDL_BF16, 1, 4, 256, 128, FAKE, NULL, 0, FAKE, st, FAKE, st, FAKE, st, FAKE, st,
+                              FAKE, S(0, 0, 248), None) == 2          # V^T rows shorter than L
+    assert lib.fdl_kv_refresh(F.FDL_BF16, 1, 4, 256, 128, FAKE, NULL, 0, FAKE, st, FAKE, st, FAKE, st, FAKE, st,
+                              NULL, z, None) == 0
+    # block means refresh: kbar and rows required, P within [1, L], bs >= 1
+    assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 4, 256, 192, 128, FAKE, st, 64, FAKE, NULL, 8, NULL,
+                                       None) == 1
+    assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 4, 256, 192, 128, FAKE, st, 64, NULL, NULL, 8, FAKE,
+                                       None) == 1
+    assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 4, 256, 300, 128, FAKE, st, 64, FAKE, NULL, 8, FAKE,
+                                       None) == 2
+    assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 4, 256, 192, 128, FAKE, st, 0, FAKE, NULL, 8, FAKE,
+                                       None) == 2
+    assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 4, 256, 192, 128, FAKE, st, 64, NULL, NULL, 0, FAKE,
+                                       None) == 0
