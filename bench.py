@@ -472,18 +472,32 @@ def main():
         knew = [torch.randn(shp, generator=g_new, device=dev).to(torch.bfloat16) for _ in range(wl.layers)]
         vnew = [torch.randn(shp, generator=g_new, device=dev).to(torch.bfloat16) for _ in range(wl.layers)]
 
+        side = torch.cuda.Stream(device=dev)
+        done = [torch.cuda.Event() for _ in range(wl.layers)]
+
         def cached_step():
+            # the refresh of every layer runs on a second stream once PCGI has the active
+            # rows; each layer waits for its own refresh (as the full pass waits for its means)
             run.pcgi(conf, mask)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for l in range(wl.layers):
+                    F.kv_refresh(run.active, knew[l], vnew[l], ks[l], vs[l], n_rows=run.n_active, vt=vts[l],
+                                 stream=side)
+                    if l >= wl.l_dense:
+                        F.block_means_refresh(ks[l], wl.P, wl.bs, run.active, run.kbar[l], n_rows=run.n_active,
+                                              stream=side)
+                    done[l].record(side)
             for l in range(wl.layers):
-                F.kv_refresh(run.active, knew[l], vnew[l], ks[l], vs[l], n_rows=run.n_active, vt=vts[l])
+                stream.wait_event(done[l])
                 if l < wl.l_dense:
                     run.dense_layer(l, qs[l], ks[l], vs[l], vts[l])
                     if l == wl.l_dense - 1:
                         run.sinks_at(qs[l], ks[l])
                 else:
-                    F.block_means_refresh(ks[l], wl.P, wl.bs, run.active, run.kbar[l], n_rows=run.n_active)
                     run.score_blocks(l, qs[l])
                     run.attend(l, qs[l], ks[l], vs[l], vts[l])
+            stream.wait_stream(side)
 
         for _ in range(2):
             cached_step()
