@@ -111,7 +111,7 @@ def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=0.25):
         threads = 1
     t = {}
     t0 = time.perf_counter()
-    focus = O.pcgi_focus(conf[0], mask[0], wl.k)
+    focus = O.pcgi_focus(conf[0], mask[0], O.focus_count(wl.n_t, wl.rho))
     active = O.window_active(focus, wl.w, wl.L)
     t["pcgi"] = time.perf_counter() - t0
     na = len(active)
@@ -425,7 +425,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.L, "prompt": wl.P, "gen": wl.G,
                    "masked": wl.masked, "heads_q_kv": [wl.Hq, wl.Hkv], "head_dim": wl.d, "layers": wl.layers,
-                   "l_dense": wl.l_dense, "k": wl.k, "w": wl.w, "block": wl.bs, "top_c": wl.C,
+                   "l_dense": wl.l_dense, "k": run.k, "w": wl.w, "block": wl.bs, "top_c": wl.C,
                    "n_sinks": wl.n_sinks, "parallelism": "single GPU"},
         "step_us": round(ms * 1000, 1),
         "pct_hbm_peak": round(100 * step_bytes / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 2),

@@ -28,8 +28,8 @@ def to_dev(a, device="cuda"):
 
 
 def gpu_select(wl, conf, mask, device="cuda"):
-    return F.pcgi_select(to_dev(conf, device), to_dev(mask, device), wl.n_t, wl.rho, wl.w,
-                         k_cap=max(wl.k, 1), nq_max=wl.nq_max)
+    """PCGI through the library; k and the active-row capacity are the library's own."""
+    return F.pcgi_select(to_dev(conf, device), to_dev(mask, device), wl.n_t, wl.rho, wl.w)
 
 
 def check_pcgi(wl, conf, mask, focus, n_focus, active, n_active):
@@ -37,8 +37,9 @@ def check_pcgi(wl, conf, mask, focus, n_focus, active, n_active):
     focus, n_focus = focus.cpu().numpy(), n_focus.cpu().numpy()
     active, n_active = active.cpu().numpy(), n_active.cpu().numpy()
     actives = []
+    k_o = O.focus_count(wl.n_t, wl.rho)
     for b in range(wl.B):
-        f_o = O.pcgi_focus(conf[b], mask[b], wl.k)
+        f_o = O.pcgi_focus(conf[b], mask[b], k_o)
         a_o = O.window_active(f_o, wl.w, wl.L)
         assert n_focus[b] == len(f_o) and n_active[b] == len(a_o)
         assert_exact_set(focus[b, : n_focus[b]], f_o, f"I_focus[{b}]")
@@ -56,7 +57,7 @@ def one_layer_step(wl, layer=0, step=0, device="cuda", check_refresh_rows=64, se
     K, V = synth.make_kv(wl, layer, device)
     Q = synth.make_q(wl, layer, step, device)
     focus, n_focus, active, n_active = gpu_select(wl, conf, mask, device)
-    kw = dict(q_idx=active, n_q=n_active, nq_max=wl.nq_max, scale=wl.scale)
+    kw = dict(q_idx=active, n_q=n_active, nq_max=active.shape[1], scale=wl.scale)
     VT = F.transpose_v(V)   # read by the bf16 d = 128 path, ignored by the others
     Od, lse = F.dense_attention(Q, K, V, vt=VT, **kw)
     sinks, scores = F.sink_identify(Q, K, lse, wl.n_sinks, want_scores=True, **kw)

@@ -247,7 +247,7 @@ def check_sink_recovery(seeds=(0, 1, 2)):
         conf, mask = synth.step_inputs(wl)
         K, V = (synth.to_f64(t)[0] for t in synth.make_kv(wl, 0))
         Q = synth.to_f64(synth.make_q(wl, 0))[0]
-        focus = O.pcgi_focus(conf[0], mask[0], wl.k)
+        focus = O.pcgi_focus(conf[0], mask[0], O.focus_count(wl.n_t, wl.rho))
         active = O.window_active(focus, wl.w, wl.L)
         _, lse = O.dense_attention(Q[:, active], K, V, wl.scale)
         sinks = O.sink_select(O.sink_scores(Q[:, active], K, lse, wl.scale), wl.n_sinks)
@@ -358,7 +358,7 @@ def check_sparse_equals_dense():
     """Every block kept and a window over the whole sequence: sparse == dense."""
     wl = configs.TINY_2K_F32
     conf, mask, Q, K, V = _tiny_inputs(wl)
-    focus = O.pcgi_focus(conf, mask, wl.k)
+    focus = O.pcgi_focus(conf, mask, O.focus_count(wl.n_t, wl.rho))
     active = O.window_active(focus, 2 * wl.L, wl.L)
     assert list(active) == list(range(wl.L))
     Qa = Q[:, active[::17]]
@@ -396,13 +396,50 @@ def check_step_composition():
     st = O.sparse_step(conf, mask, lambda l: (Q, K, V), layers=1, l_dense=1, n_t=wl.n_t,
                        rho=wl.rho, w=wl.w, P=wl.P, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
                        scale=wl.scale)
-    assert len(st.focus) == wl.k
+    assert len(st.focus) == 8   # k = floor(2 * 4) stated by the 2K workload
     assert list(st.sinks) == list(wl.sinks_fixed)
     assert {s // wl.bs for s in wl.sinks_fixed} <= set(st.blocks[0].tolist())
     out, _ = O.sparse_attention(Q[:, st.active], K, V,
                                 O.key_set(st.sinks, st.blocks[0], wl.bs, wl.P, wl.L), wl.scale)
     _close(st.out[("sparse", 0)], out, 0.0, "driver sparse output")
 
+
+
+def _touched_by_enumeration(rows, P, bs):
+    """Blocks b of [0, ceil(P/bs)) whose span [b*bs, min((b+1)*bs, P)) holds a refreshed row:
+    each block is tested against every row, with no division."""
+    nb = -(-P // bs)
+    out = []
+    for b in range(nb):
+        lo, hi = b * bs, min((b + 1) * bs, P)
+        if any(lo <= int(r) < hi for r in rows):
+            out.append(b)
+    return out
+
+
+def _check_touched_blocks(rows, P, bs, touched):
+    assert list(touched) == _touched_by_enumeration(rows, P, bs), f"touched blocks {list(touched)}"
+
+
+def check_refreshed_blocks(seed=12):
+    """The blocks a refresh touches, against enumeration over the blocks: rows at and past
+    the prompt end (one inside the prompt's last, short block span if it were not cut at P),
+    negative entries, repeats, a row in the last prompt block, and random lists."""
+    cases = [
+        ([250, 251, 255, 290, -1], 250, 16),       # only rows >= P: nothing touched
+        ([0, 15, 16, 249], 250, 16),               # block edges and the short last block
+        ([239, 240, 240, 7, 7], 250, 16),          # repeats, any order
+        ([], 250, 16),
+        ([63, 64, 127, 128], 129, 64),             # last block of one key
+    ]
+    rng = np.random.default_rng(seed)
+    for _ in range(40):
+        P = int(rng.integers(1, 400))
+        bs = int(rng.integers(1, 70))
+        rows = rng.integers(-3, P + 40, size=int(rng.integers(0, 30))).tolist()
+        cases.append((rows, P, bs))
+    for rows, P, bs in cases:
+        _check_touched_blocks(rows, P, bs, O.refreshed_blocks(rows, P, bs))
 
 
 def check_kv_refresh(seed=11):
@@ -428,7 +465,7 @@ def check_kv_refresh(seed=11):
     assert np.array_equal(K3, K) and np.array_equal(V3, V)
     old, new = O.block_means(K, P, bs), O.block_means(K2, P, bs)
     touched = O.refreshed_blocks(rows, P, bs)
-    assert list(touched) == sorted({r // bs for r in valid if r < P})
+    _check_touched_blocks(rows, P, bs, touched)
     inc = old.copy()
     for j, r in enumerate(rows):
         if 0 <= r < P:
@@ -446,5 +483,5 @@ ALL_CHECKS = [
     check_attention_invariants, check_sink_scores_vs_library, check_sink_select_dominance,
     check_sink_recovery, check_block_means_exact, check_relevance_bruteforce,
     check_block_fixture, check_key_set, check_sparse_equals_dense, check_sparse_vs_library,
-    check_step_composition, check_kv_refresh,
+    check_step_composition, check_kv_refresh, check_refreshed_blocks,
 ]

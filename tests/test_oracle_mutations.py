@@ -57,6 +57,14 @@ def _key_set_block_shift(sinks, blocks, bs, P, L):
     return _orig["key_set"](sinks, [b + 1 for b in blocks if b + 1 < -(-P // bs)], bs, P, L)
 
 
+def _refreshed_blocks_no_prompt_bound(rows, P, bs):
+    return np.array(sorted({int(r) // bs for r in rows if int(r) >= 0}), dtype=np.int64)
+
+
+def _refreshed_blocks_ceil(rows, P, bs):
+    return np.array(sorted({-(-int(r) // bs) for r in rows if 0 <= int(r) < P}), dtype=np.int64)
+
+
 MUTATIONS = {
     "tie_break_highest_index": ("rank_select", _rank_highest_index),
     "select_smallest": ("rank_select", _rank_smallest),
@@ -82,6 +90,8 @@ MUTATIONS = {
                                lambda Q, kbar, s: -_orig["block_relevance"](Q, kbar, s)),
     "key_set_without_generation_region": ("key_set", _key_set_no_gen),
     "key_set_block_off_by_one": ("key_set", _key_set_block_shift),
+    "refreshed_blocks_past_prompt": ("refreshed_blocks", _refreshed_blocks_no_prompt_bound),
+    "refreshed_blocks_rounded_up": ("refreshed_blocks", _refreshed_blocks_ceil),
     "sparse_ignores_key_set": ("sparse_attention",
                                lambda Q, K, V, I_p, s: _orig["attention"](Q, K, V, s)),
 }

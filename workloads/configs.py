@@ -34,7 +34,7 @@ class Workload:
     Hkv: int                  # key/value heads (Hq % Hkv == 0)
     d: int                    # head dim
     n_t: int                  # n(t): tokens decoded per step
-    rho: float                # expansion factor
+    rho: float                # expansion factor (k = floor(rho * n(t)) is computed by each side itself)
     w: int                    # window size around each focus position
     bs: int                   # block size of the prompt partition
     C: int                    # blocks kept by top-C
@@ -53,18 +53,8 @@ class Workload:
         return self.P + self.G
 
     @property
-    def k(self) -> int:
-        """k = floor(rho * n(t)), evaluated in double precision."""
-        return int(math.floor(float(self.rho) * self.n_t))
-
-    @property
     def nb(self) -> int:
         return -(-self.P // self.bs)
-
-    @property
-    def nq_max(self) -> int:
-        """Upper bound on |I_active|: k windows of w positions, never more than L."""
-        return min(self.k * self.w, self.L)
 
     @property
     def group(self) -> int:
