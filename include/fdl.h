@@ -139,9 +139,13 @@ fdl_status fdl_dense_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, i
  * exp(q_{h,i} . k_{g(h),j} * scale - lse_{h,i}), for every key j in [0, L); the
  * n_sinks keys of highest score form I_sink.
  *   q, q_idx, n_q, nq_max, k, ks, scale   as in fdl_dense_attention (same layer)
- *   lse        [B, Hq, nq_max] fp32, the lse output of fdl_dense_attention for these rows
+ *   lse        [B, Hq, nq_max] fp32, the lse output of fdl_dense_attention for these rows,
+ *              or NULL: the library then computes it with a dense attention pass over the
+ *              same rows and keys (its outputs discarded) inside the workspace
  *   sink_idx   [B, n_sinks] out, ascending
  *   scores     [B, L] fp32 out, or NULL
+ * Workspace: fdl_sink_identify_workspace_bytes, a size that covers lse = NULL (with lse
+ * given, only its first part is used).
  * Errors as fdl_dense_attention; n_sinks must lie in [0, L].
  */
 size_t fdl_sink_identify_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int L,
@@ -161,8 +165,10 @@ fdl_status fdl_sink_identify(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int
  * caller may compute them for every layer ahead of the layers that score them.
  *   k, ks   [B, Hkv, L, d] with strides ks (rows 0..P-1 are read)
  *   P, bs   prompt length (1 <= P <= L), block size (>= 1)
- *   kbar    [B, Hkv, nb, d] fp32 out, dense; each mean is summed in fp64 (exact for
- *           fp32/bf16 keys) and rounded once
+ *   kbar    [B, Hkv, nb, d] fp32 out, dense; each mean is summed in fp64 and rounded
+ *           once.  The sum is exact, hence the mean correctly rounded, while the binary
+ *           exponents of a block's nonzero keys span at most 29 - log2(bs) (fp32) or
+ *           45 - log2(bs) (bf16)
  * Errors: NULL pointers (FDL_ERR_NULL), bad shapes (FDL_ERR_SHAPE), as for the
  * other entry points.  No workspace.
  */
@@ -204,9 +210,15 @@ fdl_status fdl_block_score_topc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
  * (without it, keeping every block could not reproduce dense attention).  Each
  * key of I_p is attended once, however many of the three sets hold it.
  *   q, q_idx, n_q, nq_max, k, ks, v, vs, vt, vts, scale, o, os, lse   as in fdl_dense_attention
- *   sink_idx   [B, n_sinks] ascending, -1 entries ignored (fdl_sink_identify output)
- *   block_idx  [B, C] ascending, -1 entries ignored (fdl_block_score_topc output)
+ *   sink_idx   [B, n_sinks] positions (e.g. fdl_sink_identify output)
+ *   block_idx  [B, C] prompt block ids (e.g. fdl_block_score_topc output)
+ *              Each list is read as the set of its valid entries: positions in [0, L),
+ *              block ids in [0, ceil(P/bs)).  Entries outside that range (-1 padding
+ *              included) are ignored wherever they stand, repeated entries count once, and
+ *              the order is free (ascending lists, as the selections write them, take the
+ *              fast path; others are sorted on the device).
  *   P, bs      prompt length and block size used to select block_idx
+ * n_sinks and C above 4096 give FDL_ERR_UNSUPPORTED.
  */
 size_t fdl_sparse_attention_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int L,
                                             int P, int d, int nq_max, int n_sinks, int C,
@@ -244,10 +256,11 @@ fdl_status fdl_kv_refresh(fdl_dtype dtype, int B, int Hkv, int L, int d, const i
  * fdl_block_means_refresh - the block means after a KV refresh.
  * Summary page, "Method steps" (4): a block's mean depends on its own keys only, so
  * after fdl_kv_refresh only the blocks holding a refreshed prompt row (< P) change.
- * This recomputes exactly those entries of kbar [B, Hkv, nb, d] (fp32, as
- * fdl_block_means writes them, bit for bit) from the refreshed k, and leaves the
- * others as they are.  rows, n_rows, n_max as in fdl_kv_refresh; an ascending row
- * list recomputes each touched block once (any order gives the same result).
+ * This recomputes exactly those entries of kbar [B, Hkv, nb, d] (fp32) from the
+ * refreshed k, and leaves the others as they are.  Within the exponent range stated at
+ * fdl_block_means both passes sum exactly, so the entries equal what fdl_block_means
+ * writes, bit for bit.  rows, n_rows, n_max as in fdl_kv_refresh; an ascending row list
+ * recomputes each touched block once (any order gives the same result).
  * Errors: dtype, sizes, alignment as fdl_block_means; kbar NULL, or rows NULL with
  * n_max > 0, is FDL_ERR_NULL.
  */

@@ -84,6 +84,23 @@ AttnArgs attn_args(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, const voi
     return a;
 }
 
+// Workspace of fdl_sink_identify: the sink partial scores, then (used only when the caller
+// passes no lse) the lse and output rows of a dense attention pass and that pass's workspace.
+struct SinkWs {
+    size_t sink, lse, out, attn, total;
+};
+
+SinkWs sink_ws_layout(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, int nq_max) {
+    SinkWs w{};
+    w.sink = round_up(sink_workspace_bytes(B, Hkv, L), 256);
+    const size_t rows = static_cast<size_t>(B) * Hq * (nq_max > 0 ? nq_max : 0);
+    w.lse = round_up(rows * sizeof(float), 256);
+    w.out = round_up(rows * d * elem_size(dt), 256);
+    w.attn = nq_max > 0 ? round_up(plan_attention(dt, B, Hq, Hkv, d, nq_max, L, false).ws_bytes, 256) : 0;
+    w.total = w.sink + w.lse + w.out + w.attn;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,9 +167,8 @@ fdl_status fdl_dense_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int 
 }
 
 size_t fdl_sink_identify_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, int nq_max) {
-    (void)nq_max;
-    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK) return 0;
-    return sink_workspace_bytes(B, Hkv, L);
+    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 0) return 0;
+    return sink_ws_layout(dt, B, Hq, Hkv, L, d, nq_max).total;
 }
 
 fdl_status fdl_sink_identify(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d, const void* q,
@@ -165,9 +181,25 @@ fdl_status fdl_sink_identify(fdl_dtype dt, int B, int Hq, int Hkv, int L, int d,
     if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
     if ((st = check_tensor(q, qs, dt, d)) != FDL_OK) return st;
     if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
-    if (!lse || !sink_idx) return FDL_ERR_NULL;
+    if (!sink_idx) return FDL_ERR_NULL;
     if (n_sinks < 0 || n_sinks > L) return FDL_ERR_SHAPE;
-    if ((st = check_ws(ws, ws_bytes, sink_workspace_bytes(B, Hkv, L))) != FDL_OK) return st;
+    const SinkWs w = sink_ws_layout(dt, B, Hq, Hkv, L, d, nq_max);
+    if ((st = check_ws(ws, ws_bytes, lse ? w.sink : w.total)) != FDL_OK) return st;
+    if (!lse && nq_max > 0) {
+        // the log-sum-exp of the same rows over all L keys, from a dense pass whose outputs are
+        // discarded (the values do not enter the lse, so the keys serve as values)
+        uint8_t* base = static_cast<uint8_t*>(ws);
+        float* lse_ws = reinterpret_cast<float*>(base + w.sink);
+        void* o_ws = base + w.sink + w.lse;
+        const fdl_strides os = {static_cast<int64_t>(Hq) * nq_max * d, static_cast<int64_t>(nq_max) * d, d};
+        const fdl_strides none = {0, 0, 0};
+        AttnArgs a = attn_args(dt, B, Hq, Hkv, L, L, q, qs, q_idx, n_q, nq_max, k, ks, k, ks, nullptr, none, scale,
+                               d, o_ws, os, lse_ws, base + w.sink + w.lse + w.out);
+        a.sparse = 0;
+        const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, L, false);
+        if ((st = hip_status(launch_attention(dt, d, a, pl, stream))) != FDL_OK) return st;
+        lse = lse_ws;
+    }
     SinkArgs a{};
     a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
     a.q_idx = q_idx; a.n_q = n_q; a.nq_max = nq_max;
@@ -250,6 +282,7 @@ fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
     if (P < 0 || P > L || bs < 1 || C < 0 || n_sinks < 0) return FDL_ERR_SHAPE;
     if ((n_sinks > 0 && !sink_idx) || (C > 0 && !block_idx)) return FDL_ERR_NULL;
+    if (C > kPrepMaxIds || n_sinks > kPrepMaxIds) return FDL_ERR_UNSUPPORTED;
     const int64_t bound = sparse_key_bound(L, P, n_sinks, C, bs);
     if (bound > (1ll << 30)) return FDL_ERR_SHAPE;
     if (nq_max == 0) return FDL_OK;

@@ -125,6 +125,10 @@ __device__ __forceinline__ void write_zero_row(const AttnArgs& a, int b, int h, 
 }
 
 
+// Longest block and sink lists the key-list builder (attn_prep) brings to canonical form in
+// LDS; longer lists are rejected on the host.
+constexpr int kPrepMaxIds = 4096;
+
 // Keys of one sparse key set that the d = 128 kernel can map in LDS by itself.
 constexpr int kMapBlocks = 1024;
 constexpr int kMapSinks = 1024;

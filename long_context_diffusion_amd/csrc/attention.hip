@@ -44,17 +44,18 @@ namespace {
 
 // ------------------------------------------------------------------ key list
 
-constexpr int kPrepBlocksLds = 2048;   // selected-block ids staged in LDS by attn_prep
 constexpr int kPrepListWgs = 8;        // workgroups per sequence writing the key list
 
 // grid (B, kPrepListWgs + padding workgroups).  y < kPrepListWgs: write a slice of the
 // key list (y == 0 also appends the uncovered sinks and |I_p|); y >= kPrepListWgs:
-// zero padding rows when there is no key split.
+// zero padding rows when there is no key split.  The block and sink lists are brought to
+// canonical form first (valid ids, ascending, each once): at most kPrepMaxIds entries each.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d, bool build_list) {
     __shared__ int s_tmp[17];
-    __shared__ int s_carry;
-    __shared__ int s_blk[kPrepBlocksLds];
+    __shared__ int s_blk[kPrepMaxIds];
+    __shared__ int s_snk[kPrepMaxIds];
+    __shared__ int s_scr[kPrepMaxIds];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     if (blockIdx.y >= kPrepListWgs) {
@@ -79,20 +80,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d,
         return;
     }
     if (!a.sparse || !build_list) return;
-    const int32_t* blk_g = a.block_idx + static_cast<int64_t>(b) * a.C;
-    const bool in_lds = a.C <= kPrepBlocksLds;
-    int cnt = 0;
-    for (int c = tid; c < a.C; c += blockDim.x) {
-        const int v = blk_g[c];
-        if (in_lds) s_blk[c] = v;
-        cnt += v >= 0 ? 1 : 0;
-    }
-    int n_sel;
-    block_exclusive_sum(cnt, s_tmp, &n_sel);   // also orders the s_blk writes before the reads
-    n_sel = min(n_sel, a.nb);
-    const int32_t* blk = in_lds ? s_blk : blk_g;
+    const int n_sel = canonical_ids(a.block_idx + static_cast<int64_t>(b) * a.C, a.C, 0, a.nb, s_blk, s_scr, s_tmp);
     int n_blk = n_sel * a.bs;
-    if (n_sel > 0 && blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;  // short last block
+    if (n_sel > 0 && s_blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;  // short last block
     int32_t* list = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
     const int G = a.L - a.P;
     const int n_fixed = n_blk + G;
@@ -102,42 +92,18 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d,
         int key;
         if (pos < n_blk) {
             const int c = pos / a.bs;
-            // block ids come from fdl_block_score_topc; clamping keeps a malformed list in bounds
-            key = min(max(blk[c] * a.bs + (pos - c * a.bs), 0), a.L - 1);
+            key = s_blk[c] * a.bs + (pos - c * a.bs);
         } else {
             key = a.P + (pos - n_blk);
         }
         list[pos] = key;
     }
     if (blockIdx.y != 0) return;
-    if (tid == 0) s_carry = 0;
-    __syncthreads();
-    const int32_t* snk = a.sink_idx + static_cast<int64_t>(b) * a.n_sinks;
-    for (int s0 = 0; s0 < a.n_sinks; s0 += blockDim.x) {
-        const int s = s0 + tid;
-        int j = -1;
-        bool take = false;
-        if (s < a.n_sinks) {
-            j = snk[s];
-            take = j >= 0 && j < a.P && (s == 0 || snk[s - 1] != j);
-            if (take) {  // already in a selected block?  (selected blocks ascend)
-                const int target = j / a.bs;
-                int l = 0, h = n_sel;
-                while (l < h) {
-                    const int mid = (l + h) >> 1;
-                    if (blk[mid] < target) l = mid + 1; else h = mid;
-                }
-                take = !(l < n_sel && blk[l] == target);
-            }
-        }
-        int total;
-        const int off = block_exclusive_sum(take ? 1 : 0, s_tmp, &total) + s_carry;
-        if (take) list[n_fixed + off] = j;
-        __syncthreads();
-        if (tid == 0) s_carry += total;
-        __syncthreads();
-    }
-    if (tid == 0) a.n_keys[b] = n_fixed + s_carry;
+    int n_unc = canonical_ids(a.sink_idx + static_cast<int64_t>(b) * a.n_sinks, a.n_sinks, 0, a.P, s_snk, s_scr,
+                              s_tmp);
+    n_unc = filter_ids(s_snk, n_unc, s_scr, s_tmp, [&](int j) { return sorted_contains(s_blk, n_sel, j / a.bs); });
+    for (int i = tid; i < n_unc; i += blockDim.x) list[n_fixed + i] = s_snk[i];
+    if (tid == 0) a.n_keys[b] = n_fixed + n_unc;
 }
 
 // Merge of the key-range splits.  Each thread owns 8 elements of one output row

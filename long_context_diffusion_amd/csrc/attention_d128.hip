@@ -132,7 +132,6 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
     __shared__ int s_blk[MODE == kSparseLds ? kMapBlocks : 1];
     __shared__ int s_unc[MODE == kSparseLds ? kMapSinks : 1];
     __shared__ int s_tmp[17];
-    __shared__ int s_carry;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -174,51 +173,24 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         }
 
         // ---- key set of this sequence: n_keys positions; blocks first, then [P, L),
-        // then the sinks no selected block holds
+        // then the sinks no selected block holds.  The block and sink lists are taken in
+        // canonical form (valid ids only, ascending, each once; canonical_ids), sorted in LDS
+        // when they arrive in another order; the staging buffer of V rows is free here and
+        // serves as the sort's scratch.
         int n_keys = a.L, n_blk = 0, sink0 = a.L;
         const int32_t* klist = nullptr;
         if (MODE == kSparseLds) {
-            const int32_t* blk_g = a.block_idx + static_cast<int64_t>(b) * a.C;
-            int cnt = 0;
-            for (int c = tid; c < a.C; c += blockDim.x) {
-                const int v = blk_g[c];
-                s_blk[c] = v;
-                cnt += v >= 0 ? 1 : 0;
-            }
-            int n_sel;
-            block_exclusive_sum(cnt, s_tmp, &n_sel);
-            n_sel = min(n_sel, a.nb);
+            int* scratch = reinterpret_cast<int*>(s_raw);
+            const int n_sel = canonical_ids(a.block_idx + static_cast<int64_t>(b) * a.C, a.C, 0, a.nb, s_blk,
+                                            scratch, s_tmp);
             n_blk = n_sel * a.bs;
             if (n_sel > 0 && s_blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;
             sink0 = n_blk + (a.L - a.P);
-            if (tid == 0) s_carry = 0;
-            __syncthreads();
-            const int32_t* snk = a.sink_idx + static_cast<int64_t>(b) * a.n_sinks;
-            for (int s0 = 0; s0 < a.n_sinks; s0 += blockDim.x) {
-                const int s = s0 + tid;
-                int j = -1;
-                bool take = false;
-                if (s < a.n_sinks) {
-                    j = snk[s];
-                    take = j >= 0 && j < a.P && (s == 0 || snk[s - 1] != j);
-                    if (take) {
-                        const int target = j / a.bs;
-                        int lo = 0, hi = n_sel;
-                        while (lo < hi) {
-                            const int mid = (lo + hi) >> 1;
-                            if (s_blk[mid] < target) lo = mid + 1; else hi = mid;
-                        }
-                        take = !(lo < n_sel && s_blk[lo] == target);
-                    }
-                }
-                int total;
-                const int off = block_exclusive_sum(take ? 1 : 0, s_tmp, &total) + s_carry;
-                if (take) s_unc[off] = j;
-                __syncthreads();
-                if (tid == 0) s_carry += total;
-                __syncthreads();
-            }
-            n_keys = sink0 + s_carry;
+            int n_unc = canonical_ids(a.sink_idx + static_cast<int64_t>(b) * a.n_sinks, a.n_sinks, 0, a.P, s_unc,
+                                      scratch, s_tmp);
+            n_unc = filter_ids(s_unc, n_unc, scratch, s_tmp,
+                               [&](int j) { return sorted_contains(s_blk, n_sel, j / a.bs); });
+            n_keys = sink0 + n_unc;
         } else if (MODE == kSparseList) {
             n_keys = a.n_keys[b];
             klist = a.kv_list + static_cast<int64_t>(b) * a.key_cap;

@@ -13,8 +13,11 @@
 // many workgroups (a single CU pulls only about 20 GB/s from memory, so a pass that
 // one workgroup runs is bound by it):
 //   block_means        one streaming read of the prompt keys, 16 bytes per lane,
-//                      fp64 sums (exact for bf16/fp32 inputs), one rounding of the
-//                      mean to fp32.
+//                      fp64 sums, one rounding of the mean to fp32.  The fp64 sum of a
+//                      block is exact (so any order of the additions gives it) while the
+//                      binary exponents of its nonzero keys span at most 29 - log2(bs)
+//                      (fp32 keys) or 45 - log2(bs) (bf16 keys); beyond that range the
+//                      result can depend on the order in the last bit.
 //   block_dots         per (KV head g, 4096/d blocks): R is linear in the queries, so the
 //                      workgroup first sums the query rows of g's query heads (fp64),
 //                      qsum_g, and qsum_g . kbar_gb is that head's part of R_b.
@@ -105,8 +108,8 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
                 for (int e = 0; e < EPP; ++e) acc[c][e] += static_cast<double>(v[e]);
             }
     }
-    // the row groups of a wave (lanes NP apart) fold with shuffles; the fp64 sums of bf16 or
-    // fp32 keys are exact, so the order of the additions does not change them
+    // the row groups of a wave (lanes NP apart) fold with shuffles; within the exponent range
+    // stated at the top the fp64 sums are exact, so the order of the additions does not change them
 #pragma unroll
     for (int c = 0; c < kMeansBlocks; ++c)
 #pragma unroll

@@ -12,8 +12,10 @@
 //                        when the caller keeps one.
 //   block_means_refresh  64 list entries per workgroup: each entry that starts a block
 //                        in the (ascending) list has the workgroup recompute that
-//                        block's mean with an fp64 sum (exact for bf16 and fp32 keys,
-//                        so the result has the same single rounding as the full pass).
+//                        block's mean with an fp64 sum and one rounding, like the full
+//                        pass.  Both sums are exact while the exponents of a block's keys
+//                        span at most 29 - log2(bs) (fp32) or 45 - log2(bs) (bf16), and then
+//                        agree bit for bit although they add the rows in different orders.
 
 #include "ops.cuh"
 
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(co
         const int lo = blk * a.bs, hi = min(lo + a.bs, a.P);
         double s = 0.0;
         for (int j0 = lo + part; j0 < hi; j0 += 16 * parts) {
-            float x[16];   // 16 loads in flight, then the (exact) fp64 adds in row order
+            float x[16];   // 16 loads in flight, then the fp64 adds in row order
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int j = j0 + u * parts;

@@ -101,6 +101,96 @@ __device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
     return before + inc - x;
 }
 
+// Canonical form of an index list: the entries v of src[0, n) with lo <= v < hi, ascending and
+// each once, written to dst[0, m); returns m (the same in every thread).  Every thread of the
+// block calls it; blockDim.x is a multiple of 64.  The selections of this library write
+// strictly ascending lists with -1 padding after them: those cost one compaction pass and a
+// check.  Any other order, repeated entries and out-of-range entries anywhere in the list are
+// sorted (bitonic, in LDS) and de-duplicated.  dst (LDS) holds at least the next power of two
+// >= n ints, scratch (LDS) at least n ints; s_tmp at least 17 ints.
+__device__ inline int canonical_ids(const int32_t* src, int n, int lo, int hi, int* dst, int* scratch,
+                                    int* s_tmp) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int m = 0;
+    for (int base = 0; base < n; base += nt) {
+        const int i = base + tid;
+        const int v = i < n ? src[i] : lo - 1;
+        const bool ok = i < n && v >= lo && v < hi;
+        int tot;
+        const int off = block_exclusive_sum(ok ? 1 : 0, s_tmp, &tot);
+        if (ok) dst[m + off] = v;
+        m += tot;
+    }
+    __syncthreads();
+    int bad = 0;
+    for (int i = tid + 1; i < m; i += nt) bad += dst[i] <= dst[i - 1] ? 1 : 0;
+    int nbad;
+    block_exclusive_sum(bad, s_tmp, &nbad);
+    if (nbad == 0) return m;
+    int p2 = 1;
+    while (p2 < m) p2 <<= 1;
+    for (int i = m + tid; i < p2; i += nt) dst[i] = 0x7fffffff;
+    __syncthreads();
+    for (int k = 2; k <= p2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int t = tid; t < p2 / 2; t += nt) {
+                const int i = (t / j) * 2 * j + (t % j);   // bit j of i is clear; partner i + j
+                const int x = dst[i], y = dst[i + j];
+                if ((x > y) == ((i & k) == 0)) {
+                    dst[i] = y;
+                    dst[i + j] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int u = 0;
+    for (int base = 0; base < m; base += nt) {
+        const int i = base + tid;
+        const int v = i < m ? dst[i] : 0;
+        const bool keep = i < m && (i == 0 || dst[i - 1] != v);
+        int tot;
+        const int off = block_exclusive_sum(keep ? 1 : 0, s_tmp, &tot);
+        if (keep) scratch[u + off] = v;
+        u += tot;
+    }
+    __syncthreads();
+    for (int i = tid; i < u; i += nt) dst[i] = scratch[i];
+    __syncthreads();
+    return u;
+}
+
+// Keeps the entries of list[0, n) (LDS) for which drop(v) is false, in order; returns the new
+// length.  scratch (LDS) holds at least n ints.  Every thread of the block calls it.
+template <typename Drop>
+__device__ inline int filter_ids(int* list, int n, int* scratch, int* s_tmp, Drop drop) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int u = 0;
+    for (int base = 0; base < n; base += nt) {
+        const int i = base + tid;
+        const int v = i < n ? list[i] : 0;
+        const bool keep = i < n && !drop(v);
+        int tot;
+        const int off = block_exclusive_sum(keep ? 1 : 0, s_tmp, &tot);
+        if (keep) scratch[u + off] = v;
+        u += tot;
+    }
+    __syncthreads();
+    for (int i = tid; i < u; i += nt) list[i] = scratch[i];
+    __syncthreads();
+    return u;
+}
+
+// True when sorted[0, n) (ascending, LDS or global) holds x.
+__device__ __forceinline__ bool sorted_contains(const int* sorted, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sorted[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo < n && sorted[lo] == x;
+}
+
 // ------------------------------------------------------------------ top-k selection
 //
 // Selections keep the k entries with the largest ordered keys, the lower index

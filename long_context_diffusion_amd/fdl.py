@@ -345,7 +345,8 @@ def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, vt=None, 
                      workspace=None, stream=None):
     """Attention of the active queries over I_p only (fdl_sparse_attention).
 
-    sink_idx [B, n_sinks] and block_idx [B, C] int32 (ascending, -1 padded) or None;
+    sink_idx [B, n_sinks] and block_idx [B, C] int32 or None: each read as the set of its
+    valid entries (any order, repeats count once, -1 and out-of-range entries ignored);
     vt None or transpose_v(v).
     Returns (o [B, Hq, nq_max, d], lse or None).
     """

@@ -13,6 +13,12 @@ only; with overlap_means a sparse step computes them for every sparse layer on a
 second stream, one event per layer, while the layers before it attend on the
 caller's stream, and each layer's scoring waits for its own means.  Without it,
 each layer computes its means right before scoring them.
+
+cached_step is the same step over an approximate KV cache ("Prerequisites",
+approximate KV cache): every layer first writes the recomputed keys and values
+of U(t) = I_active into its cache, then recomputes only the block means those
+rows touch (the means of the other blocks are kept from the previous step), so
+the per-layer scan of the prompt keys is skipped.
 """
 from __future__ import annotations
 
@@ -124,6 +130,48 @@ class StepRunner:
                 run("sparse", lambda: self.attend(l, q, k, v, vt))
         if overlap:
             main.wait_stream(self.side)
+
+    def init_means(self, ks):
+        """Block means of every sparse layer from its whole cache (after a block-entry step),
+        the state cached_step keeps up to date."""
+        for l, kb in self.kbar.items():
+            F.block_means(ks[l], self.P, self.bs, out=kb)
+
+    def cached_step(self, conf, mask, qs, ks, vs, k_new, v_new, hooks=None, vts=None):
+        """A non-block-entry step over an approximate KV cache.
+
+        k_new[l], v_new[l] ([B, Hkv, nq_max, d]) hold layer l's recomputed keys and values of
+        the active rows, row i for active_idx[b, i].  Layer l's new rows come from layer l's
+        own forward pass, which follows layer l-1's attention, so each layer refreshes its cache
+        (and V^T, when kept), and a sparse layer its touched block means, on the caller's
+        stream right before it attends.  self.kbar must hold the means of the cache as it was
+        before the step (init_means, or the previous cached step).  Stage names for `hooks`:
+        "pcgi", "refresh", "dense", "sinks", "blocks", "sparse"."""
+        def run(name, fn):
+            h = hooks.get(name) if hooks else None
+            if h:
+                h[0]()
+            fn()
+            if h:
+                h[1]()
+        run("pcgi", lambda: self.pcgi(conf, mask))
+        for l in range(self.layers):
+            q, k, v = qs[l], ks[l], vs[l]
+            vt = vts[l] if vts is not None else None
+
+            def refresh():
+                F.kv_refresh(self.active, k_new[l], v_new[l], k, v, n_rows=self.n_active, vt=vt)
+                if l >= self.l_dense and self.C:
+                    F.block_means_refresh(k, self.P, self.bs, self.active, self.kbar[l], n_rows=self.n_active)
+            run("refresh", refresh)
+            if l < self.l_dense:
+                run("dense", lambda: self.dense_layer(l, q, k, v, vt))
+                if l == self.l_dense - 1:
+                    run("sinks", lambda: self.sinks_at(q, k))
+            else:
+                if self.C:
+                    run("blocks", lambda: self.score_blocks(l, q))
+                run("sparse", lambda: self.attend(l, q, k, v, vt))
 
     def dense_refresh(self, qs, ks, vs, outs, vts=None):
         """A block-entry step: every query row of every layer attends to all L keys."""

@@ -5,13 +5,16 @@ score lies within 1e-5 * |cut| of the oracle's cut score (the k-th / C-th
 value): an fp32 or fp64 rounding difference can legitimately reorder such
 near-ties.  PCGI gets no band (its keys are compared exactly on both sides).
 Outputs: max abs error <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs (fp32
-accumulation).  A relative self-check (max abs error / max |reference|) is
-reported as well and held to 1e-5 (fp32) and 2e-2 (bf16).
+accumulation).  A relative check (max abs error / max |reference|) is held to
+1e-5 (fp32) and 1e-2 (bf16, about 2.5 units in the last place of the largest
+output): the absolute bf16 bound alone is larger than the outputs themselves
+(|O| is a few 1e-3 with the workloads' sigma = 1/8), so the relative one is the
+bound that bites.
 """
 import numpy as np
 
 ABS_TOL = {"f32": 1e-5, "bf16": 2e-2}
-REL_TOL = {"f32": 1e-5, "bf16": 2e-2}
+REL_TOL = {"f32": 1e-5, "bf16": 1e-2}
 TIE_BAND = 1e-5
 
 

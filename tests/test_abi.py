@@ -71,8 +71,12 @@ def test_workspace_sizes():
     assert n >= 2 * 32 * 1024 * (128 + 2) * 4
     assert lib.fdl_sparse_attention_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128,
                                                      1024, 16, 64, 128) > 0
+    # sinks: the partial scores, then room for the lse pass it runs when given no lse (lse and
+    # output rows of the active queries, and that dense pass's own workspace)
+    def r256_(x):
+        return -(-x // 256) * 256
     assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 128, 1024) == \
-        (32 * 32768 + 32768) * 4
+        r256_((32 * 32768 + 32768) * 4) + r256_(32 * 1024 * 4) + r256_(32 * 1024 * 128 * 2) + cap
     # block scoring: each KV head's part of R, R, and room for the block means when they are
     # computed from the keys; the number of query rows does not change it
     nb = 252
@@ -152,8 +156,13 @@ def test_sparse_and_sink_and_block_validation():
     st = S(4 * 256 * 128, 256 * 128, 128)
     # sparse: the key list always needs a workspace
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
-                                    FAKE, st, NULL, S(0, 0, 0), FAKE, 5000, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0,
+                                    FAKE, st, NULL, S(0, 0, 0), FAKE, 4000, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0,
                                     None) == 5
+    # sparse: sink or block lists longer than the device canonicalises (4096 entries)
+    for n_sinks, C in ((4097, 2), (4, 4097)):
+        assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
+                                        FAKE, st, NULL, S(0, 0, 0), FAKE, n_sinks, FAKE, C, 64, 0.0, FAKE, st, NULL,
+                                        NULL, 0, None) == 7
     # sparse: P > L, bs < 1, block list missing
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 300, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
                                     FAKE, st, NULL, S(0, 0, 0), FAKE, 4, FAKE, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 2
@@ -162,8 +171,13 @@ def test_sparse_and_sink_and_block_validation():
     assert lib.fdl_sparse_attention(F.FDL_BF16, 1, 4, 4, 256, 192, 128, FAKE, st, NULL, NULL, 64, FAKE, st,
                                     FAKE, st, NULL, S(0, 0, 0), FAKE, 4, NULL, 2, 64, 0.0, FAKE, st, NULL, NULL, 0, None) == 1
     # sinks: lse and output required, n_sinks within [0, L], workspace
+    # no lse: the library computes it, in a larger workspace than the one the scores alone need
+    small = (4 * 256 + 256) * 4
+    assert lib.fdl_sink_identify_workspace_bytes(F.FDL_BF16, 1, 4, 4, 256, 128, 64) > small
     assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
-                                 NULL, 4, FAKE, NULL, FAKE, 1 << 20, None) == 1
+                                 NULL, 4, FAKE, NULL, FAKE, small, None) == 5
+    assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
+                                 FAKE, 4, NULL, NULL, FAKE, 1 << 20, None) == 1
     assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,
                                  FAKE, 257, FAKE, NULL, FAKE, 1 << 20, None) == 2
     assert lib.fdl_sink_identify(F.FDL_BF16, 1, 4, 4, 256, 128, FAKE, st, NULL, NULL, 64, FAKE, st, 0.0,

@@ -56,8 +56,9 @@ def test_kv_and_means_refresh_small(dtype, d, with_vt):
 
 
 def test_refresh_at_32k_with_active_rows():
-    """U(t) = I_active of the 32K step; then scoring and sparse attention read the refreshed
-    cache: the means equal the oracle's on every touched block and stay as they were elsewhere."""
+    """U(t) = I_active of the 32K step: the refreshed rows and V^T land where the oracle puts
+    them, and the means equal the oracle's on every touched block and stay as they were
+    elsewhere.  (Scoring and attention over a refreshed cache: test_cached_step_*.)"""
     import gpu_cases
     from workloads import configs, synth
     wl = configs.CTX32K_STACK
@@ -90,3 +91,108 @@ def test_refresh_at_32k_with_active_rows():
     untouched = np.setdiff1d(np.arange(wl.nb), touched)
     assert torch.equal(kbar[0][:, untouched], kbar_old[0][:, untouched])
     gpu_cases.log(f"refresh: {na} rows, {len(touched)} prompt blocks touched")
+
+
+# ------------------------------------------------------------------ the cached-means step
+
+def _cached_setup(layers=3, l_dense=1):
+    """The 8K workload cut to a few layers, its inputs, and per-layer new K/V rows."""
+    import dataclasses
+    from long_context_diffusion_amd.step import StepRunner
+    from workloads import configs, synth
+    wl = dataclasses.replace(configs.CTX8K_MHA, layers=layers, l_dense=l_dense)
+    conf, mask = synth.step_inputs(wl)
+    qs, ks, vs = [], [], []
+    for l in range(wl.layers):
+        k, v = synth.make_kv(wl, l, DEV)
+        ks.append(k)
+        vs.append(v)
+        qs.append(synth.make_q(wl, l, 0, DEV))
+
+    def runner():
+        return StepRunner(B=wl.B, L=wl.L, P=wl.P, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, dtype=torch.bfloat16,
+                          n_t=wl.n_t, rho=wl.rho, w=wl.w, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
+                          layers=wl.layers, l_dense=wl.l_dense, scale=wl.scale, device=DEV)
+    run = runner()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(88)
+    shp = (wl.B, wl.Hkv, run.nq_max, wl.d)
+    knew = [(torch.randn(shp, generator=g, device=DEV) * wl.sigma).to(torch.bfloat16) for _ in range(wl.layers)]
+    vnew = [(torch.randn(shp, generator=g, device=DEV) * wl.sigma).to(torch.bfloat16) for _ in range(wl.layers)]
+    return wl, run, runner, torch.from_numpy(conf).to(DEV), torch.from_numpy(mask).to(DEV), qs, ks, vs, knew, vnew, \
+        (conf, mask)
+
+
+def test_cached_step_against_full_means_and_oracle():
+    """A cached-means step (each layer: refresh its cache rows, refresh the touched block means,
+    score from the kept means, attend) gives bit for bit what a full-means step gives on the
+    refreshed caches, and the oracle's refresh -> block means -> relevance -> top-C -> sparse
+    attention on a sampled layer."""
+    import gpu_cases
+    from parity import assert_close, assert_selection, valid
+    wl, run, runner, conf, mask, qs, ks, vs, knew, vnew, host = _cached_setup()
+    ks0 = [synth_f64(k) for k in ks]
+    vs0 = [synth_f64(v) for v in vs]
+    vts = [F().transpose_v(v) for v in vs]
+    run.init_means(ks)
+    run.cached_step(conf, mask, qs, ks, vs, knew, vnew, vts=vts)
+    torch.cuda.synchronize()
+    # the full-means step on the caches the cached step left behind
+    full = runner()
+    full.sparse_step(conf, mask, qs, ks, vs, vts=vts)
+    torch.cuda.synchronize()
+    for l in range(wl.l_dense, wl.layers):
+        assert torch.equal(run.kbar[l], full.kbar[l]), f"kept means differ from a full pass, layer {l}"
+        assert torch.equal(run.blocks[l], full.blocks[l]), f"blocks differ, layer {l}"
+    for l in range(wl.layers):
+        assert torch.equal(run.out[l], full.out[l]), f"outputs differ, layer {l}"
+    assert torch.equal(run.sinks, full.sinks)
+    for l in range(wl.layers):
+        assert torch.equal(vts[l], vs[l].transpose(2, 3)), f"V^T not refreshed, layer {l}"
+    # oracle: the refreshed cache of the last layer and everything downstream of it
+    conf_h, mask_h = host
+    actives = gpu_cases.check_pcgi(wl, conf_h, mask_h, run.focus, run.n_focus, run.active, run.n_active)
+    act = actives[0]
+    na = len(act)
+    l = wl.layers - 1
+    K2, V2 = O.kv_refresh(ks0[l][0], vs0[l][0], act, f64(knew[l][0])[:, :na], f64(vnew[l][0])[:, :na])
+    assert np.array_equal(K2, f64(ks[l][0])) and np.array_equal(V2, f64(vs[l][0])), "refreshed cache"
+    Qa = synth_f64(qs[l])[0][:, act]
+    kb = O.block_means(K2, wl.P, wl.bs)
+    assert np.array_equal(run.kbar[l][0].cpu().numpy(), kb.astype(np.float32)), "kept means vs oracle"
+    R = O.block_relevance(Qa, kb, wl.scale)
+    blk = run.blocks[l][0, : wl.C].cpu().numpy()
+    assert_selection(blk, O.top_blocks(R, wl.C), R, "cached blocks")
+    I_p = O.key_set(valid(run.sinks[0].cpu().numpy()), valid(blk), wl.bs, wl.P, wl.L)
+    o_ref, _ = O.sparse_attention(Qa, K2, V2, I_p, wl.scale)
+    err = assert_close(synth_f64(run.out[l][0, :, :na]), o_ref, "bf16", "cached sparse O")
+    gpu_cases.log(f"cached step: {na} refreshed rows, max abs err {err[0]:.3e}, rel {err[1]:.3e}")
+
+
+def test_cached_step_graph_replays():
+    """The cached step captured in a HIP graph: every replay (the refresh rewrites the same rows,
+    so the step is repeatable) equals the eager step, with eager work between replays."""
+    wl, run, runner, conf, mask, qs, ks, vs, knew, vnew, _ = _cached_setup()
+    vts = [F().transpose_v(v) for v in vs]
+    run.init_means(ks)
+    run.cached_step(conf, mask, qs, ks, vs, knew, vnew, vts=vts)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in run.out] + [b.clone() for b in run.blocks] + [run.sinks.clone()]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run.cached_step(conf, mask, qs, ks, vs, knew, vnew, vts=vts)
+    for rep in range(3):
+        for o in run.out:
+            o.fill_(5.0)
+        for b in run.blocks:
+            b.fill_(-3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in run.out] + [b.clone() for b in run.blocks] + [run.sinks.clone()]
+        for a, b in zip(eager, got):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager cached step"
+
+
+def synth_f64(t):
+    return f64(t)
