@@ -38,7 +38,7 @@ struct AttnArgs {
     int key_cap;           // row stride of kv_list (upper bound on |I_p|)
     int32_t* kv_list;      // [B, key_cap] keys of I_p (sparse), built by attn_prep
     int32_t* n_keys;       // [B] |I_p| (sparse)
-    float* part_o;         // [B*Hq*nq_max][n_splits][d] unnormalised outputs (bf16 when dyn)
+    float* part_o;         // [B*Hq*nq_max][n_splits][d] unnormalised fp32 outputs
     float* part_ml;        // [B*Hq*nq_max][n_splits][2] running max (log2 domain) and sum
 };
 

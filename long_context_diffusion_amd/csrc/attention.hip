@@ -162,22 +162,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
                     const int64_t idx = base + (s0 + j) * step;
                     m[j] = a.part_ml[2 * idx];
                     l[j] = a.part_ml[2 * idx + 1];
-                    if (a.dyn) {
-                        // the persistent bf16 kernel stores its partial rows in bf16
-                        const u32x4 w = *reinterpret_cast<const u32x4*>(
-                            reinterpret_cast<const uint16_t*>(a.part_o) + idx * D + kMergeEpt * sub);
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            x[j][0][2 * e] = bf16lo(w[e]);
-                            x[j][0][2 * e + 1] = bf16hi(w[e]);
-                            x[j][1][2 * e] = bf16lo(w[2 + e]);
-                            x[j][1][2 * e + 1] = bf16hi(w[2 + e]);
-                        }
-                    } else {
-                        const float* po = a.part_o + idx * D + kMergeEpt * sub;
-                        x[j][0] = *reinterpret_cast<const f32x4*>(po);
-                        x[j][1] = *reinterpret_cast<const f32x4*>(po + 4);
-                    }
+                    const float* po = a.part_o + idx * D + kMergeEpt * sub;
+                    x[j][0] = *reinterpret_cast<const f32x4*>(po);
+                    x[j][1] = *reinterpret_cast<const f32x4*>(po + 4);
                 }
             }
             float Mg = M;

@@ -33,86 +33,11 @@
 //     (exp2 units), so rescaling the accumulators is rare; the final
 //     normalisation is exact either way.
 
-#include "attention.cuh"
+#include "attention_tiles.cuh"
 
 namespace fdl {
 
 namespace {
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kRowB = 256;           // bytes per K/V row in LDS
-constexpr int kTileB = 64 * kRowB;   // one 64-key tile: 16 KB
-constexpr float kSlack = 8.0f;       // max growth (log2 units) tolerated before a rescale
-
-// key sets: every key of [0, L); I_p mapped from LDS copies of its parts; I_p read
-// from the list attn_prep wrote (parts too large for LDS)
-enum KeyMode { kDense = 0, kSparseLds = 1, kSparseList = 2 };
-
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
-// Row r of a K tile (and of the S^T accumulator) holds key position vt_row(r) of the
-// tile, where vt_row swaps bits 2 and 3.  A lane's P fragment for 16-key chunk kc holds
-// S^T rows 16kc + 8(j/4) + 4hf + j%4, j = 0..7, which are then key positions
-// 16kc + 8hf + j: so slot s (0..63) of a V^T row is simply key position s, and 8
-// consecutive keys of one d fill one 16-byte chunk.
-// V^T tile: 128 rows (d) of 128 bytes.  Chunk c of row d sits at c ^ vt_swz(d), chosen by measuring the LDS bank-conflict
-// counter over candidate swizzles on gfx950: the fragment reads are conflict-free and the
-// transposing stores (rows 8 apart in one instruction) 2-way; with bits 1-3 of d alone
-// the stores are 8-way.
-__host__ __device__ constexpr int vt_row(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
-__host__ __device__ constexpr int vt_swz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
-__host__ __device__ constexpr int vt_off(int d, int s) { return d * 128 + 16 * ((s >> 3) ^ vt_swz(d)) + 2 * (s & 7); }
-
-// The two writers of a V^T tile compute vt_off in closed forms; both are checked here
-// against it at compile time.  The V^T DMA: instruction m, lane l writes LDS bytes
-// 1024 m + 16 l, the chunk of row d = 8 m + l / 8 that holds slots 8 ((l % 8) ^ vt_swz(d)) + 0..7.
-// The transposing store of thread t: word e at A(t) ^ (128 e + 16 (e / 2)), d = 8 (t % 16) + e,
-// slot vt_row(2 (t / 16)).
-constexpr bool vt_writers_match_layout() {
-    for (int m = 0; m < 16; ++m)
-        for (int l = 0; l < 64; ++l) {
-            const int d = 8 * m + l / 8;
-            if (vt_off(d, 8 * ((l % 8) ^ vt_swz(d))) != 1024 * m + 16 * l) return false;
-        }
-    for (int t = 0; t < 512; ++t) {
-        const int c8 = t & 15, sl = vt_row(2 * (t >> 4));
-        const int A = 1024 * c8 + 2 * (sl & 7) + 16 * (((sl >> 3) ^ (4 * (c8 & 1)) ^ (c8 >> 1)) & 7);
-        for (int e = 0; e < 8; ++e)
-            if ((A ^ (128 * e + 16 * (e >> 1))) != vt_off(8 * c8 + e, sl)) return false;
-    }
-    return true;
-}
-static_assert(vt_writers_match_layout(), "V^T writers disagree with vt_off");
-
-
-// floor(n / d) for 0 <= n < 2^30 and d >= 1, with m = ceil(2^32 / d) for d >= 2.
-__device__ __forceinline__ int div_magic(int n, int d, uint32_t m) {
-    if (d == 1) return n;
-    uint32_t q = __umulhi(static_cast<uint32_t>(n), m);   // floor(n/d) or one more
-    if (q * static_cast<uint32_t>(d) > static_cast<uint32_t>(n)) --q;
-    return static_cast<int>(q);
-}
-
-// Workgroup barrier that leaves this wave's newest `keep` loads in flight: LDS reads
-// have returned and every older load (LDS DMA included) has landed.  A plain
-// __syncthreads() would also wait for the newest loads: its release fence drains
-// every outstanding memory operation.
-template <int keep>
-__device__ __forceinline__ void barrier_keep() {
-    static_assert(keep >= 0 && keep < 16, "vmcnt field");
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(keep | (7 << 4));   // vmcnt(keep) expcnt(7) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// The value this lane's partner (lane ^ 32) holds.
-__device__ __forceinline__ float xhalf(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
 
 template <int MODE>
 __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
@@ -132,6 +57,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
     __shared__ int s_blk[MODE == kSparseLds ? kMapBlocks : 1];
     __shared__ int s_unc[MODE == kSparseLds ? kMapSinks : 1];
     __shared__ int s_tmp[17];
+    __shared__ uint64_t s_tmp64[8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -156,41 +82,50 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         const int rows_valid = a.Gq * nq;
 
         // ---- Q fragments (B operand of S^T = K Q^T): d = 16c + 8hf .. +7 of the row.  Their
-        // loads go out before the key map is built, so both round trips overlap.
+        // loads go out before the key map is built, so both round trips overlap.  With a
+        // key map to build, the rows go by DMA into the idle V^T tile buffers (wave wv's 32
+        // rows at its epilogue staging area, chunk c of row r at slot c ^ (r & 15)) and reach
+        // registers after the map is done, so no registers are held across the map.
         const int p = u.qt * kD128Rows + wv * 32 + col;   // 8 waves x 32 rows
         const bool row_ok = p < rows_valid;
         bf16x8 qf[NQC];
-        {
-            const int rr = row_ok ? p / a.Gq : 0;
-            const int hh = row_ok ? g * a.Gq + p % a.Gq : g * a.Gq;
+        uint8_t* qstage = (wv < 2 ? s_t0 : wv < 4 ? s_t1 : wv < 6 ? s_t2 : s_t3) + (wv & 1) * 8192;
+        auto q_row_ptr = [&](int pr) __attribute__((always_inline)) {
+            const bool ok = pr < rows_valid;
+            const int rr = ok ? pr / a.Gq : 0;
+            const int hh = ok ? g * a.Gq + pr % a.Gq : g * a.Gq;
             int phys = a.q_idx ? a.q_idx[static_cast<int64_t>(b) * a.nq_max + rr] : rr;
             phys = max(phys, 0);
-            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh +
-                                   static_cast<int64_t>(phys) * a.qsr;
+            return static_cast<const uint16_t*>(a.q) + b * a.qsb + hh * a.qsh + static_cast<int64_t>(phys) * a.qsr;
+        };
+        if (MODE == kSparseLds) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                const uint16_t* src = q_row_ptr(u.qt * kD128Rows + wv * 32 + r) + 8 * ((lane & 15) ^ (r & 15));
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)(qstage + 1024 * i), 16, 0, 0);
+            }
+        } else {
+            const uint16_t* qrow = q_row_ptr(p);
 #pragma unroll
             for (int c = 0; c < NQC; ++c)
                 qf[c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * c + 8 * hf));
         }
 
-        // ---- key set of this sequence: n_keys positions; blocks first, then [P, L),
-        // then the sinks no selected block holds.  The block and sink lists are taken in
-        // canonical form (valid ids only, ascending, each once; canonical_ids), sorted in LDS
-        // when they arrive in another order; the staging buffer of V rows is free here and
-        // serves as the sort's scratch.
+        // ---- key set of this sequence (build_key_map): blocks, then [P, L), then the sinks
+        // no selected block holds; the V-row staging buffer is the sort scratch
         int n_keys = a.L, n_blk = 0, sink0 = a.L;
         const int32_t* klist = nullptr;
         if (MODE == kSparseLds) {
-            int* scratch = reinterpret_cast<int*>(s_raw);
-            const int n_sel = canonical_ids(a.block_idx + static_cast<int64_t>(b) * a.C, a.C, 0, a.nb, s_blk,
-                                            scratch, s_tmp);
-            n_blk = n_sel * a.bs;
-            if (n_sel > 0 && s_blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;
-            sink0 = n_blk + (a.L - a.P);
-            int n_unc = canonical_ids(a.sink_idx + static_cast<int64_t>(b) * a.n_sinks, a.n_sinks, 0, a.P, s_unc,
-                                      scratch, s_tmp);
-            n_unc = filter_ids(s_unc, n_unc, scratch, s_tmp,
-                               [&](int j) { return sorted_contains(s_blk, n_sel, j / a.bs); });
-            n_keys = sink0 + n_unc;
+            build_key_map<512>(a, b, s_blk, s_unc, s_tmp, s_tmp64, reinterpret_cast<int*>(s_raw), n_blk, sink0, n_keys);
+            // the Q rows have landed in this wave's staging area: fragments to registers, then
+            // every wave is done with the staging areas before tile loads overwrite them
+            __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+            for (int c = 0; c < NQC; ++c)
+                qf[c] = *reinterpret_cast<const bf16x8*>(qstage + col * kRowB + 16 * ((2 * c + hf) ^ (col & 15)));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         } else if (MODE == kSparseList) {
             n_keys = a.n_keys[b];
             klist = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
@@ -474,7 +409,8 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 mx = fmaxf(mx, xhalf(mx));
                 const float mc = mx * a.sl2;
                 const bool need = mc > m_run + kSlack;
-                if (__any(need)) {
+                // a rare, real branch: if-converted, the 64 multiplies ran on every tile
+                if (__builtin_expect(__any(need), 0)) {
                     const float m_new = need ? mc : m_run;
                     const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
@@ -551,17 +487,18 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             __builtin_amdgcn_s_waitcnt(0);   // drain the loads past the split before LDS is reused
         }
 
-        // ---- epilogue: normalised rows (one split) or unnormalised partials, in bf16.
-        // Each wave stages its 32 rows in LDS (row i at 256 i, 16-byte chunk c at slot
-        // c ^ (i & 15): conflict-free both ways), then stores whole rows, 4 rows (1 KB)
-        // per instruction.  Stored straight from the accumulator layout, every
-        // instruction would write 16-byte pieces of 32 different rows, which drains
-        // several times slower.  The loop ended on a barrier that every wave reached
-        // with its loads landed, so no tile buffer is in use any more.
+        // ---- epilogue: normalised rows in bf16 (one split) or unnormalised fp32 partials.
+        // Each wave stages its 32 rows in LDS, then stores whole rows: bf16 rows (256 B, chunk
+        // c of row i at slot c ^ (i & 15)) 4 per instruction, fp32 rows (512 B, chunk c at
+        // slot c ^ (i & 31)) 2 per instruction.  Stored straight from the accumulator layout,
+        // every instruction would write 16-byte pieces of 32 different rows, which drains
+        // several times slower.  The loop ended on a barrier that every wave reached with its
+        // loads landed, so no tile buffer is in use any more.
         const float l_tot = l_run + xhalf(l_run);
-        {
+        const int row0 = u.qt * kD128Rows + wv * 32;   // logical row of this wave's row 0
+        if (n_splits == 1) {
             uint8_t* stage = (wv < 2 ? s_t0 : wv < 4 ? s_t1 : wv < 6 ? s_t2 : s_t3) + (wv & 1) * 8192;
-            const float sc = n_splits > 1 ? 1.0f : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+            const float sc = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             // The lane id goes through an empty asm, so the per-lane offsets below are formed
             // here rather than hoisted above the tile loop (where they would stay live and spill).
             int el = lane;
@@ -579,8 +516,6 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                     *reinterpret_cast<u32x2*>(stage + (wbase ^ (16 * (4 * db + qd)))) = w;
                 }
             const int cc = el & 15;
-            const int row0 = u.qt * kD128Rows + wv * 32;   // logical row of this wave's row 0
-            const int64_t pidx0 = n_splits > 1 ? d128_part_index(a, nqt_max, n_splits, b, g, u.split, row0) : 0;
             // row i = 4k + lane/16: (i & 15) = 4 (k & 3) + lane/16
             const int rbase = 256 * (el >> 4) + ((16 * cc) ^ (16 * (el >> 4)));
 #pragma unroll
@@ -588,17 +523,35 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 const int i = 4 * k + (el >> 4);
                 const int pr = row0 + i;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stage + 1024 * k + (rbase ^ (64 * (k & 3))));
-                if (n_splits == 1) {
-                    if (pr < rows_all) {
-                        const int rr = pr / a.Gq;
-                        const int hh = g * a.Gq + pr % a.Gq;
-                        uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + hh * a.osh + static_cast<int64_t>(rr) * a.osr;
-                        *reinterpret_cast<u32x4*>(orow + 8 * cc) = pr < rows_valid ? v : u32x4{0u, 0u, 0u, 0u};
-                    }
-                } else if (pr < rows_valid) {
-                    uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (pidx0 + i) * 128;
-                    *reinterpret_cast<u32x4*>(po + 8 * cc) = v;
+                if (pr < rows_all) {
+                    const int rr = pr / a.Gq;
+                    const int hh = g * a.Gq + pr % a.Gq;
+                    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.osb + hh * a.osh + static_cast<int64_t>(rr) * a.osr;
+                    *reinterpret_cast<u32x4*>(orow + 8 * cc) = pr < rows_valid ? v : u32x4{0u, 0u, 0u, 0u};
                 }
+            }
+        } else {
+            uint8_t* stage = wv == 0 ? s_t0 : wv == 1 ? s_t1 : wv == 2 ? s_t2 : wv == 3 ? s_t3 :
+                             wv == 4 ? s_k0 : wv == 5 ? s_k1 : wv == 6 ? s_k2 : s_k3;
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            const int i0 = el & 31;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    // d = 32 db + 8 qd + 4 hf .. +3: 16-byte chunk 8 db + 2 qd + hf of row i0
+                    const int c = 8 * db + 2 * qd + (el >> 5);
+                    const f32x4 w = {acc[db][4 * qd + 0], acc[db][4 * qd + 1], acc[db][4 * qd + 2], acc[db][4 * qd + 3]};
+                    *reinterpret_cast<f32x4*>(stage + 512 * i0 + 16 * (c ^ i0)) = w;
+                }
+            const int64_t pidx0 = d128_part_index(a, nqt_max, n_splits, b, g, u.split, row0);
+            const int cc = el & 31;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int i = 2 * k + (el >> 5);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(stage + 512 * i + 16 * (cc ^ i));
+                if (row0 + i < rows_valid) *reinterpret_cast<f32x4*>(a.part_o + (pidx0 + i) * 128 + 4 * cc) = v;
             }
         }
         // softmax statistics, one lane per row

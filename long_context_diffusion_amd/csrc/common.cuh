@@ -101,6 +101,19 @@ __device__ inline int block_exclusive_sum(int x, int* s_tmp, int* total) {
     return before + inc - x;
 }
 
+// Sum of a 64-bit value over the block (blockDim.x a multiple of 64, <= 512); every thread
+// gets the total.  s_tmp holds at least blockDim.x / 64 values.  Two barriers.
+__device__ inline uint64_t block_sum_u64(uint64_t x, uint64_t* s_tmp) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[threadIdx.x / kWave] = x;
+    __syncthreads();
+    uint64_t tot = 0;
+    for (int w = 0; w < static_cast<int>(blockDim.x) / kWave; ++w) tot += s_tmp[w];
+    __syncthreads();
+    return tot;
+}
+
 // Canonical form of an index list: the entries v of src[0, n) with lo <= v < hi, ascending and
 // each once, written to dst[0, m); returns m (the same in every thread).  Every thread of the
 // block calls it; blockDim.x is a multiple of 64.  The selections of this library write
