@@ -204,6 +204,24 @@ fdl_status fdl_block_score_topc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * fdl_block_score_topc_noalloc - fdl_block_score_topc for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, results and errors as fdl_block_score_topc, without ws and
+ * ws_bytes: the workspace is a device array inside the library, one per GPU, of
+ * fdl_block_score_topc_noalloc_max_bytes() bytes (8 MiB), held until the process ends.
+ * A call whose fdl_block_score_topc_workspace_bytes exceeds it returns FDL_ERR_WORKSPACE;
+ * a failed lookup of the array returns FDL_ERR_HIP.  It allocates nothing.  Every call on
+ * one GPU uses that GPU's array: calls that overlap on one GPU (different streams, or
+ * unordered host threads) race.
+ */
+size_t fdl_block_score_topc_noalloc_max_bytes(void);
+fdl_status fdl_block_score_topc_noalloc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int P, int d,
+                                        const void* q, fdl_strides qs, const int32_t* q_idx,
+                                        const int32_t* n_q, int nq_max,
+                                        const void* k, fdl_strides ks, float scale, int bs, int C,
+                                        int32_t* block_idx, double* R, float* kbar, hipStream_t stream);
+
+/*
  * fdl_sparse_attention - attention of the active queries over I_p only.
  * Summary page, "Method steps" (5): I_p is the union of the sinks and the
  * selected prompt blocks; this library also adds the generation region [P, L)

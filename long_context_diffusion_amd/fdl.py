@@ -31,6 +31,7 @@ EXPORTS = (
     "fdl_block_means", "fdl_block_score_topc_workspace_bytes", "fdl_block_score_topc",
     "fdl_sparse_attention_workspace_bytes", "fdl_sparse_attention",
     "fdl_kv_refresh", "fdl_block_means_refresh",
+    "fdl_block_score_topc_noalloc_max_bytes", "fdl_block_score_topc_noalloc",
 )
 
 
@@ -68,6 +69,9 @@ _SIGS = {
     "fdl_kv_refresh": (_I, [_I, _I, _I, _I, _I, _P, _P, _I, _P, Strides, _P, Strides, _P, Strides, _P, Strides,
                             _P, Strides, _P]),
     "fdl_block_means_refresh": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _I, _P, _P, _I, _P, _P]),
+    "fdl_block_score_topc_noalloc_max_bytes": (_SZ, []),
+    "fdl_block_score_topc_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
+                                          _I, _I, _P, _P, _P, _P]),
     "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
                                   Strides, _P, Strides, _P, _I, _P, _I, _I, _F, _P, Strides, _P, _P, _SZ, _P]),
 }
