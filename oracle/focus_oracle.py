@@ -34,6 +34,9 @@ reason in the design notes):
   R5 key set: I_p = I_sink U (selected prompt blocks) U [P, L), each key once.
      Without the generation region, attention with every block kept and a
      window covering the sequence could not equal dense attention.
+  R12 confidence: the largest softmax probability of a masked position's
+     predicted distribution; its argmax (lowest id among equal maxima) is the
+     predicted token; the n(t) most confident masked rows are unmasked.
 
 Pins (tests marked "not gpu"): brute-force dominance and exhaustive subset
 checks for every selection, exact rational block means, closed-form and
@@ -257,6 +260,44 @@ def sparse_attention(Q_rows, K, V, I_p, scale: float):
     """
     I_p = np.asarray(I_p, dtype=np.int64)
     return attention(Q_rows, np.asarray(K)[:, I_p], np.asarray(V)[:, I_p], scale)
+
+
+# ------------------------------------------------------------------ confidence and unmasking
+
+def token_confidence(logits_row):
+    """Confidence and predicted token of one masked position.
+
+    Summary, "Prerequisites" (dLLMs): at every denoising step the model gives each
+    [MASK] position a probability distribution over the vocabulary and positions are
+    unmasked by their confidence.  Reading R12: the confidence is the largest softmax
+    probability, c = max_v exp(z_v) / sum_u exp(z_u), and the predicted token is the
+    argmax (the lowest token id among equal maxima).  Returns (c, token) in fp64.
+    """
+    z = np.asarray(logits_row, dtype=np.float64)
+    top = z.max()
+    token = int(np.flatnonzero(z == top)[0])
+    return 1.0 / np.exp(z - top).sum(), token
+
+
+def unmask_step(logits, positions, mask, n_t: int):
+    """One unmasking decision: the confidence c_t of the listed positions and the n(t) of
+    them that are unmasked.
+
+    Summary, "Prerequisites" (dLLMs: positions are unmasked by confidence) and "Core
+    method" (n(t) is the number of tokens decoded at step t; c_t is the confidence PCGI
+    reads at step t+1).  logits [M, V] are the rows of `positions` [M].  Among the rows
+    whose position is still masked, the n(t) with the highest confidence are unmasked
+    (the lower position first among equal confidences).  Returns (conf, tokens, chosen):
+    conf [M] and tokens [M] per row, chosen the unmasked positions, ascending.
+    """
+    conf = np.zeros(len(positions))
+    tokens = np.zeros(len(positions), dtype=np.int64)
+    for r, z in enumerate(logits):
+        conf[r], tokens[r] = token_confidence(z)
+    cand = [r for r in range(len(positions)) if mask[int(positions[r])]]
+    ranked = sorted(cand, key=lambda r: (-conf[r], int(positions[r])))
+    chosen = np.array(sorted(int(positions[r]) for r in ranked[: max(n_t, 0)]), dtype=np.int64)
+    return conf, tokens, chosen
 
 
 # ------------------------------------------------------------------ one step

@@ -477,6 +477,60 @@ def check_kv_refresh(seed=11):
     assert np.array_equal(new[:, untouched], old[:, untouched])
 
 
+def check_confidence_fixture():
+    """Hand-worked confidences, tokens and unmask choices (tests/golden/confidence_hand.json)."""
+    for case in _golden("confidence_hand.json")["cases"]:
+        logits = np.log(np.asarray(case["logits_exp"], dtype=np.float64))
+        mask = np.zeros(case["L"], dtype=bool)
+        mask[case["masked"]] = True
+        conf, tokens, chosen = O.unmask_step(logits, np.array(case["positions"]), mask, case["n_t"])
+        _close(conf, case["conf"], 1e-15, "fixture confidence")
+        assert list(tokens) == case["tokens"], f"fixture tokens {list(tokens)}"
+        assert list(chosen) == case["chosen"], f"fixture unmask {list(chosen)}"
+
+
+def check_confidence_vs_library(seed=13):
+    """c against scipy's softmax on random rows; closed forms: uniform logits give 1/V and
+    token 0, one logit T above V-1 zeros gives e^T / (e^T + V - 1); shifting a row leaves
+    c unchanged; argmax by brute force with planted ties."""
+    rng = np.random.default_rng(seed)
+    for V in (2, 5, 97, 1000):
+        for _ in range(5):
+            z = rng.normal(size=V) * rng.uniform(0.1, 6.0)
+            z[rng.integers(V)] = z.max()                 # an exact tie at the max
+            c, tok = O.token_confidence(z)
+            _close(c, scipy.special.softmax(z).max(), 1e-14, "confidence vs scipy")
+            assert tok == min(i for i in range(V) if z[i] == z.max())
+            _close(O.token_confidence(z + 7.25)[0], c, 1e-14, "shift invariance")
+        c, tok = O.token_confidence(np.full(V, -3.5))
+        _close(c, 1.0 / V, 1e-15, "uniform confidence")
+        assert tok == 0
+        for T in (0.0, 1.0, 9.0):
+            z = np.zeros(V)
+            z[V // 2] = T
+            c, tok = O.token_confidence(z)
+            _close(c, math.exp(T) / (math.exp(T) + V - 1), 1e-14, "one peak")
+            assert tok == (V // 2 if T > 0 else 0)
+
+
+def check_unmask_dominance(trials=200, seed=14):
+    """The unmasked set is the top n(t) of the masked rows by confidence (dominance), with
+    planted ties and rows whose position is no longer masked."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        L = int(rng.integers(8, 80))
+        M = int(rng.integers(1, L))
+        positions = np.sort(rng.choice(L, M, replace=False))
+        mask = rng.random(L) < 0.7
+        V = int(rng.integers(2, 9))
+        logits = np.log(rng.integers(1, 4, size=(M, V)).astype(np.float64))   # many equal confidences
+        n_t = int(rng.integers(0, M + 2))
+        conf, _, chosen = O.unmask_step(logits, positions, mask, n_t)
+        row_of = {int(p): r for r, p in enumerate(positions)}
+        cand = [int(p) for p in positions if mask[p]]
+        assert dominance_ok({p: conf[row_of[p]] for p in cand}, cand, chosen, n_t)
+
+
 ALL_CHECKS = [
     check_focus_count, check_pcgi_dominance, check_pcgi_exhaustive, check_pcgi_window_fixture,
     check_window_closed_forms, check_attention_closed_form, check_attention_vs_library,
@@ -484,4 +538,5 @@ ALL_CHECKS = [
     check_sink_recovery, check_block_means_exact, check_relevance_bruteforce,
     check_block_fixture, check_key_set, check_sparse_equals_dense, check_sparse_vs_library,
     check_step_composition, check_kv_refresh, check_refreshed_blocks,
+    check_confidence_fixture, check_confidence_vs_library, check_unmask_dominance,
 ]

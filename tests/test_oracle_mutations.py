@@ -65,6 +65,28 @@ def _refreshed_blocks_ceil(rows, P, bs):
     return np.array(sorted({-(-int(r) // bs) for r in rows if 0 <= int(r) < P}), dtype=np.int64)
 
 
+def _confidence_max_logit(z):
+    z = np.asarray(z, dtype=np.float64)
+    return float(z.max()), int(np.argmax(z))
+
+
+def _confidence_argmax_last(z):
+    c, _ = _orig["token_confidence"](z)
+    z = np.asarray(z, dtype=np.float64)
+    return c, int(np.flatnonzero(z == z.max())[-1])
+
+
+def _unmask_least_confident(logits, positions, mask, n_t):
+    conf, tokens, _ = _orig["unmask_step"](logits, positions, mask, n_t)
+    cand = [r for r in range(len(positions)) if mask[int(positions[r])]]
+    ranked = sorted(cand, key=lambda r: (conf[r], int(positions[r])))
+    return conf, tokens, np.array(sorted(int(positions[r]) for r in ranked[:max(n_t, 0)]), dtype=np.int64)
+
+
+def _unmask_ignores_mask(logits, positions, mask, n_t):
+    return _orig["unmask_step"](logits, positions, np.ones(len(mask), dtype=bool), n_t)
+
+
 MUTATIONS = {
     "tie_break_highest_index": ("rank_select", _rank_highest_index),
     "select_smallest": ("rank_select", _rank_smallest),
@@ -92,6 +114,10 @@ MUTATIONS = {
     "key_set_block_off_by_one": ("key_set", _key_set_block_shift),
     "refreshed_blocks_past_prompt": ("refreshed_blocks", _refreshed_blocks_no_prompt_bound),
     "refreshed_blocks_rounded_up": ("refreshed_blocks", _refreshed_blocks_ceil),
+    "confidence_is_max_logit": ("token_confidence", _confidence_max_logit),
+    "confidence_argmax_last_tie": ("token_confidence", _confidence_argmax_last),
+    "unmask_least_confident": ("unmask_step", _unmask_least_confident),
+    "unmask_ignores_mask": ("unmask_step", _unmask_ignores_mask),
     "sparse_ignores_key_set": ("sparse_attention",
                                lambda Q, K, V, I_p, s: _orig["attention"](Q, K, V, s)),
 }
