@@ -14,6 +14,7 @@
  *   fdl_sparse_attention  (5) attention of the active queries over I_p only
  *   fdl_kv_refresh        approximate KV cache: the rows of U(t) take new K/V (Prerequisites)
  *   fdl_block_means_refresh  (4) the means of the blocks a refresh touched
+ *   fdl_confidence_unmask    confidence of the masked positions, unmasking of n(t) of them
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
@@ -286,6 +287,36 @@ fdl_status fdl_block_means_refresh(fdl_dtype dtype, int B, int Hkv, int L, int P
                                    const void* k, fdl_strides ks, int bs, const int32_t* rows,
                                    const int32_t* n_rows, int n_max, float* kbar,
                                    hipStream_t stream);
+
+/*
+ * fdl_confidence_unmask - the confidence of the masked positions and the unmasking of
+ * step t (the step that produces the c_t fdl_pcgi_select reads at step t+1).
+ * Summary page, "Prerequisites" (dLLMs: every [MASK] position gets a distribution over
+ * the vocabulary; positions are unmasked by confidence) and "Core method" (n(t) tokens
+ * are decoded at step t).  For each listed row r of sequence b, with logits z over the V
+ * tokens: c_r = max_v softmax(z)_v = 1 / sum_v exp(z_v - max z) (fp32), and its token is
+ * the argmax (the lowest id among equal maxima).  Among the rows whose position is still
+ * masked, the n_t of highest c (the lower position first among equal c) are unmasked.
+ *   logits     [B, m_max, V] (dtype FDL_F32 or FDL_BF16): row r of sequence b at
+ *              logits + b*ls.b + r*ls.r (elements; ls.h unused), the V logits contiguous,
+ *              rows 16-byte aligned, ls.r >= V
+ *   pos        [B, m_max] int32: the position of each row, ascending within a sequence;
+ *              rows r >= n_rows[b] (n_rows NULL: none) and positions outside [0, L) are
+ *              ignored
+ *   n_t        tokens to unmask per sequence (fewer candidates: all of them)
+ *   mask       [B, L] uint8, in/out: the unmasked positions are cleared
+ *   conf       [B, L] fp32, out at the listed positions: c for rows that stay masked, 0 for
+ *              the rows unmasked now and for rows whose position was not masked; other
+ *              positions untouched
+ *   tokens     [B, L] int32 out at the unmasked positions (the argmax), or NULL
+ *   unmasked   [B, n_t] int32 out, the unmasked positions ascending, -1 padded, or NULL
+ * m_max above 4096 is FDL_ERR_UNSUPPORTED.  Workspace: fdl_confidence_unmask_workspace_bytes.
+ */
+size_t fdl_confidence_unmask_workspace_bytes(int B, int V, int m_max);
+fdl_status fdl_confidence_unmask(fdl_dtype dtype, int B, int L, int V, const void* logits, fdl_strides ls,
+                                 const int32_t* pos, const int32_t* n_rows, int m_max, int n_t,
+                                 uint8_t* mask, float* conf, int32_t* tokens, int32_t* unmasked,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -345,4 +345,28 @@ fdl_status fdl_block_means_refresh(fdl_dtype dt, int B, int Hkv, int L, int P, i
     return hip_status(launch_block_means_refresh(dt, a, stream));
 }
 
+size_t fdl_confidence_unmask_workspace_bytes(int B, int V, int m_max) {
+    if (B < 1 || V < 1 || m_max < 0 || m_max > kMaxConfRows) return 0;
+    return confidence_workspace_bytes(B, V, m_max);
+}
+
+fdl_status fdl_confidence_unmask(fdl_dtype dt, int B, int L, int V, const void* logits, fdl_strides ls,
+                                 const int32_t* pos, const int32_t* n_rows, int m_max, int n_t, uint8_t* mask,
+                                 float* conf, int32_t* tokens, int32_t* unmasked, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    if (dt != FDL_F32 && dt != FDL_BF16) return FDL_ERR_DTYPE;
+    if (B < 1 || L < 1 || V < 1 || m_max < 0 || n_t < 0) return FDL_ERR_SHAPE;
+    if (m_max > kMaxConfRows) return FDL_ERR_UNSUPPORTED;
+    if (!mask || !conf) return FDL_ERR_NULL;
+    if (m_max == 0) return FDL_OK;
+    if (!logits || !pos) return FDL_ERR_NULL;
+    const int64_t e = static_cast<int64_t>(elem_size(dt));
+    if (!aligned16(logits) || (ls.b * e) % 16 || (ls.r * e) % 16) return FDL_ERR_ALIGN;
+    if (ls.r < V || ls.r >= (1ll << 40)) return FDL_ERR_SHAPE;
+    fdl_status st;
+    if ((st = check_ws(ws, ws_bytes, confidence_workspace_bytes(B, V, m_max))) != FDL_OK) return st;
+    return hip_status(launch_confidence_unmask(dt, B, L, V, logits, ls.b, ls.r, pos, n_rows, m_max, n_t, mask, conf,
+                                               tokens, unmasked, ws, stream));
+}
+
 }  // extern "C"

@@ -71,4 +71,13 @@ hipError_t launch_block_means_refresh(fdl_dtype dtype, const CacheArgs& a, hipSt
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream);
 
+// token confidence and unmasking (confidence.hip)
+constexpr int kMaxConfRows = 4096;   // listed rows per sequence
+int conf_chunks(int V);
+size_t confidence_workspace_bytes(int B, int V, int m_max);
+hipError_t launch_confidence_unmask(fdl_dtype dtype, int B, int L, int V, const void* logits, int64_t lsb,
+                                    int64_t lsr, const int32_t* pos, const int32_t* n_rows, int m_max, int n_t,
+                                    uint8_t* mask, float* conf, int32_t* tokens, int32_t* unmasked, void* ws,
+                                    hipStream_t stream);
+
 }  // namespace fdl

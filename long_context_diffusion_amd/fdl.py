@@ -32,6 +32,7 @@ EXPORTS = (
     "fdl_sparse_attention_workspace_bytes", "fdl_sparse_attention",
     "fdl_kv_refresh", "fdl_block_means_refresh",
     "fdl_block_score_topc_noalloc_max_bytes", "fdl_block_score_topc_noalloc",
+    "fdl_confidence_unmask_workspace_bytes", "fdl_confidence_unmask",
 )
 
 
@@ -70,6 +71,8 @@ _SIGS = {
                             _P, Strides, _P]),
     "fdl_block_means_refresh": (_I, [_I, _I, _I, _I, _I, _I, _P, Strides, _I, _P, _P, _I, _P, _P]),
     "fdl_block_score_topc_noalloc_max_bytes": (_SZ, []),
+    "fdl_confidence_unmask_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "fdl_confidence_unmask": (_I, [_I, _I, _I, _I, _P, Strides, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "fdl_block_score_topc_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
                                           _I, _I, _P, _P, _P, _P]),
     "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
@@ -378,3 +381,30 @@ def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, vt=None, 
                                     _ptr(lse), ws, ws_n, _stream(stream))
     _check(st, "fdl_sparse_attention")
     return out, lse
+
+
+def confidence_unmask(logits, pos, mask, conf, n_t: int, *, n_rows=None, tokens=None, unmasked=None,
+                      want_unmasked=True, workspace=None, stream=None):
+    """Confidence of the listed masked rows and the unmasking of n_t of them
+    (fdl_confidence_unmask).  logits [B, m_max, V] fp32 or bf16 (last axis contiguous),
+    pos [B, m_max] int32 ascending; mask [B, L] uint8 and conf [B, L] fp32 are updated in
+    place; tokens [B, L] int32 or None.  Returns unmasked [B, n_t] int32 (or None)."""
+    if logits.dim() != 3 or logits.stride(2) != 1:
+        raise FdlError(2, "logits must be [B, m_max, V] with a contiguous last axis")
+    B, m_max, V = logits.shape
+    L = mask.shape[1]
+    for name, t, dt in (("pos", pos, torch.int32), ("mask", mask, torch.uint8), ("conf", conf, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise FdlError(2, f"{name} must be a contiguous {dt} tensor")
+    if tokens is not None and (tokens.dtype != torch.int32 or not tokens.is_contiguous()):
+        raise FdlError(2, "tokens must be a contiguous int32 [B, L] tensor")
+    if unmasked is None and want_unmasked:
+        unmasked = torch.empty((B, max(n_t, 1)), dtype=torch.int32, device=logits.device)
+    nbytes = int(lib().fdl_confidence_unmask_workspace_bytes(B, V, m_max))
+    ws, ws_n = _ws(workspace, logits.device).get(nbytes)
+    st = lib().fdl_confidence_unmask(_dtype_code(logits), B, L, V, _ptr(logits),
+                                     Strides(logits.stride(0), 0, logits.stride(1)), _ptr(pos), _ptr(n_rows), m_max,
+                                     int(n_t), _ptr(mask), _ptr(conf), _ptr(tokens), _ptr(unmasked), ws, ws_n,
+                                     _stream(stream))
+    _check(st, "fdl_confidence_unmask")
+    return None if unmasked is None else unmasked[:, :n_t]

@@ -18,6 +18,10 @@ Recipe (shared by every workload in ``workloads.configs``):
     replacement.  Prompt positions are never masked.
   * Confidence of the previous step: fp32, U(0,1) or Beta(2,5) on masked
     slots, 0 elsewhere.
+  * Logits of the masked rows (the confidence and unmask step): sigma_z * N(0, 1) per
+    vocabulary entry (fp32, then bf16 by round-to-nearest-even), plus a peak of
+    2 + 6 u (u ~ U(0, 1)) at one seeded token of each row, so confidences spread
+    from near 1/V to near 1.
   * Multi-step scenario (the batch-of-4 workload): after each step the
     model's new confidence is c_t = 0.9*c_{t-1} + 0.1*U(0,1) (fp32) and the
     decoder unmasks the n(t) masked positions with the highest c_t, lowest
@@ -169,3 +173,15 @@ def sample_rows(n_rows: int, count: int, seed: int) -> np.ndarray:
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of an fp32 or bf16 tensor to an fp64 numpy array on the host."""
     return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def make_logits(B: int, M: int, V: int, seed: int, device="cpu", dtype=torch.bfloat16, sigma_z: float = 1.0):
+    """Logits [B, M, V] of M masked rows per sequence: sigma_z N(0, 1) plus one peak per row."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    z = torch.randn((B, M, V), generator=g, device=dev, dtype=torch.float32).mul_(sigma_z)
+    peak_tok = torch.randint(0, V, (B, M, 1), generator=g, device=dev)
+    peak = 2.0 + 6.0 * torch.rand((B, M, 1), generator=g, device=dev)
+    z.scatter_add_(2, peak_tok, peak)
+    return z.to(dtype).contiguous()
