@@ -37,6 +37,9 @@ reason in the design notes):
   R12 confidence: the largest softmax probability of a masked position's
      predicted distribution; its argmax (lowest id among equal maxima) is the
      predicted token; the n(t) most confident masked rows are unmasked.
+  D1-D4 (the DCU workload of the fifth page): cosine distance of the normalised
+     inputs, proportional budgets by largest remainder, mandatory windows around
+     given key tokens, top-budget of the other tokens.
 
 Pins (tests marked "not gpu"): brute-force dominance and exhaustive subset
 checks for every selection, exact rational block means, closed-form and
@@ -298,6 +301,76 @@ def unmask_step(logits, positions, mask, n_t: int):
     ranked = sorted(cand, key=lambda r: (-conf[r], int(positions[r])))
     chosen = np.array(sorted(int(positions[r]) for r in ranked[: max(n_t, 0)]), dtype=np.int64)
     return conf, tokens, chosen
+
+
+# ------------------------------------------------------------------ dynamic cache update (DCU)
+#
+# The fifth page (the Dynamic-dLLM article, section "DCU：动态缓存更新") describes a second
+# data-parallel workload: which tokens' caches a layer refreshes.  Readings D1-D4 are
+# listed in the design notes.
+
+def dcu_distance(x_now, x_prev) -> np.ndarray:
+    """Per-token change of a layer's normalised input between adjacent steps (reading D1).
+
+    DCU section: the cosine distance between the normalised token inputs of adjacent
+    steps measures how much a token's representation changed.  x_now, x_prev [L, H] ->
+    d [L] = 1 - x.y / (|x| |y|), with d = 0 where a norm is zero.
+    """
+    x = np.asarray(x_now, dtype=np.float64)
+    y = np.asarray(x_prev, dtype=np.float64)
+    d = np.zeros(x.shape[0])
+    for i in range(x.shape[0]):
+        nx, ny = math.sqrt(float(x[i] @ x[i])), math.sqrt(float(y[i] @ y[i]))
+        if nx > 0.0 and ny > 0.0:
+            d[i] = 1.0 - float(x[i] @ y[i]) / (nx * ny)
+    return d
+
+
+def dcu_budgets(activity, total: int) -> np.ndarray:
+    """Split of the update budget over layers in proportion to their activity (reading D2).
+
+    DCU section: token-level changes are summed into each layer's activity and the total
+    update budget is tilted towards the layers that changed most.  Layer l gets
+    floor(total a_l / sum a) tokens; the rest go one each to the layers with the largest
+    fractional parts (the lower layer first among equal parts); equal shares when every
+    activity is zero.
+    """
+    a = np.asarray(activity, dtype=np.float64)
+    A = a.sum()
+    q = np.full(len(a), total / len(a)) if A <= 0.0 else total * a / A
+    base = np.floor(q).astype(np.int64)
+    frac = q - base
+    order = sorted(range(len(a)), key=lambda l: (-frac[l], l))
+    for l in order[: total - int(base.sum())]:
+        base[l] += 1
+    return base
+
+
+def dcu_mandatory(key_tokens, w_m: int, L: int) -> np.ndarray:
+    """The mandatory update window (reading D3): w_m positions around each key token,
+    [c - floor(w_m/2), c - floor(w_m/2) + w_m) clipped to [0, L), ascending (the same
+    placement as the PCGI windows)."""
+    return window_active([c for c in key_tokens if c >= 0], w_m, L)
+
+
+def dcu_update_set(d, mandatory, budget: int) -> np.ndarray:
+    """One layer's update set (reading D4): the mandatory window and the `budget` other
+    tokens of largest change (the lower position first among equal changes), ascending."""
+    must = set(int(j) for j in mandatory)
+    rest = [j for j in range(len(d)) if j not in must]
+    picked = rank_select(d, rest, budget)
+    return np.array(sorted(must | set(int(j) for j in picked)), dtype=np.int64)
+
+
+def dcu_select(x_now, x_prev, key_tokens, w_m: int, total: int):
+    """Every layer's update set of one sequence: x_now, x_prev [layers, L, H].
+    Returns (d [layers, L], activity [layers], budgets [layers], sets [list of arrays])."""
+    layers, L = np.asarray(x_now).shape[:2]
+    d = np.stack([dcu_distance(x_now[l], x_prev[l]) for l in range(layers)])
+    activity = d.sum(axis=1)
+    budgets = dcu_budgets(activity, total)
+    must = dcu_mandatory(key_tokens, w_m, L)
+    return d, activity, budgets, [dcu_update_set(d[l], must, int(budgets[l])) for l in range(layers)]
 
 
 # ------------------------------------------------------------------ one step

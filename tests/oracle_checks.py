@@ -26,6 +26,7 @@ from fractions import Fraction
 
 import numpy as np
 import scipy.special
+import scipy.spatial.distance
 import torch
 
 from oracle import focus_oracle as O
@@ -531,6 +532,58 @@ def check_unmask_dominance(trials=200, seed=14):
         assert dominance_ok({p: conf[row_of[p]] for p in cand}, cand, chosen, n_t)
 
 
+def check_dcu_budget_fixture():
+    """Hand-worked budget splits and a mandatory window (tests/golden/dcu_budget_hand.json)."""
+    g = _golden("dcu_budget_hand.json")
+    for case in g["cases"]:
+        got = O.dcu_budgets(case["activity"], case["total"])
+        assert list(got) == case["budgets"], f"budgets {list(got)} for {case}"
+    for case in g["window_cases"]:
+        got = O.dcu_mandatory(case["key_tokens"], case["w_m"], case["L"])
+        assert list(got) == case["mandatory"], f"window {list(got)}"
+
+
+def check_dcu_distance_vs_library(seed=15):
+    """Cosine distance against scipy.spatial.distance.cosine; closed forms: a vector and a
+    positive multiple of it give 0, its negative 2, orthogonal vectors 1; zero rows give 0."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(12, 33))
+    y = x + rng.normal(size=(12, 33)) * rng.uniform(0.0, 2.0, size=(12, 1))
+    d = O.dcu_distance(x, y)
+    for i in range(12):
+        _close(d[i], scipy.spatial.distance.cosine(x[i], y[i]), 1e-12, "cosine distance")
+    e = np.eye(4)
+    _close(O.dcu_distance(np.stack([e[0], e[1], e[2], np.zeros(4)]),
+                          np.stack([3 * e[0], -2 * e[1], e[3], e[0]])), [0.0, 2.0, 1.0, 0.0], 1e-15, "closed forms")
+
+
+def check_dcu_selection(trials=120, seed=16):
+    """Budgets sum to the total and stay within one token of the proportional share;
+    each update set holds the mandatory window and the top-budget others (dominance)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        layers, L, H = int(rng.integers(1, 6)), int(rng.integers(4, 60)), int(rng.integers(1, 9))
+        x = rng.normal(size=(layers, L, H))
+        y = x + rng.normal(size=(layers, L, H)) * rng.uniform(0, 1, size=(layers, 1, 1))
+        y[:, ::5] = x[:, ::5]                            # unchanged tokens: d = 0 ties
+        keys = rng.integers(-1, L, size=int(rng.integers(0, 4)))
+        w_m = int(rng.integers(1, 7))
+        total = int(rng.integers(0, layers * L))
+        d, act, budgets, sets = O.dcu_select(x, y, keys, w_m, total)
+        assert int(budgets.sum()) == total
+        share = total * act / act.sum() if act.sum() > 0 else np.full(layers, total / layers)
+        assert np.all(np.abs(budgets - share) < 1.0)
+        must = set(int(j) for j in O.dcu_mandatory(keys, w_m, L))
+        brute = set(j for c in keys if c >= 0 for j in range(c - w_m // 2, c - w_m // 2 + w_m) if 0 <= j < L)
+        assert must == brute
+        for l in range(layers):
+            got = [int(j) for j in sets[l]]
+            assert got == sorted(set(got)) and must <= set(got)
+            rest = [j for j in range(L) if j not in must]
+            extra = sorted(set(got) - must)
+            assert dominance_ok(d[l], rest, extra, int(budgets[l]))
+
+
 ALL_CHECKS = [
     check_focus_count, check_pcgi_dominance, check_pcgi_exhaustive, check_pcgi_window_fixture,
     check_window_closed_forms, check_attention_closed_form, check_attention_vs_library,
@@ -539,4 +592,5 @@ ALL_CHECKS = [
     check_block_fixture, check_key_set, check_sparse_equals_dense, check_sparse_vs_library,
     check_step_composition, check_kv_refresh, check_refreshed_blocks,
     check_confidence_fixture, check_confidence_vs_library, check_unmask_dominance,
+    check_dcu_budget_fixture, check_dcu_distance_vs_library, check_dcu_selection,
 ]

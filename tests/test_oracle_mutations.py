@@ -87,6 +87,29 @@ def _unmask_ignores_mask(logits, positions, mask, n_t):
     return _orig["unmask_step"](logits, positions, np.ones(len(mask), dtype=bool), n_t)
 
 
+def _dcu_similarity(x, y):
+    return 1.0 - _orig["dcu_distance"](x, y)
+
+
+def _dcu_budget_floor_only(activity, total):
+    a = np.asarray(activity, dtype=np.float64)
+    return np.floor(total * a / a.sum() if a.sum() > 0 else np.full(len(a), total / len(a))).astype(np.int64)
+
+
+def _dcu_budget_highest_layer_first(activity, total):
+    a = np.asarray(activity, dtype=np.float64)
+    q = np.full(len(a), total / len(a)) if a.sum() <= 0 else total * a / a.sum()
+    base = np.floor(q).astype(np.int64)
+    frac = q - base
+    for l in sorted(range(len(a)), key=lambda l: (-frac[l], -l))[: total - int(base.sum())]:
+        base[l] += 1
+    return base
+
+
+def _dcu_set_without_window(d, mandatory, budget):
+    return _orig["dcu_update_set"](d, [], budget)
+
+
 MUTATIONS = {
     "tie_break_highest_index": ("rank_select", _rank_highest_index),
     "select_smallest": ("rank_select", _rank_smallest),
@@ -118,6 +141,10 @@ MUTATIONS = {
     "confidence_argmax_last_tie": ("token_confidence", _confidence_argmax_last),
     "unmask_least_confident": ("unmask_step", _unmask_least_confident),
     "unmask_ignores_mask": ("unmask_step", _unmask_ignores_mask),
+    "dcu_similarity_not_distance": ("dcu_distance", _dcu_similarity),
+    "dcu_budget_floor_only": ("dcu_budgets", _dcu_budget_floor_only),
+    "dcu_budget_ties_to_higher_layer": ("dcu_budgets", _dcu_budget_highest_layer_first),
+    "dcu_set_without_mandatory_window": ("dcu_update_set", _dcu_set_without_window),
     "sparse_ignores_key_set": ("sparse_attention",
                                lambda Q, K, V, I_p, s: _orig["attention"](Q, K, V, s)),
 }
