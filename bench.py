@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--no-cached-means", action="store_true",
                     help="skip the step variant that refreshes the KV cache and its touched block means")
     ap.add_argument("--refresh-reps", type=int, default=3)
+    ap.add_argument("--no-dcu", action="store_true", help="skip the dynamic cache update scoring measurement")
+    ap.add_argument("--dcu-reps", type=int, default=20)
+    ap.add_argument("--dcu-only", action="store_true",
+                    help="only the dynamic cache update scoring measurement (the run profiled for it)")
     ap.add_argument("--serial-means", action="store_true",
                     help="block means right before each layer's scoring instead of on a second stream")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -231,6 +235,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     F.fdl.lib()
+    if args.dcu_only:
+        print(json.dumps({"dcu": dcu_measurement(F, dev, torch.cuda.current_stream(), args)}), flush=True)
+        return
     t_setup = time.time()
     conf_np, mask_np = synth.step_inputs(wl)
     conf = torch.from_numpy(conf_np).to(dev)
@@ -503,7 +510,65 @@ def main():
             "algorithmic_bytes": int(cbytes), "refreshed_rows": na, "prompt_blocks_touched": touched,
             "note": "each layer refreshes the active rows of its KV cache and the block means they touch "
                     "right before attending, instead of the full per-layer means scan; not the headline workload"}
+    if not args.no_dcu:
+        result["dcu"] = dcu_measurement(F, dev, stream, args)
     print(json.dumps(result), flush=True)
+
+
+def dcu_measurement(F, dev, stream, args):
+    """The dynamic cache update scoring of one denoising step (fdl_dcu_select) over the same
+    32-layer, 32768-token stack: hidden size 4096, bf16 inputs of two adjacent steps, the 16
+    tokens decoded at the step (drawn from the 512-token generation block) as key tokens,
+    mandatory windows of 32 and an update budget of a tenth of the stack's layer-tokens.
+    Algorithmic bytes per call: both inputs read once (2 H 2 bytes a token), the fp32
+    distance written (4 bytes a token) and the update lists written (4 bytes an entry)."""
+    import numpy as np
+    import torch
+    from workloads import synth
+    B, NL, L, H, n_keys, w_m = 1, 32, 32768, 4096, 16, 32
+    total = NL * L // 10
+    x_now, x_prev = synth.make_dcu_inputs(B, NL, L, H, seed=31, device=dev, dtype=torch.bfloat16)
+    keys = torch.from_numpy(synth.make_key_tokens(B, n_keys, L - 512, L, seed=31)).to(dev)
+    ws = F.Workspace(dev)
+    out = F.dcu_select(x_now, x_prev, keys, w_m, total, workspace=ws, stream=stream)
+    for _ in range(2):
+        F.dcu_select(x_now, x_prev, keys, w_m, total, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.dcu_reps):
+        F.dcu_select(x_now, x_prev, keys, w_m, total, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.dcu_reps
+    n_upd = int(out[4].sum())
+    nbytes = B * NL * L * (2 * H * 2 + 4) + 4 * n_upd
+    gbs = nbytes / (ms / 1000) / 1e9
+    res = {
+        "workload": f"dynamic cache update scoring: {NL} layers x {L} tokens, hidden {H}, bf16, {n_keys} key "
+                    f"tokens, window {w_m}, budget {total} layer-tokens",
+        "ms_per_call": round(ms, 4), "tokens_per_s": round(B * NL * L / (ms / 1000), 1),
+        "update_entries": n_upd, "algorithmic_bytes_per_call": int(nbytes),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "fdl_dcu_select (distance, activity, selection)", "calls_timed": args.dcu_reps},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's distance on a bounded sample: 2048 tokens of each of 4 layers
+        from oracle import focus_oracle as O
+        layers = [0, 10, 20, 31]
+        rows = np.sort(np.random.default_rng(3).choice(L, 2048, replace=False))
+        xs = [(synth.to_f64(x_now[0, l, rows]), synth.to_f64(x_prev[0, l, rows])) for l in layers]
+        t0 = time.perf_counter()
+        for x, y in xs:
+            O.dcu_distance(x, y)
+        sec = time.perf_counter() - t0
+        n_tok = len(layers) * len(rows)
+        res["cpu_baseline"] = {"value": round(n_tok / sec, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the oracle's fp64 distance of {n_tok} tokens (2048 of each of "
+                                         f"{len(layers)} layers); budgets and selection not included"}
+    del x_now, x_prev
+    return res
 
 
 if __name__ == "__main__":

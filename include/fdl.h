@@ -15,6 +15,7 @@
  *   fdl_kv_refresh        approximate KV cache: the rows of U(t) take new K/V (Prerequisites)
  *   fdl_block_means_refresh  (4) the means of the blocks a refresh touched
  *   fdl_confidence_unmask    confidence of the masked positions, unmasking of n(t) of them
+ *   fdl_dcu_select           per-layer cache update sets of the dynamic cache update (DCU)
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
@@ -317,6 +318,41 @@ fdl_status fdl_confidence_unmask(fdl_dtype dtype, int B, int L, int V, const voi
                                  const int32_t* pos, const int32_t* n_rows, int m_max, int n_t,
                                  uint8_t* mask, float* conf, int32_t* tokens, int32_t* unmasked,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fdl_dcu_select - the dynamic cache update (DCU) of Dynamic-dLLM: which tokens each layer
+ * refreshes.  Dynamic-dLLM article, section "DCU：动态缓存更新": the change of a token's
+ * normalised layer input between adjacent steps is its cosine distance, a layer's activity
+ * is the sum of its tokens' changes, the total update budget goes to the layers in proportion
+ * to their activity, and a mandatory window around each key token is always refreshed.
+ * For sequence b and layer l, with x = x_now[b, l, i] and y = x_prev[b, l, i] (H values):
+ *   dist[b, l, i]   d = 1 - x.y / (|x| |y|) (0 where a norm is 0), computed in fp32 as
+ *                   (|x - y|^2 - (|x| - |y|)^2) / (2 |x| |y|), clamped at +0
+ *   activity[b, l]  the fp64 sum of dist[b, l, :] (in a fixed order: the same on every run)
+ *   budgets[b, l]   floor(total a_l / sum_m a_m), plus one for the total - sum of floors
+ *                   layers of largest fractional part (the lower layer first among equal
+ *                   parts); total / NL shares when every activity is 0
+ *   upd_idx[b, l, :n_upd[b, l]]  ascending: every position within a mandatory window
+ *                   [c - floor(w_m/2), c - floor(w_m/2) + w_m) of a key token c (clipped to
+ *                   [0, L)), and the budgets[b, l] other positions of largest d (the lower
+ *                   position first among equal d; all of them when there are fewer)
+ *   x_now, x_prev   [B, NL, L, H] (dtype FDL_F32 or FDL_BF16): token i of layer l of sequence
+ *                   b at x + b*s.b + l*s.h + i*s.r (elements), H values contiguous, every
+ *                   token's row 16-byte aligned; inputs finite (NaN distances come out 0)
+ *   key_tokens      [B, n_keys] int32, entries outside [0, L) ignored (may be NULL when
+ *                   n_keys is 0); w_m >= 1 when n_keys > 0
+ *   total           update budget of each sequence, shared by its NL layers (>= 0)
+ *   dist [B, NL, L] fp32, activity [B, NL] fp64, budgets [B, NL] int32, upd_idx [B, NL, L]
+ *   int32 (entries past n_upd untouched), n_upd [B, NL] int32: all outputs, all required.
+ * A caller that walks the layers one at a time passes NL = 1 and the layer's own budget as
+ * total.  L above 262144 or NL above 1024 is FDL_ERR_UNSUPPORTED.
+ * Workspace: fdl_dcu_select_workspace_bytes.
+ */
+size_t fdl_dcu_select_workspace_bytes(int B, int NL, int L);
+fdl_status fdl_dcu_select(fdl_dtype dtype, int B, int NL, int L, int H, const void* x_now, fdl_strides xns,
+                          const void* x_prev, fdl_strides xps, const int32_t* key_tokens, int n_keys, int w_m,
+                          int total, float* dist, double* activity, int32_t* budgets, int32_t* upd_idx,
+                          int32_t* n_upd, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -369,4 +369,39 @@ fdl_status fdl_confidence_unmask(fdl_dtype dt, int B, int L, int V, const void* 
                                                tokens, unmasked, ws, stream));
 }
 
+size_t fdl_dcu_select_workspace_bytes(int B, int NL, int L) {
+    if (B < 1 || NL < 1 || L < 1) return 0;
+    return dcu_workspace_bytes(B, NL, L);
+}
+
+fdl_status fdl_dcu_select(fdl_dtype dt, int B, int NL, int L, int H, const void* x_now, fdl_strides xns,
+                          const void* x_prev, fdl_strides xps, const int32_t* key_tokens, int n_keys, int w_m,
+                          int total, float* dist, double* activity, int32_t* budgets, int32_t* upd_idx,
+                          int32_t* n_upd, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (dt != FDL_F32 && dt != FDL_BF16) return FDL_ERR_DTYPE;
+    if (B < 1 || NL < 1 || L < 1 || H < 1 || n_keys < 0 || total < 0) return FDL_ERR_SHAPE;
+    if (n_keys > 0 && w_m < 1) return FDL_ERR_SHAPE;
+    if (L > kDcuMaxTokens || NL > kDcuMaxLayers) return FDL_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(B) * NL * dcu_chunks(L) >= (1ll << 31)) return FDL_ERR_SHAPE;
+    if (!x_now || !x_prev || !dist || !activity || !budgets || !upd_idx || !n_upd) return FDL_ERR_NULL;
+    if (n_keys > 0 && !key_tokens) return FDL_ERR_NULL;
+    const int64_t e = static_cast<int64_t>(elem_size(dt));
+    for (const fdl_strides& s : {xns, xps}) {
+        if ((s.b * e) % 16 || (s.h * e) % 16 || (s.r * e) % 16) return FDL_ERR_ALIGN;
+        for (int64_t v : {s.b, s.h, s.r})
+            if (v <= -(1ll << 40) || v >= (1ll << 40)) return FDL_ERR_SHAPE;
+    }
+    if (!aligned16(x_now) || !aligned16(x_prev)) return FDL_ERR_ALIGN;
+    fdl_status st;
+    if ((st = check_ws(ws, ws_bytes, dcu_workspace_bytes(B, NL, L))) != FDL_OK) return st;
+    DcuArgs a{};
+    a.B = B; a.NL = NL; a.L = L; a.H = H;
+    a.x_now = x_now; a.xnb = xns.b; a.xnl = xns.h; a.xnr = xns.r;
+    a.x_prev = x_prev; a.xpb = xps.b; a.xpl = xps.h; a.xpr = xps.r;
+    a.keys = key_tokens; a.n_keys = n_keys; a.w_m = w_m; a.total = total;
+    a.dist = dist; a.activity = activity; a.budgets = budgets; a.upd_idx = upd_idx; a.n_upd = n_upd;
+    a.ws = ws;
+    return hip_status(launch_dcu_select(dt, a, stream));
+}
+
 }  // extern "C"

@@ -71,6 +71,28 @@ hipError_t launch_block_means_refresh(fdl_dtype dtype, const CacheArgs& a, hipSt
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream);
 
+// dynamic cache update scoring (dcu.hip)
+constexpr int kDcuMaxTokens = 1 << 18;   // tokens per layer (the mandatory-window bitmask sits in LDS)
+constexpr int kDcuMaxLayers = 1024;
+struct DcuArgs {
+    int B, NL, L, H;
+    const void* x_now;
+    int64_t xnb, xnl, xnr;
+    const void* x_prev;
+    int64_t xpb, xpl, xpr;
+    const int32_t* keys;     // [B, n_keys] key tokens, entries outside [0, L) ignored
+    int n_keys, w_m, total;
+    float* dist;             // [B, NL, L]
+    double* activity;        // [B, NL]
+    int32_t* budgets;        // [B, NL]
+    int32_t* upd_idx;        // [B, NL, L], the first n_upd entries written
+    int32_t* n_upd;          // [B, NL]
+    void* ws;                // [B, NL, dcu_chunks(L)] doubles
+};
+int dcu_chunks(int L);
+size_t dcu_workspace_bytes(int B, int NL, int L);
+hipError_t launch_dcu_select(fdl_dtype dtype, const DcuArgs& a, hipStream_t stream);
+
 // token confidence and unmasking (confidence.hip)
 constexpr int kMaxConfRows = 4096;   // listed rows per sequence
 int conf_chunks(int V);

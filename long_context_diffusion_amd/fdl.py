@@ -33,6 +33,7 @@ EXPORTS = (
     "fdl_kv_refresh", "fdl_block_means_refresh",
     "fdl_block_score_topc_noalloc_max_bytes", "fdl_block_score_topc_noalloc",
     "fdl_confidence_unmask_workspace_bytes", "fdl_confidence_unmask",
+    "fdl_dcu_select_workspace_bytes", "fdl_dcu_select",
 )
 
 
@@ -73,6 +74,9 @@ _SIGS = {
     "fdl_block_score_topc_noalloc_max_bytes": (_SZ, []),
     "fdl_confidence_unmask_workspace_bytes": (_SZ, [_I, _I, _I]),
     "fdl_confidence_unmask": (_I, [_I, _I, _I, _I, _P, Strides, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fdl_dcu_select_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "fdl_dcu_select": (_I, [_I, _I, _I, _I, _I, _P, Strides, _P, Strides, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                            _SZ, _P]),
     "fdl_block_score_topc_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
                                           _I, _I, _P, _P, _P, _P]),
     "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
@@ -408,3 +412,42 @@ def confidence_unmask(logits, pos, mask, conf, n_t: int, *, n_rows=None, tokens=
                                      _stream(stream))
     _check(st, "fdl_confidence_unmask")
     return None if unmasked is None else unmasked[:, :n_t]
+
+
+def dcu_select(x_now, x_prev, key_tokens, w_m: int, total: int, *, out=None, workspace=None, stream=None):
+    """Per-layer cache update sets of the dynamic cache update (fdl_dcu_select).
+    x_now, x_prev [B, NL, L, H] fp32 or bf16 (last axis contiguous); key_tokens [B, n_keys]
+    int32 (entries outside [0, L) ignored) or None.  Returns (dist [B, NL, L] fp32,
+    activity [B, NL] fp64, budgets [B, NL] int32, upd_idx [B, NL, L] int32, n_upd [B, NL]
+    int32); the update set of (b, l) is upd_idx[b, l, :n_upd[b, l]].  `out` may hold those five
+    tensors to write into."""
+    if x_now.dim() != 4 or x_now.shape != x_prev.shape or x_now.dtype != x_prev.dtype:
+        raise FdlError(2, "x_now and x_prev must be [B, NL, L, H] tensors of one shape and dtype")
+    if x_now.stride(3) != 1 or x_prev.stride(3) != 1:
+        raise FdlError(2, "x_now and x_prev need a contiguous last axis")
+    B, NL, L, H = x_now.shape
+    dev = x_now.device
+    if key_tokens is not None and (key_tokens.dtype != torch.int32 or not key_tokens.is_contiguous()
+                                   or key_tokens.dim() != 2 or key_tokens.shape[0] != B):
+        raise FdlError(2, "key_tokens must be a contiguous int32 [B, n_keys] tensor")
+    n_keys = 0 if key_tokens is None else key_tokens.shape[1]
+    if out is None:
+        out = (torch.empty((B, NL, L), dtype=torch.float32, device=dev),
+               torch.empty((B, NL), dtype=torch.float64, device=dev),
+               torch.empty((B, NL), dtype=torch.int32, device=dev),
+               torch.empty((B, NL, L), dtype=torch.int32, device=dev),
+               torch.empty((B, NL), dtype=torch.int32, device=dev))
+    dist, activity, budgets, upd_idx, n_upd = out
+    for name, t, dt in (("dist", dist, torch.float32), ("activity", activity, torch.float64),
+                        ("budgets", budgets, torch.int32), ("upd_idx", upd_idx, torch.int32),
+                        ("n_upd", n_upd, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise FdlError(2, f"{name} must be a contiguous {dt} tensor")
+    nbytes = int(lib().fdl_dcu_select_workspace_bytes(B, NL, L))
+    ws, ws_n = _ws(workspace, dev).get(nbytes)
+    xs = [Strides(t.stride(0), t.stride(1), t.stride(2)) for t in (x_now, x_prev)]
+    st = lib().fdl_dcu_select(_dtype_code(x_now), B, NL, L, H, _ptr(x_now), xs[0], _ptr(x_prev), xs[1],
+                              _ptr(key_tokens), n_keys, int(w_m), int(total), _ptr(dist), _ptr(activity),
+                              _ptr(budgets), _ptr(upd_idx), _ptr(n_upd), ws, ws_n, _stream(stream))
+    _check(st, "fdl_dcu_select")
+    return dist, activity, budgets, upd_idx, n_upd

@@ -28,8 +28,10 @@ def assert_exact_set(got, expect, what):
     assert np.array_equal(got, expect), f"{what}: got {got[:20]}... expected {expect[:20]}..."
 
 
-def assert_selection(got, expect, scores, what):
-    """Selection equal to the oracle's, up to swaps inside the tie band at the cut.
+def assert_selection(got, expect, scores, what, abs_band=0.0):
+    """Selection equal to the oracle's, up to swaps inside the tie band at the cut (TIE_BAND
+    relative to the cut, widened by `abs_band` where the oracle's own scores carry an absolute
+    rounding error).
 
     Returns True when the sets are identical."""
     got, expect = valid(got), np.asarray(expect)
@@ -39,7 +41,7 @@ def assert_selection(got, expect, scores, what):
         return True
     scores = np.asarray(scores, dtype=np.float64)
     cut = scores[expect].min() if len(expect) else 0.0
-    band = TIE_BAND * abs(cut)
+    band = TIE_BAND * abs(cut) + abs_band
     diff = np.setxor1d(got, expect)
     far = diff[np.abs(scores[diff] - cut) > band]
     assert far.size == 0, (f"{what}: members {far[:10]} differ outside the tie band "

@@ -247,3 +247,44 @@ def test_kv_refresh_validation():
                                        None) == 2
     assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 4, 256, 192, 128, FAKE, st, 64, NULL, NULL, 0, FAKE,
                                        None) == 0
+
+
+def test_confidence_validation():
+    lib = F.lib()
+    ls = S(4 * 1024, 0, 1024)
+    ws_n = lib.fdl_confidence_unmask_workspace_bytes(1, 1000, 4)
+    assert ws_n == 4 * 1 * 16                                  # one (m, s, arg) part per row and chunk
+    assert lib.fdl_confidence_unmask_workspace_bytes(1, 1000, 4097) == 0
+
+    def call(dt=F.FDL_BF16, B=1, L=64, V=1000, logits=FAKE, s=ls, pos=FAKE, m_max=4, n_t=2, mask=FAKE,
+             conf=FAKE, ws=FAKE, n=ws_n):
+        return lib.fdl_confidence_unmask(dt, B, L, V, logits, s, pos, NULL, m_max, n_t, mask, conf, NULL, NULL,
+                                         ws, n, None)
+    assert call(dt=5) == 3
+    assert call(n_t=-1) == 2 and call(V=0) == 2 and call(s=S(0, 0, 992)) == 2   # rows shorter than V
+    assert call(m_max=4097) == 7
+    assert call(mask=NULL) == 1 and call(pos=NULL) == 1
+    assert call(logits=MISALIGNED) == 4 and call(s=S(0, 0, 1001)) == 4
+    assert call(ws=NULL) == 5 and call(n=ws_n - 1) == 5
+    assert call(m_max=0) == 0                                  # nothing listed: nothing to do
+
+
+def test_dcu_validation():
+    lib = F.lib()
+    # the fp64 partial sums of 32-token groups of every (sequence, layer)
+    assert lib.fdl_dcu_select_workspace_bytes(1, 32, 32768) == 32 * 1024 * 8
+    assert lib.fdl_dcu_select_workspace_bytes(2, 3, 33) == 2 * 3 * 2 * 8
+    assert lib.fdl_dcu_select_workspace_bytes(0, 3, 33) == 0
+    xs = S(32 * 1024 * 4096, 1024 * 4096, 4096)
+    ws_n = lib.fdl_dcu_select_workspace_bytes(1, 32, 1024)
+
+    def call(dt=F.FDL_BF16, B=1, NL=32, L=1024, H=4096, xn=FAKE, sn=xs, xp=FAKE, sp=xs, keys=FAKE, n_keys=4,
+             w_m=8, total=100, out=FAKE, ws=FAKE, n=ws_n):
+        return lib.fdl_dcu_select(dt, B, NL, L, H, xn, sn, xp, sp, keys, n_keys, w_m, total, out, out, out, out,
+                                  out, ws, n, None)
+    assert call(dt=2) == 3
+    assert call(H=0) == 2 and call(total=-1) == 2 and call(w_m=0) == 2 and call(n_keys=-1) == 2
+    assert call(L=(1 << 18) + 1) == 7 and call(NL=1025) == 7
+    assert call(xp=NULL) == 1 and call(out=NULL) == 1 and call(keys=NULL) == 1
+    assert call(xn=MISALIGNED) == 4 and call(sp=S(0, 0, 4100)) == 4
+    assert call(ws=NULL) == 5 and call(n=ws_n - 8) == 5

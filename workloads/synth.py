@@ -185,3 +185,43 @@ def make_logits(B: int, M: int, V: int, seed: int, device="cpu", dtype=torch.bfl
     peak = 2.0 + 6.0 * torch.rand((B, M, 1), generator=g, device=dev)
     z.scatter_add_(2, peak_tok, peak)
     return z.to(dtype).contiguous()
+
+
+def make_dcu_inputs(B: int, NL: int, L: int, H: int, seed: int, device="cpu", dtype=torch.bfloat16,
+                    unchanged: float = 0.25, zero_rows: int = 0):
+    """Normalised layer inputs of two adjacent steps, (x_now, x_prev) [B, NL, L, H].
+
+    x_prev ~ N(0, 1).  A token of layer l changes by sigma N(0, 1) with
+    sigma = s_l exp(0.75 N(0, 1)), s_l rising from 0.02 at the first layer to 0.3 at the last
+    (deeper layers change more); a share `unchanged` of the tokens keeps x_now == x_prev
+    exactly (distance 0, so equal distances occur); `zero_rows` tokens per (b, l) are all
+    zero in both steps.  Generated one layer at a time on `device`."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    x_now = torch.empty((B, NL, L, H), dtype=dtype, device=dev)
+    x_prev = torch.empty((B, NL, L, H), dtype=dtype, device=dev)
+    for b in range(B):
+        for l in range(NL):
+            s_l = 0.02 + 0.28 * (l / max(NL - 1, 1))
+            y = torch.randn((L, H), generator=g, device=dev, dtype=torch.float32)
+            sigma = s_l * torch.exp(0.75 * torch.randn((L, 1), generator=g, device=dev))
+            sigma = sigma * (torch.rand((L, 1), generator=g, device=dev) >= unchanged)
+            x = y + sigma * torch.randn((L, H), generator=g, device=dev, dtype=torch.float32)
+            if zero_rows:
+                rows = torch.randperm(L, generator=g, device=dev)[:zero_rows]
+                x[rows] = 0.0
+                y[rows] = 0.0
+            x_prev[b, l] = y.to(dtype)
+            x_now[b, l] = torch.where(sigma > 0, x, y).to(dtype)
+    return x_now, x_prev
+
+
+def make_key_tokens(B: int, n_keys: int, lo: int, hi: int, seed: int, pad: int = 0) -> np.ndarray:
+    """[B, n_keys + pad] int32: n_keys distinct positions drawn from [lo, hi) per sequence
+    (the tokens decoded at the step), in random order, then `pad` entries of -1."""
+    rng = np.random.default_rng(seed)
+    out = np.full((B, n_keys + pad), -1, dtype=np.int32)
+    for b in range(B):
+        out[b, :n_keys] = rng.choice(np.arange(lo, hi), size=n_keys, replace=False)
+    return out
