@@ -34,6 +34,13 @@ reason in the design notes):
   R5 key set: I_p = I_sink U (selected prompt blocks) U [P, L), each key once.
      Without the generation region, attention with every block kept and a
      window covering the sequence could not equal dense attention.
+  R13 alpha: the share of prompt blocks pruned, C = nb - floor(alpha nb).
+  R14 N_sinks = floor(0.01 L) (the pages' M read as the sequence length).
+  R15 dense tail: the last layers of a step attend densely (the pages report that
+     Dream needs its last 4 layers kept).
+  R16 per-KV-head blocks: R_{g,b} sums over the query heads of KV head g only, and
+     each KV head keeps its own top-C; its query heads attend over its own I_p.
+  R17 max aggregator: R_b = scale * max over heads and queries of q . kbar.
   R12 confidence: the largest softmax probability of a masked position's
      predicted distribution; its argmax (lowest id among equal maxima) is the
      predicted token; the n(t) most confident masked rows are unmasked.
@@ -240,6 +247,58 @@ def top_blocks(R, C: int) -> np.ndarray:
     return rank_select(R, range(len(R)), C)
 
 
+def block_relevance_per_head(Q_rows, kbar, scale: float) -> np.ndarray:
+    """R_{g,b} for per-KV-head block selection (reading R16): the part of R_b that the
+    query heads of KV head g contribute, R_{g,b} = scale * sum over h with g(h) = g and
+    active queries i of q_{h,i} . kbar_{g,b}.  Returns [Hkv, nb]; summed over g it is R_b.
+
+    Summary, "Method steps" (4) scores the blocks against the candidate queries; the
+    per-head form keeps one block set per KV head instead of one shared by all heads.
+    """
+    Q_rows = np.asarray(Q_rows, dtype=np.float64)
+    Hq, Hkv = Q_rows.shape[0], kbar.shape[0]
+    R = np.zeros((Hkv, kbar.shape[1]))
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        R[g] += (Q_rows[h] @ kbar[g].T).sum(axis=0)
+    return R * scale
+
+
+def block_relevance_max(Q_rows, kbar, scale: float, per_head: bool = False) -> np.ndarray:
+    """The max aggregator of the relevance (reading R17): a block scores by its strongest
+    single query, R_b = scale * max over heads h and active queries i of
+    q_{h,i} . kbar_{g(h),b} ([nb]), or per KV head over the heads of g only ([Hkv, nb]).
+    With no active query every block scores -inf.
+
+    Summary, "Independent weaknesses": the block representative and the summed relevance
+    can wash out a block that matters to a few queries only; this variant keeps such a
+    block's strongest match.
+    """
+    Q_rows = np.asarray(Q_rows, dtype=np.float64)
+    Hq, Hkv, nb = Q_rows.shape[0], kbar.shape[0], kbar.shape[1]
+    R = np.full((Hkv, nb), -np.inf)
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        if Q_rows.shape[1]:
+            R[g] = np.maximum(R[g], (Q_rows[h] @ kbar[g].T).max(axis=0))
+    R = R * scale
+    return R if per_head else R.max(axis=0)
+
+
+def blocks_kept(nb: int, alpha: float) -> int:
+    """Top-C from the sparsity ratio alpha (reading R13): alpha is the share of prompt
+    blocks pruned, so C = nb - floor(alpha * nb) are kept (the pages' default 0.5 keeps
+    half).  Summary, "Reproducibility" and "Limitations" list alpha among the
+    hyper-parameters without a formula."""
+    return int(nb) - int(math.floor(float(alpha) * int(nb)))
+
+
+def paper_sink_count(L: int) -> int:
+    """N_sinks = floor(0.01 * M) with M read as the sequence length L (reading R14);
+    Summary, "Reproducibility"."""
+    return int(math.floor(0.01 * int(L)))
+
+
 def key_set(sinks, blocks, bs: int, P: int, L: int) -> np.ndarray:
     """I_p: sinks, the keys of the selected prompt blocks and the generation region.
 
@@ -263,6 +322,21 @@ def sparse_attention(Q_rows, K, V, I_p, scale: float):
     """
     I_p = np.asarray(I_p, dtype=np.int64)
     return attention(Q_rows, np.asarray(K)[:, I_p], np.asarray(V)[:, I_p], scale)
+
+
+def sparse_attention_per_head(Q_rows, K, V, key_sets, scale: float):
+    """Sparse attention with one key set per KV head: query head h attends over the keys
+    of key_sets[g(h)] only (reading R16).  Returns (O [Hq, n, d], lse [Hq, n])."""
+    Q_rows = np.asarray(Q_rows, dtype=np.float64)
+    Hq, Hkv = Q_rows.shape[0], len(key_sets)
+    O = np.zeros(Q_rows.shape)
+    lse = np.zeros(Q_rows.shape[:2])
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        I_p = np.asarray(key_sets[g], dtype=np.int64)
+        O[h:h + 1], lse[h:h + 1] = attention(Q_rows[h:h + 1], np.asarray(K)[g:g + 1, I_p],
+                                             np.asarray(V)[g:g + 1, I_p], scale)
+    return O, lse
 
 
 # ------------------------------------------------------------------ confidence and unmasking
@@ -389,7 +463,8 @@ class SparseStep:
 
 def sparse_step(conf, mask, layer_inputs, *, layers: int, l_dense: int, n_t: int,
                 rho: float, w: int, P: int, bs: int, C: int, n_sinks: int,
-                scale: float, layer_subset=None) -> SparseStep:
+                scale: float, layer_subset=None, dense_tail: int = 0, per_head: bool = False,
+                aggregator: str = "sum") -> SparseStep:
     """One non-block-entry denoising step of one sequence, in the pages' order.
 
     Summary, "Method steps" (1)-(5): PCGI focus, window expansion, dense
@@ -399,6 +474,11 @@ def sparse_step(conf, mask, layer_inputs, *, layers: int, l_dense: int, n_t: int
     layer l (0-based).  `layer_subset` limits which layers are evaluated; the
     layer l_dense - 1 is always evaluated because the sinks come from it.
     A one-layer step (layers == l_dense == 1) uses that layer both ways.
+
+    Variants (Summary, "Independent weaknesses" and "Reproducibility"): the last
+    `dense_tail` layers attend densely like the first l_dense (reading R15); `per_head`
+    keeps one block set per KV head (R16, blocks[l] is then [Hkv, C]); `aggregator`
+    "max" scores a block by its strongest query (R17) instead of the sum.
     """
     L = len(mask)
     st = SparseStep(focus=pcgi_focus(conf, mask, focus_count(n_t, rho)), active=None)
@@ -408,16 +488,27 @@ def sparse_step(conf, mask, layer_inputs, *, layers: int, l_dense: int, n_t: int
     for l in sorted(wanted):
         Q, K, V = layer_inputs(l)
         Qa = np.asarray(Q, dtype=np.float64)[:, st.active]
-        if l < l_dense:
+        if l < l_dense or l >= layers - dense_tail:
             st.out[l], st.lse[l] = dense_attention(Qa, K, V, scale)
             if l == l_dense - 1:
                 st.sink_scores = sink_scores(Qa, K, st.lse[l], scale)
                 st.sinks = sink_select(st.sink_scores, n_sinks)
-        if l >= l_dense or layers == l_dense == 1:
-            R = block_relevance(Qa, block_means(K, P, bs), scale)
+        if (l_dense <= l < layers - dense_tail) or layers == l_dense == 1:
+            kbar = block_means(K, P, bs)
+            if aggregator == "max":
+                R = block_relevance_max(Qa, kbar, scale, per_head=per_head)
+            elif per_head:
+                R = block_relevance_per_head(Qa, kbar, scale)
+            else:
+                R = block_relevance(Qa, kbar, scale)
             st.relevance[l] = R
-            st.blocks[l] = top_blocks(R, C)
-            I_p = key_set(st.sinks, st.blocks[l], bs, P, L)
             key = l if l >= l_dense else ("sparse", l)
-            st.out[key], st.lse[key] = sparse_attention(Qa, K, V, I_p, scale)
+            if per_head:
+                st.blocks[l] = np.stack([top_blocks(R[g], C) for g in range(R.shape[0])])
+                sets = [key_set(st.sinks, st.blocks[l][g], bs, P, L) for g in range(R.shape[0])]
+                st.out[key], st.lse[key] = sparse_attention_per_head(Qa, K, V, sets, scale)
+            else:
+                st.blocks[l] = top_blocks(R, C)
+                I_p = key_set(st.sinks, st.blocks[l], bs, P, L)
+                st.out[key], st.lse[key] = sparse_attention(Qa, K, V, I_p, scale)
     return st

@@ -532,6 +532,92 @@ def check_unmask_dominance(trials=200, seed=14):
         assert dominance_ok({p: conf[row_of[p]] for p in cand}, cand, chosen, n_t)
 
 
+def check_per_head_relevance(trials=40, seed=17):
+    """Per-KV-head relevance: summed over the KV heads it is the shared R_b (pinned by its
+    own checks); with one KV head it is R_b; each head's top-C dominates its own scores."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        Hkv = int(rng.choice([1, 2, 3]))
+        Hq = Hkv * int(rng.integers(1, 4))
+        n, d, nb = int(rng.integers(0, 6)), int(rng.integers(1, 6)), int(rng.integers(1, 9))
+        Q = rng.normal(size=(Hq, n, d))
+        kbar = rng.normal(size=(Hkv, nb, d))
+        s = float(rng.uniform(0.1, 1.0))
+        Rg = O.block_relevance_per_head(Q, kbar, s)
+        assert Rg.shape == (Hkv, nb)
+        _close(Rg.sum(axis=0), O.block_relevance(Q, kbar, s), 1e-12, "sum over KV heads")
+        if Hkv == 1:
+            _close(Rg[0], O.block_relevance(Q, kbar, s), 1e-12, "one KV head")
+        C = int(rng.integers(0, nb + 2))
+        for g in range(Hkv):
+            assert dominance_ok(Rg[g], range(nb), O.top_blocks(Rg[g], C), C)
+
+
+def check_max_relevance(trials=40, seed=18):
+    """Max aggregator: one query of one head gives s q.kbar; identical queries over one KV
+    head give the summed relevance divided by their count; adding a query never lowers a
+    score; the per-head scores reduce to the shared ones by a max over the KV heads; no
+    query gives -inf."""
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=5)
+    kbar = rng.normal(size=(1, 4, 5))
+    _close(O.block_relevance_max(q.reshape(1, 1, 5), kbar, 0.5), 0.5 * kbar[0] @ q, 1e-12, "one query")
+    Q = np.broadcast_to(q, (3, 4, 5))
+    _close(O.block_relevance_max(Q, kbar, 0.5), O.block_relevance(Q, kbar, 0.5) / 12, 1e-12, "identical queries")
+    assert np.all(O.block_relevance_max(np.zeros((2, 0, 5)), kbar, 0.5) == -np.inf)
+    for _ in range(trials):
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.integers(1, 3))
+        n, d, nb = int(rng.integers(1, 6)), int(rng.integers(1, 6)), int(rng.integers(1, 8))
+        Q = rng.normal(size=(Hq, n, d))
+        kb = rng.normal(size=(Hkv, nb, d))
+        R = O.block_relevance_max(Q, kb, 0.3)
+        Rg = O.block_relevance_max(Q, kb, 0.3, per_head=True)
+        _close(Rg.max(axis=0), R, 0.0, "max over KV heads")
+        more = np.concatenate([Q, rng.normal(size=(Hq, 2, d))], axis=1)
+        assert np.all(O.block_relevance_max(more, kb, 0.3) >= R - 1e-12 * np.abs(R))   # matmul rounding
+
+
+def check_paper_defaults():
+    """alpha = 0.5 keeps half of an even block count, 0 keeps all, 1 none; N_sinks at
+    32K and 8K (Summary, "Reproducibility")."""
+    assert O.blocks_kept(504, 0.5) == 252 and O.blocks_kept(7, 0.5) == 4
+    assert O.blocks_kept(504, 0.0) == 504 and O.blocks_kept(504, 1.0) == 0
+    assert O.paper_sink_count(32768) == 327 and O.paper_sink_count(8192) == 81 and O.paper_sink_count(99) == 0
+
+
+def check_step_variants():
+    """The step with a dense tail runs dense attention in its last layers and sparse in
+    the others; with one KV head the per-head step equals the shared one."""
+    wl = configs.TINY_2K_F32
+    conf, mask, Q, K, V = _tiny_inputs(wl)
+    rng = np.random.default_rng(19)
+    Qs = [Q, Q[:, :, ::-1].copy(), Q * 0.5]
+    kw = dict(layers=3, l_dense=1, n_t=wl.n_t, rho=wl.rho, w=wl.w, P=wl.P, bs=wl.bs, C=wl.C,
+              n_sinks=wl.n_sinks, scale=wl.scale)
+    st = O.sparse_step(conf, mask, lambda l: (Qs[l], K, V), dense_tail=1, **kw)
+    Qa = Qs[2][:, st.active]
+    _close(st.out[2], O.dense_attention(Qa, K, V, wl.scale)[0], 0.0, "dense tail layer")
+    assert 1 in st.blocks and 2 not in st.blocks
+    I_p = O.key_set(st.sinks, st.blocks[1], wl.bs, wl.P, wl.L)
+    _close(st.out[1], O.sparse_attention(Qs[1][:, st.active], K, V, I_p, wl.scale)[0], 0.0, "sparse layer")
+    K1, V1 = K[:1], V[:1]
+    shared = O.sparse_step(conf, mask, lambda l: (Qs[l], K1, V1), **kw)
+    ph = O.sparse_step(conf, mask, lambda l: (Qs[l], K1, V1), per_head=True, **kw)
+    for l in (1, 2):
+        assert list(ph.blocks[l][0]) == list(shared.blocks[l])
+        _close(ph.out[l], shared.out[l], 1e-12, f"per-head layer {l}")
+    # two KV heads, one attending over every key and one over a subset: the first head's
+    # output is dense attention, the second's sparse attention over its own set
+    L = 40
+    Qh = rng.normal(size=(2, 3, 4))
+    Kh, Vh = rng.normal(size=(2, L, 4)), rng.normal(size=(2, L, 4))
+    sub = np.array([0, 3, 7, 21, 39])
+    O2, _ = O.sparse_attention_per_head(Qh, Kh, Vh, [np.arange(L), sub], 0.5)
+    _close(O2[:1], O.dense_attention(Qh[:1], Kh[:1], Vh[:1], 0.5)[0], 1e-12, "per-head set of all keys")
+    _close(O2[1:], O.sparse_attention(Qh[1:], Kh[1:], Vh[1:], sub, 0.5)[0], 1e-12, "per-head subset")
+
+
 def check_dcu_budget_fixture():
     """Hand-worked budget splits and a mandatory window (tests/golden/dcu_budget_hand.json)."""
     g = _golden("dcu_budget_hand.json")
@@ -593,4 +679,5 @@ ALL_CHECKS = [
     check_step_composition, check_kv_refresh, check_refreshed_blocks,
     check_confidence_fixture, check_confidence_vs_library, check_unmask_dominance,
     check_dcu_budget_fixture, check_dcu_distance_vs_library, check_dcu_selection,
+    check_per_head_relevance, check_max_relevance, check_paper_defaults, check_step_variants,
 ]

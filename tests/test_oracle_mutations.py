@@ -110,6 +110,36 @@ def _dcu_set_without_window(d, mandatory, budget):
     return _orig["dcu_update_set"](d, [], budget)
 
 
+def _per_head_modulo_group(Q, kbar, scale):
+    Q = np.asarray(Q, dtype=np.float64)
+    Hq, Hkv = Q.shape[0], kbar.shape[0]
+    R = np.zeros((Hkv, kbar.shape[1]))
+    for h in range(Hq):
+        R[h % Hkv] += (Q[h] @ kbar[h % Hkv].T).sum(axis=0)
+    return R * scale
+
+
+def _max_is_min(Q, kbar, scale, per_head=False):
+    return -_orig["block_relevance_max"](-np.asarray(Q), kbar, scale, per_head)
+
+
+def _max_is_sum(Q, kbar, scale, per_head=False):
+    return (_orig["block_relevance_per_head"](Q, kbar, scale) if per_head
+            else _orig["block_relevance"](Q, kbar, scale))
+
+
+def _blocks_kept_is_pruned(nb, alpha):
+    return int(np.floor(alpha * nb))
+
+
+def _sinks_of_prompt(L):
+    return _orig["paper_sink_count"](L - 512)
+
+
+def _per_head_attention_first_key_set(Q, K, V, key_sets, scale):
+    return _orig["sparse_attention"](Q, K, V, key_sets[0], scale)
+
+
 MUTATIONS = {
     "tie_break_highest_index": ("rank_select", _rank_highest_index),
     "select_smallest": ("rank_select", _rank_smallest),
@@ -141,6 +171,12 @@ MUTATIONS = {
     "confidence_argmax_last_tie": ("token_confidence", _confidence_argmax_last),
     "unmask_least_confident": ("unmask_step", _unmask_least_confident),
     "unmask_ignores_mask": ("unmask_step", _unmask_ignores_mask),
+    "per_head_relevance_modulo_group": ("block_relevance_per_head", _per_head_modulo_group),
+    "max_relevance_is_min": ("block_relevance_max", _max_is_min),
+    "max_relevance_is_sum": ("block_relevance_max", _max_is_sum),
+    "blocks_kept_is_pruned_count": ("blocks_kept", _blocks_kept_is_pruned),
+    "sink_count_of_prompt": ("paper_sink_count", _sinks_of_prompt),
+    "per_head_attention_one_key_set": ("sparse_attention_per_head", _per_head_attention_first_key_set),
     "dcu_similarity_not_distance": ("dcu_distance", _dcu_similarity),
     "dcu_budget_floor_only": ("dcu_budgets", _dcu_budget_floor_only),
     "dcu_budget_ties_to_higher_layer": ("dcu_budgets", _dcu_budget_highest_layer_first),
