@@ -12,6 +12,8 @@
  *   fdl_block_means       (4) mean key per prompt block (keys only: can run ahead)
  *   fdl_block_score_topc  (4) relevance R_b of the active queries, top-C blocks
  *   fdl_sparse_attention  (5) attention of the active queries over I_p only
+ *   fdl_block_score_topc_ex, fdl_sparse_attention_ex   per-KV-head block sets and the
+ *                         max-over-queries relevance
  *   fdl_kv_refresh        approximate KV cache: the rows of U(t) take new K/V (Prerequisites)
  *   fdl_block_means_refresh  (4) the means of the blocks a refresh touched
  *   fdl_confidence_unmask    confidence of the masked positions, unmasking of n(t) of them
@@ -206,6 +208,31 @@ fdl_status fdl_block_score_topc(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * fdl_block_score_topc_ex - fdl_block_score_topc with the relevance variants.  Summary page,
+ * "Independent weaknesses" (the block representative and the relevance may hide blocks that
+ * matter to few queries; Dream-like models differ per layer) and "Method steps" (4).  mode is
+ * a combination of:
+ *   FDL_SCORE_PER_HEAD  every KV head g keeps its own top-C from its own part of the
+ *                       relevance, R_{g,b} = scale * sum over the query heads h of g and the
+ *                       valid rows i of q_{h,i} . kbar_{g,b}; block_idx is [B, Hkv, C] and R
+ *                       [B, Hkv, nb]; pass the lists to fdl_sparse_attention_ex with
+ *                       blocks_per_head = 1
+ *   FDL_SCORE_MAX       a block scores by its strongest single query: the maximum over the
+ *                       heads (of g, per head) and valid rows of q_{h,i} . kbar, each dot in
+ *                       fp64, times scale; -inf for every block of a sequence without valid
+ *                       rows (the lowest C block ids are then kept)
+ * FDL_SCORE_SUM (0) is fdl_block_score_topc.  Other arguments, the workspace and the errors
+ * as there; a mode outside these bits is FDL_ERR_SHAPE.
+ */
+typedef enum fdl_score_mode { FDL_SCORE_SUM = 0, FDL_SCORE_PER_HEAD = 1, FDL_SCORE_MAX = 2 } fdl_score_mode;
+fdl_status fdl_block_score_topc_ex(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int P, int d,
+                                   const void* q, fdl_strides qs, const int32_t* q_idx,
+                                   const int32_t* n_q, int nq_max,
+                                   const void* k, fdl_strides ks, float scale, int bs, int C, int mode,
+                                   int32_t* block_idx, double* R, float* kbar,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * fdl_block_score_topc_noalloc - fdl_block_score_topc for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  Same arguments, results and errors as fdl_block_score_topc, without ws and
@@ -252,6 +279,27 @@ fdl_status fdl_sparse_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int L, 
                                 const int32_t* block_idx, int C, int bs,
                                 float scale, void* o, fdl_strides os, float* lse,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * fdl_sparse_attention_ex - fdl_sparse_attention with one block list per KV head when
+ * blocks_per_head is 1 (FDL_SCORE_PER_HEAD selections): block_idx is [B, Hkv, C], and the
+ * query heads of KV head g attend over the sinks, the blocks of list (b, g) and [P, L).  The
+ * sinks stay shared.  blocks_per_head 0 is fdl_sparse_attention; other values are
+ * FDL_ERR_SHAPE.  Workspace: fdl_sparse_attention_ex_workspace_bytes (the key lists of
+ * the list-building path are per (sequence, KV head)).
+ */
+size_t fdl_sparse_attention_ex_workspace_bytes(fdl_dtype dtype, int B, int Hq, int Hkv, int L,
+                                               int P, int d, int nq_max, int n_sinks, int C,
+                                               int bs, int blocks_per_head);
+fdl_status fdl_sparse_attention_ex(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int P, int d,
+                                   const void* q, fdl_strides qs, const int32_t* q_idx,
+                                   const int32_t* n_q, int nq_max,
+                                   const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                   const void* vt, fdl_strides vts,
+                                   const int32_t* sink_idx, int n_sinks,
+                                   const int32_t* block_idx, int C, int blocks_per_head, int bs,
+                                   float scale, void* o, fdl_strides os, float* lse,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * fdl_kv_refresh - the approximate KV cache refresh of one step.

@@ -232,11 +232,11 @@ size_t fdl_block_score_topc_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv
     return block_workspace_bytes(B, Hq, Hkv, P, d, bs, nq_max);
 }
 
-fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
-                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
-                                const void* k, fdl_strides ks, float scale, int bs, int C,
-                                int32_t* block_idx, double* R, float* kbar, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+fdl_status fdl_block_score_topc_ex(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
+                                   fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                                   const void* k, fdl_strides ks, float scale, int bs, int C, int mode,
+                                   int32_t* block_idx, double* R, float* kbar, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
     fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
     if (st != FDL_OK) return st;
     if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
@@ -245,6 +245,7 @@ fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if (!k && !kbar) return FDL_ERR_NULL;
     if (!block_idx) return FDL_ERR_NULL;
     if (P < 1 || P > L || bs < 1 || C < 0) return FDL_ERR_SHAPE;
+    if (mode < 0 || mode > (FDL_SCORE_PER_HEAD | FDL_SCORE_MAX)) return FDL_ERR_SHAPE;
     if ((st = check_ws(ws, ws_bytes, block_workspace_bytes(B, Hq, Hkv, P, d, bs, nq_max))) != FDL_OK) return st;
     BlockArgs a{};
     a.q = q; a.qsb = qs.b; a.qsh = qs.h; a.qsr = qs.r;
@@ -254,24 +255,40 @@ fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     a.nb = static_cast<int>((static_cast<int64_t>(P) + bs - 1) / bs);
     a.scale = resolve_scale(scale, d);
     a.kbar = kbar;
+    a.mode = (mode & FDL_SCORE_PER_HEAD ? kScorePerHead : 0) | (mode & FDL_SCORE_MAX ? kScoreMax : 0);
     return hip_status(launch_block_score_topc(dt, d, a, C, block_idx, R, ws, stream));
+}
+
+fdl_status fdl_block_score_topc(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
+                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                                const void* k, fdl_strides ks, float scale, int bs, int C,
+                                int32_t* block_idx, double* R, float* kbar, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    return fdl_block_score_topc_ex(dt, B, Hq, Hkv, L, P, d, q, qs, q_idx, n_q, nq_max, k, ks, scale, bs, C,
+                                   FDL_SCORE_SUM, block_idx, R, kbar, ws, ws_bytes, stream);
+}
+
+size_t fdl_sparse_attention_ex_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d,
+                                               int nq_max, int n_sinks, int C, int bs, int blocks_per_head) {
+    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 1 || bs < 1 || P < 0 || P > L ||
+        C < 0 || n_sinks < 0 || (blocks_per_head != 0 && blocks_per_head != 1))
+        return 0;
+    return plan_attention(dt, B, Hq, Hkv, d, nq_max, sparse_key_bound(L, P, n_sinks, C, bs), true,
+                          blocks_per_head != 0).ws_bytes;
 }
 
 size_t fdl_sparse_attention_workspace_bytes(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d,
                                             int nq_max, int n_sinks, int C, int bs) {
-    if (check_dtype_dims(dt, B, Hq, Hkv, L, d) != FDL_OK || nq_max < 1 || bs < 1 || P < 0 || P > L ||
-        C < 0 || n_sinks < 0)
-        return 0;
-    return plan_attention(dt, B, Hq, Hkv, d, nq_max, sparse_key_bound(L, P, n_sinks, C, bs), true).ws_bytes;
+    return fdl_sparse_attention_ex_workspace_bytes(dt, B, Hq, Hkv, L, P, d, nq_max, n_sinks, C, bs, 0);
 }
 
-fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
-                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
-                                const void* k, fdl_strides ks, const void* v, fdl_strides vs,
-                                const void* vt, fdl_strides vts,
-                                const int32_t* sink_idx, int n_sinks, const int32_t* block_idx, int C,
-                                int bs, float scale, void* o, fdl_strides os, float* lse, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+fdl_status fdl_sparse_attention_ex(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
+                                   fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                                   const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                   const void* vt, fdl_strides vts,
+                                   const int32_t* sink_idx, int n_sinks, const int32_t* block_idx, int C,
+                                   int blocks_per_head, int bs, float scale, void* o, fdl_strides os, float* lse,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
     fdl_status st = check_dtype_dims(dt, B, Hq, Hkv, L, d);
     if (st != FDL_OK) return st;
     if ((st = check_rows(nq_max, Hq / Hkv)) != FDL_OK) return st;
@@ -281,12 +298,13 @@ fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     if ((st = check_vt(vt, vts, dt, d, L)) != FDL_OK) return st;
     if ((st = check_tensor(o, os, dt, d)) != FDL_OK) return st;
     if (P < 0 || P > L || bs < 1 || C < 0 || n_sinks < 0) return FDL_ERR_SHAPE;
+    if (blocks_per_head != 0 && blocks_per_head != 1) return FDL_ERR_SHAPE;
     if ((n_sinks > 0 && !sink_idx) || (C > 0 && !block_idx)) return FDL_ERR_NULL;
     if (C > kPrepMaxIds || n_sinks > kPrepMaxIds) return FDL_ERR_UNSUPPORTED;
     const int64_t bound = sparse_key_bound(L, P, n_sinks, C, bs);
     if (bound > (1ll << 30)) return FDL_ERR_SHAPE;
     if (nq_max == 0) return FDL_OK;
-    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, bound, true);
+    const AttnPlan pl = plan_attention(dt, B, Hq, Hkv, d, nq_max, bound, true, blocks_per_head != 0);
     if ((st = check_ws(ws, ws_bytes, pl.ws_bytes)) != FDL_OK) return st;
     AttnArgs a = attn_args(dt, B, Hq, Hkv, L, P, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, vt, vts, scale, d,
                            o, os, lse, ws);
@@ -295,9 +313,21 @@ fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int
     a.n_sinks = n_sinks;
     a.block_idx = block_idx;
     a.C = C;
+    a.blk_per_head = blocks_per_head;
     a.bs = bs;
     a.nb = static_cast<int>((static_cast<int64_t>(P) + bs - 1) / bs);
     return hip_status(launch_attention(dt, d, a, pl, stream));
+}
+
+fdl_status fdl_sparse_attention(fdl_dtype dt, int B, int Hq, int Hkv, int L, int P, int d, const void* q,
+                                fdl_strides qs, const int32_t* q_idx, const int32_t* n_q, int nq_max,
+                                const void* k, fdl_strides ks, const void* v, fdl_strides vs,
+                                const void* vt, fdl_strides vts,
+                                const int32_t* sink_idx, int n_sinks, const int32_t* block_idx, int C,
+                                int bs, float scale, void* o, fdl_strides os, float* lse, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    return fdl_sparse_attention_ex(dt, B, Hq, Hkv, L, P, d, q, qs, q_idx, n_q, nq_max, k, ks, v, vs, vt, vts,
+                                   sink_idx, n_sinks, block_idx, C, 0, bs, scale, o, os, lse, ws, ws_bytes, stream);
 }
 
 fdl_status fdl_kv_refresh(fdl_dtype dt, int B, int Hkv, int L, int d, const int32_t* rows,

@@ -26,8 +26,9 @@ struct AttnArgs {
     int sparse;            // 0: keys [0, L); 1: I_p from sink_idx / block_idx / [P, L)
     const int32_t* sink_idx;
     int n_sinks;
-    const int32_t* block_idx;
+    const int32_t* block_idx;  // [B, C], or [B, Hkv, C] with blk_per_head
     int C, bs, nb;
+    int blk_per_head;      // 1: one block list (and key set) per KV head
     uint32_t bs_magic;     // ceil(2^32 / bs) for bs >= 2: division by bs as a multiply-high
     int n_splits;          // key-range splits (upper bound when dyn); > 1: partials combined by attn_merge
     int tiles_per_split;   // key tiles per split (static plans)
@@ -36,11 +37,16 @@ struct AttnArgs {
     int slots;             // workgroups of a persistent launch
     int dyn;               // 1: the persistent kernel picks the split count from the device row counts
     int key_cap;           // row stride of kv_list (upper bound on |I_p|)
-    int32_t* kv_list;      // [B, key_cap] keys of I_p (sparse), built by attn_prep
-    int32_t* n_keys;       // [B] |I_p| (sparse)
+    int32_t* kv_list;      // [lists, key_cap] keys of I_p (sparse), built by attn_prep
+    int32_t* n_keys;       // [lists] |I_p| (sparse)
     float* part_o;         // [B*Hq*nq_max][n_splits][d] unnormalised fp32 outputs
     float* part_ml;        // [B*Hq*nq_max][n_splits][2] running max (log2 domain) and sum
 };
+
+// The key set of (sequence b, KV head g): one per sequence, or one per KV head of each
+// sequence when every KV head has its own block list.
+__host__ __device__ inline int list_of(const AttnArgs& a, int b, int g) { return a.blk_per_head ? b * a.Hkv + g : b; }
+__host__ __device__ inline int n_lists(const AttnArgs& a) { return a.blk_per_head ? a.B * a.Hkv : a.B; }
 
 struct AttnPlan {
     int q_tiles, n_splits, tiles_per_split, tile_keys, rows_per_tile, tiles_total;
@@ -153,7 +159,7 @@ __device__ __forceinline__ int64_t d128_part_index(const AttnArgs& a, int nqt_ma
 hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream);
 
 AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_max,
-                        int64_t key_bound, bool sparse);
+                        int64_t key_bound, bool sparse, bool per_head = false);
 
 hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args, const AttnPlan& plan,
                             hipStream_t stream);

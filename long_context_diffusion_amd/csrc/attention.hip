@@ -46,9 +46,10 @@ namespace {
 
 constexpr int kPrepListWgs = 8;        // workgroups per sequence writing the key list
 
-// grid (B, kPrepListWgs + padding workgroups).  y < kPrepListWgs: write a slice of the
-// key list (y == 0 also appends the uncovered sinks and |I_p|); y >= kPrepListWgs:
-// zero padding rows when there is no key split.  The block and sink lists are brought to
+// grid (key lists, kPrepListWgs + padding workgroups), one key list per sequence or per
+// (sequence, KV head).  y < kPrepListWgs: write a slice of the key list (y == 0 also
+// appends the uncovered sinks and |I_p|); y >= kPrepListWgs: zero padding rows of the
+// sequence when there is no key split (the workgroups of its first list only).  The block and sink lists are brought to
 // canonical form first (valid ids, ascending, each once): at most kPrepMaxIds entries each.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d, bool build_list) {
@@ -56,9 +57,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d,
     __shared__ int s_blk[kPrepMaxIds];
     __shared__ int s_snk[kPrepMaxIds];
     __shared__ int s_scr[kPrepMaxIds];
-    const int b = blockIdx.x;
+    const int li = blockIdx.x;
+    const int b = a.blk_per_head ? li / a.Hkv : li;
     const int tid = threadIdx.x;
     if (blockIdx.y >= kPrepListWgs) {
+        if (a.blk_per_head && li % a.Hkv != 0) return;
         // padding rows r in [n_q[b], nq_max) of every query head: O = 0, lse = -inf
         // (only without a key split: the split merge writes them otherwise)
         if (!a.n_q || a.n_splits > 1) return;
@@ -80,10 +83,10 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d,
         return;
     }
     if (!a.sparse || !build_list) return;
-    const int n_sel = canonical_ids(a.block_idx + static_cast<int64_t>(b) * a.C, a.C, 0, a.nb, s_blk, s_scr, s_tmp);
+    const int n_sel = canonical_ids(a.block_idx + static_cast<int64_t>(li) * a.C, a.C, 0, a.nb, s_blk, s_scr, s_tmp);
     int n_blk = n_sel * a.bs;
     if (n_sel > 0 && s_blk[n_sel - 1] == a.nb - 1) n_blk -= a.nb * a.bs - a.P;  // short last block
-    int32_t* list = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
+    int32_t* list = a.kv_list + static_cast<int64_t>(li) * a.key_cap;
     const int G = a.L - a.P;
     const int n_fixed = n_blk + G;
     const int per = (n_fixed + kPrepListWgs - 1) / kPrepListWgs;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const AttnArgs a, int d,
                               s_tmp);
     n_unc = filter_ids(s_snk, n_unc, s_scr, s_tmp, [&](int j) { return sorted_contains(s_blk, n_sel, j / a.bs); });
     for (int i = tid; i < n_unc; i += blockDim.x) list[n_fixed + i] = s_snk[i];
-    if (tid == 0) a.n_keys[b] = n_fixed + n_unc;
+    if (tid == 0) a.n_keys[li] = n_fixed + n_unc;
 }
 
 // Merge of the key-range splits.  Each thread owns 8 elements of one output row
@@ -240,11 +243,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnArgs a) {
     const int h = g * a.Gq + p % a.Gq;
     const int r = p / a.Gq;
 
-    const int n_keys = SPARSE ? a.n_keys[b] : a.L;
+    const int n_keys = SPARSE ? a.n_keys[list_of(a, b, g)] : a.L;
     const int n_tiles = (n_keys + 63) / 64;
     const int t_begin = u.split * a.tiles_per_split;
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
-    const int32_t* klist = SPARSE ? a.kv_list + static_cast<int64_t>(b) * a.key_cap : nullptr;
+    const int32_t* klist = SPARSE ? a.kv_list + static_cast<int64_t>(list_of(a, b, g)) * a.key_cap : nullptr;
 
     // Key index of row `row` of tile t.  Rows outside the split or past n_keys read a
     // clamped valid row instead: such rows are masked (-inf score) or never computed,
@@ -484,11 +487,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnArgs a) {
     const bool row_ok = p < rows_valid;
     const int h = g * a.Gq + p % a.Gq;
     const int r = p / a.Gq;
-    const int n_keys = SPARSE ? a.n_keys[b] : a.L;
+    const int n_keys = SPARSE ? a.n_keys[list_of(a, b, g)] : a.L;
     const int n_tiles = (n_keys + kF32Keys - 1) / kF32Keys;
     const int t_begin = u.split * a.tiles_per_split;
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
-    const int32_t* klist = SPARSE ? a.kv_list + static_cast<int64_t>(b) * a.key_cap : nullptr;
+    const int32_t* klist = SPARSE ? a.kv_list + static_cast<int64_t>(list_of(a, b, g)) * a.key_cap : nullptr;
 
     float qv[D];
     float acc[D];
@@ -594,7 +597,7 @@ void launch_kernel(fdl_dtype dtype, const AttnArgs& a, dim3 grid, hipStream_t st
 }  // namespace
 
 AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_max,
-                        int64_t key_bound, bool sparse) {
+                        int64_t key_bound, bool sparse, bool per_head) {
     AttnPlan pl;
     const bool bf16 = dtype == FDL_BF16;
     const bool d128 = bf16 && d == 128;
@@ -622,7 +625,8 @@ AttnPlan plan_attention(fdl_dtype dtype, int B, int Hq, int Hkv, int d, int nq_m
     pl.tiles_per_split = static_cast<int>((tiles + splits - 1) / splits);
     if (pl.tiles_per_split < 1) pl.tiles_per_split = 1;
     pl.key_cap = sparse ? key_bound : 0;
-    pl.list_bytes = sparse ? round_up(static_cast<size_t>(B) * (key_bound + 1) * sizeof(int32_t), 256) : 0;
+    const int64_t lists = per_head ? static_cast<int64_t>(B) * Hkv : B;
+    pl.list_bytes = sparse ? round_up(static_cast<size_t>(lists) * (key_bound + 1) * sizeof(int32_t), 256) : 0;
     pl.part_bytes = 0;
     if (pl.n_splits > 1) {
         int64_t nrows;
@@ -650,7 +654,7 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     a.n_keys = nullptr;
     if (a.sparse) {
         a.kv_list = reinterpret_cast<int32_t*>(ws);
-        a.n_keys = a.kv_list + static_cast<int64_t>(a.B) * pl.key_cap;
+        a.n_keys = a.kv_list + static_cast<int64_t>(n_lists(a)) * pl.key_cap;
     }
     a.part_o = pl.part_bytes ? reinterpret_cast<float*>(ws + pl.list_bytes) : nullptr;
     a.part_ml = a.part_o ? a.part_o + static_cast<int64_t>(pl.part_bytes / ((d + 2) * sizeof(float))) * d : nullptr;
@@ -664,7 +668,7 @@ hipError_t launch_attention(fdl_dtype dtype, int d, const AttnArgs& args_in, con
     const bool need_list = a.sparse && !(dtype == FDL_BF16 && d == 128 && sparse_map_in_lds(a));
     if (need_list || zero_pad) {
         const int pad_wgs = zero_pad ? 64 : 0;   // extra workgroups that zero the padding rows
-        const dim3 pgrid(a.B, kPrepListWgs + pad_wgs);
+        const dim3 pgrid(n_lists(a), kPrepListWgs + pad_wgs);
         if (dtype == FDL_BF16) hipLaunchKernelGGL(attn_prep_kernel<uint16_t>, pgrid, dim3(256), 0, stream, a, d, need_list);
         else hipLaunchKernelGGL(attn_prep_kernel<float>, pgrid, dim3(256), 0, stream, a, d, need_list);
         hipError_t err = hipGetLastError();

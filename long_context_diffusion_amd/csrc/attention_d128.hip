@@ -117,7 +117,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         int n_keys = a.L, n_blk = 0, sink0 = a.L;
         const int32_t* klist = nullptr;
         if (MODE == kSparseLds) {
-            build_key_map<512>(a, b, s_blk, s_unc, s_tmp, s_tmp64, reinterpret_cast<int*>(s_raw), n_blk, sink0, n_keys);
+            build_key_map<512>(a, b, g, s_blk, s_unc, s_tmp, s_tmp64, reinterpret_cast<int*>(s_raw), n_blk, sink0, n_keys);
             // the Q rows have landed in this wave's staging area: fragments to registers, then
             // every wave is done with the staging areas before tile loads overwrite them
             __builtin_amdgcn_s_waitcnt(0);
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         } else if (MODE == kSparseList) {
-            n_keys = a.n_keys[b];
-            klist = a.kv_list + static_cast<int64_t>(b) * a.key_cap;
+            n_keys = a.n_keys[list_of(a, b, g)];
+            klist = a.kv_list + static_cast<int64_t>(list_of(a, b, g)) * a.key_cap;
         }
         const int n_tiles = (n_keys + 63) / 64;
         const int t_begin = u.split * tps;

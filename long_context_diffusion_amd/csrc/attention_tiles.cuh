@@ -83,7 +83,8 @@ __device__ __forceinline__ float xhalf(float x) {
 }
 
 
-// The LDS map of one sequence's sparse key set I_p: the selected blocks (s_blk, ascending,
+// The LDS map of the sparse key set I_p of sequence b (of its KV head g, when every KV head
+// has its own block list): the selected blocks (s_blk, ascending,
 // n_sel of them), then [P, L), then the sinks that no selected block holds (s_unc).  The
 // key set has n_keys positions: [0, n_blk) in blocks, [n_blk, sink0) the generation
 // region, [sink0, n_keys) the uncovered sinks.  The block and sink lists are taken as the
@@ -93,11 +94,11 @@ __device__ __forceinline__ float xhalf(float x) {
 // with `scratch`, at least 1024 ints of LDS, as the sort's scratch).  Every thread of the
 // block calls it, THREADS of them; C and n_sinks are at most 1024.
 template <int THREADS>
-__device__ inline void build_key_map(const AttnArgs& a, int b, int* s_blk, int* s_unc, int* s_tmp,
+__device__ inline void build_key_map(const AttnArgs& a, int b, int g, int* s_blk, int* s_unc, int* s_tmp,
                                      uint64_t* s_tmp64, int* scratch, int& n_blk, int& sink0, int& n_keys) {
     constexpr int EPT = 1024 / THREADS;   // entries of each list per thread
     const int tid = threadIdx.x;
-    const int32_t* blk_g = a.block_idx + static_cast<int64_t>(b) * a.C;
+    const int32_t* blk_g = a.block_idx + static_cast<int64_t>(list_of(a, b, g)) * a.C;
     const int32_t* snk_g = a.sink_idx + static_cast<int64_t>(b) * a.n_sinks;
     int sv[EPT];
     uint64_t packed = 0;   // bad entries << 40 | valid block ids << 20 | valid sinks

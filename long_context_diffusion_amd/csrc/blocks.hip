@@ -24,6 +24,14 @@
 //   block_select       one workgroup per sequence adds the head parts in head order,
 //                      scales by `scale`, and keeps the top-C blocks (lower block
 //                      index first among equal scores), ascending.
+// Variants of the relevance (Summary, "Independent weaknesses"): with kScorePerHead every
+// KV head keeps its own top-C from its own part of R (block_select runs per (sequence, KV
+// head)); with kScoreMax a block scores by its strongest single query,
+//   block_max          per (KV head g, 16 blocks): max over the query rows of g's query
+//                      heads of q . kbar_gb, each dot in fp64 (the products of bf16 or
+//                      fp32 queries and fp32 means are exact in fp64); the maximum does not
+//                      depend on the order the rows are visited in,
+// and block_select takes the max over the KV heads instead of the sum.
 
 #include "ops.cuh"
 
@@ -257,6 +265,83 @@ __global__ __launch_bounds__(kDotThreads) void block_dots_kernel(const BlockArgs
     if (sub == 0 && blk < a.nb) a.rpart[(static_cast<int64_t>(b) * a.Hkv + g) * a.nb + blk] = s;
 }
 
+constexpr int kMaxThreads = 512;
+constexpr int kMaxBlocks = 16;    // blocks per block_max workgroup
+
+// rpart[b][g][blk] = max over packed rows p < Gq * nq of q_p . kbar[b][g][blk] (-inf with no
+// rows).  Every wave covers all kMaxBlocks blocks of the workgroup: lanes 4j .. 4j+3 hold
+// block j's mean in four slices of D/4 elements (fp64), and each row's dot is the sum of the
+// four slice dots (two shuffles).  Waves take rows w, w + waves, ..., a batch of them in
+// flight (32 loads of 16 bytes per lane); the per-wave maxima combine through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(kMaxThreads) void block_max_kernel(const BlockArgs a) {
+    constexpr int SL = 4;                       // lanes per block
+    constexpr int EPL = D / SL;                 // elements per lane
+    constexpr int EPP = 16 / sizeof(T);         // elements per 16-byte load
+    constexpr int NLD = EPL / EPP;              // loads per lane and row
+    constexpr int kWaves = kMaxThreads / kWave;
+    constexpr int kMaxBatch = 32 / NLD > 2 ? 32 / NLD : 2;   // query rows in flight per wave
+    static_assert(kWave / SL == kMaxBlocks, "one wave covers the workgroup's blocks");
+    __shared__ double s_m[kWaves][kMaxBlocks];
+    __shared__ int s_phys[kQRows];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int nbc = (a.nb + kMaxBlocks - 1) / kMaxBlocks;
+    const int bc = blockIdx.x % nbc;
+    const int bg = blockIdx.x / nbc;
+    const int g = bg % a.Hkv, b = bg / a.Hkv;
+    const int j = lane / SL, sl = lane % SL;
+    const int blk = bc * kMaxBlocks + j;
+    const float* krow = a.kbar_in + ((static_cast<int64_t>(b) * a.Hkv + g) * a.nb + min(blk, a.nb - 1)) * D + sl * EPL;
+    double kv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kv[e] = static_cast<double>(krow[e]);
+    const int nq = a.n_q ? a.n_q[b] : a.nq_max;
+    const int rows = min(a.Gq * nq, a.Gq * a.nq_max);
+    const T* qhead = static_cast<const T*>(a.q) + b * a.qsb + static_cast<int64_t>(g) * a.Gq * a.qsh + sl * EPL;
+    double m = -INFINITY;
+    for (int c0 = 0; c0 < rows; c0 += kQRows) {
+        const int cn = min(kQRows, rows - c0);
+        __syncthreads();   // the previous chunk's indices are no longer read
+        for (int i = tid; i < cn; i += kMaxThreads) {
+            const int r = (c0 + i) / a.Gq;
+            s_phys[i] = a.q_idx ? max(a.q_idx[static_cast<int64_t>(b) * a.nq_max + r], 0) : r;
+        }
+        __syncthreads();
+        for (int i0 = wv; i0 < cn; i0 += kWaves * kMaxBatch) {
+            u32x4 x[kMaxBatch][NLD];
+#pragma unroll
+            for (int u = 0; u < kMaxBatch; ++u) {
+                const int i = min(i0 + kWaves * u, cn - 1);
+                const T* qrow = qhead + ((c0 + i) % a.Gq) * a.qsh + static_cast<int64_t>(s_phys[i]) * a.qsr;
+#pragma unroll
+                for (int t = 0; t < NLD; ++t) x[u][t] = *reinterpret_cast<const u32x4*>(qrow + t * EPP);
+            }
+#pragma unroll
+            for (int u = 0; u < kMaxBatch; ++u) {
+                double s = 0.0;
+#pragma unroll
+                for (int t = 0; t < NLD; ++t) {
+                    float v[EPP];
+                    unpack16<T>(x[u][t], v);
+#pragma unroll
+                    for (int e = 0; e < EPP; ++e) s = fma(static_cast<double>(v[e]), kv[t * EPP + e], s);
+                }
+                s += __shfl_xor(s, 1, kWave);
+                s += __shfl_xor(s, 2, kWave);
+                if (i0 + kWaves * u < cn) m = fmax(m, s);
+            }
+        }
+    }
+    if (sl == 0) s_m[wv][j] = m;
+    __syncthreads();
+    if (tid < kMaxBlocks) {
+        double mm = s_m[0][tid];
+        for (int w = 1; w < kWaves; ++w) mm = fmax(mm, s_m[w][tid]);
+        const int bk = bc * kMaxBlocks + tid;
+        if (bk < a.nb) a.rpart[(static_cast<int64_t>(b) * a.Hkv + g) * a.nb + bk] = mm;
+    }
+}
+
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectLds = 2048;   // blocks ranked in LDS
 constexpr int kSlices = 4;         // threads summing the head parts of one block
@@ -269,13 +354,18 @@ __device__ __forceinline__ uint64_t distinct_key(double r, int blk) {
     return (okey64(r) & ~uint64_t(0x7ff)) | static_cast<uint64_t>(0x7ff - blk);
 }
 
-// R_b = scale * sum over g of rpart[b][g][blk] (KV heads in order), then the top-C blocks.
+// R_b = scale * sum over g of rpart[b][g][blk] (KV heads in order; their max with
+// kScoreMax), then the top-C blocks.  With kScorePerHead one workgroup per (b, g) keeps the
+// top-C of scale * rpart[b][g][:] in block_idx[b][g] (R_out [b][g] likewise).
 __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const BlockArgs a, int C,
                                                                        int32_t* block_idx, double* R_out) {
     __shared__ SelectSmem sm;
     __shared__ uint64_t s_key[kSelectLds];
     __shared__ double s_slice[kSlices][kSelectThreads / kSlices];
-    const int b = blockIdx.x;
+    const bool per_head = (a.mode & kScorePerHead) != 0, use_max = (a.mode & kScoreMax) != 0;
+    const int li = blockIdx.x;   // list: b, or b * Hkv + g per head
+    const int b = per_head ? li / a.Hkv : li;
+    const int gh = per_head ? li % a.Hkv : 0;
     const int tid = threadIdx.x;
     // thread slice `slice` sums KV heads [slice*per, (slice+1)*per)
     const int per = (a.Hkv + kSlices - 1) / kSlices;
@@ -286,7 +376,7 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
     for (int blk0 = 0; blk0 < a.nb; blk0 += kSelectThreads / kSlices) {
         const int blk = blk0 + lb;
         double s = 0.0;
-        if (blk < a.nb) {
+        if (blk < a.nb && !per_head && !use_max) {
             // 16 loads in flight; head g's part is nb doubles after head g-1's
             for (int g = g0; g < g1; g += 16) {
                 double x[16];
@@ -300,23 +390,37 @@ __global__ __launch_bounds__(kSelectThreads) void block_select_kernel(const Bloc
         __syncthreads();
         if (slice == 0 && blk < a.nb) {
             double tot = 0.0;
+            if (per_head) {
+                tot = rp[static_cast<int64_t>(gh) * a.nb + blk];
+            } else if (use_max) {
+                tot = -INFINITY;
+                for (int g = 0; g < a.Hkv; ++g) tot = fmax(tot, rp[static_cast<int64_t>(g) * a.nb + blk]);
+            } else {
 #pragma unroll
-            for (int i = 0; i < kSlices; ++i) tot += s_slice[i][lb];
+                for (int i = 0; i < kSlices; ++i) tot += s_slice[i][lb];
+            }
             const double val = tot * static_cast<double>(a.scale);
             if (a.nb <= kSelectThreads) s_key[blk] = distinct_key(val, blk);
             else if (a.nb <= kSelectLds) s_key[blk] = okey64(val);
-            else R[blk] = val;
-            if (R_out) R_out[static_cast<int64_t>(b) * a.nb + blk] = val;
+            else if (!per_head) R[blk] = val;
+            if (R_out) R_out[static_cast<int64_t>(li) * a.nb + blk] = val;
         }
         __syncthreads();
     }
     __threadfence_block();
-    int32_t* out = block_idx + static_cast<int64_t>(b) * C;
+    int32_t* out = block_idx + static_cast<int64_t>(li) * C;
     if (a.nb <= kSelectThreads) {
         block_topk_distinct(a.nb, C, [&](int j) { return s_key[j]; }, [](int j) { return j; }, out, C, &sm);
     } else if (a.nb <= kSelectLds) {
         auto key_of = [&](int j, uint64_t* key) -> bool {
             *key = s_key[j];
+            return true;
+        };
+        block_emit_topk<uint64_t>(a.nb, C, key_of, [](int j) { return j; }, out, C, &sm);
+    } else if (per_head) {
+        const double* rg = rp + static_cast<int64_t>(gh) * a.nb;
+        auto key_of = [&](int j, uint64_t* key) -> bool {
+            *key = okey64(rg[j] * static_cast<double>(a.scale));
             return true;
         };
         block_emit_topk<uint64_t>(a.nb, C, key_of, [](int j) { return j; }, out, C, &sm);
@@ -364,15 +468,25 @@ hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, i
         if (err != hipSuccess) return err;
     }
     a.kbar_in = a.kbar;
-    const int nbc = (a.nb + dot_blocks(d) - 1) / dot_blocks(d);
-    const dim3 dgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * nbc));
+    if (a.mode & kScoreMax) {
+        const int nbc = (a.nb + kMaxBlocks - 1) / kMaxBlocks;
+        const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * nbc));
+#define FDL_MAXK(T, DD) hipLaunchKernelGGL((block_max_kernel<T, DD>), mgrid, dim3(kMaxThreads), 0, stream, a)
+        if (dtype == FDL_BF16) { if (d == 128) FDL_MAXK(uint16_t, 128); else FDL_MAXK(uint16_t, 64); }
+        else { if (d == 128) FDL_MAXK(float, 128); else FDL_MAXK(float, 64); }
+#undef FDL_MAXK
+    } else {
+        const int nbc = (a.nb + dot_blocks(d) - 1) / dot_blocks(d);
+        const dim3 dgrid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * nbc));
 #define FDL_DOTS(T, DD) hipLaunchKernelGGL((block_dots_kernel<T, DD>), dgrid, dim3(kDotThreads), 0, stream, a)
-    if (dtype == FDL_BF16) { if (d == 128) FDL_DOTS(uint16_t, 128); else FDL_DOTS(uint16_t, 64); }
-    else { if (d == 128) FDL_DOTS(float, 128); else FDL_DOTS(float, 64); }
+        if (dtype == FDL_BF16) { if (d == 128) FDL_DOTS(uint16_t, 128); else FDL_DOTS(uint16_t, 64); }
+        else { if (d == 128) FDL_DOTS(float, 128); else FDL_DOTS(float, 64); }
 #undef FDL_DOTS
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(block_select_kernel, dim3(a.B), dim3(kSelectThreads), 0, stream, a, C, block_idx, R_out);
+    const int lists = (a.mode & kScorePerHead) ? a.B * a.Hkv : a.B;
+    hipLaunchKernelGGL(block_select_kernel, dim3(lists), dim3(kSelectThreads), 0, stream, a, C, block_idx, R_out);
     return hipGetLastError();
 }
 

@@ -33,9 +33,12 @@ struct BlockArgs {
     float scale;
     float* kbar;            // [B, Hkv, nb, d] block means written by block_means, or NULL
     const float* kbar_in;   // [B, Hkv, nb, d] block means the relevance is scored against
-    double* rpart;          // [B, Hkv, nb] each KV head's part of R
+    double* rpart;          // [B, Hkv, nb] each KV head's part of R (its max with kScoreMax)
     double* rfull;          // [B, nb]
+    int mode;               // kScorePerHead | kScoreMax bits (0: one summed R per sequence)
 };
+constexpr int kScorePerHead = 1;   // one relevance and block set per KV head
+constexpr int kScoreMax = 2;       // relevance = max over the queries instead of their sum
 
 hipError_t launch_pcgi_select(const float* conf, const uint8_t* mask, int B, int L, int k, int w,
                               int32_t* focus_idx, int32_t* n_focus, int k_cap,

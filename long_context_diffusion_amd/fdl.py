@@ -34,7 +34,9 @@ EXPORTS = (
     "fdl_block_score_topc_noalloc_max_bytes", "fdl_block_score_topc_noalloc",
     "fdl_confidence_unmask_workspace_bytes", "fdl_confidence_unmask",
     "fdl_dcu_select_workspace_bytes", "fdl_dcu_select",
+    "fdl_block_score_topc_ex", "fdl_sparse_attention_ex_workspace_bytes", "fdl_sparse_attention_ex",
 )
+FDL_SCORE_PER_HEAD, FDL_SCORE_MAX = 1, 2
 
 
 class FdlError(RuntimeError):
@@ -75,6 +77,12 @@ _SIGS = {
     "fdl_confidence_unmask_workspace_bytes": (_SZ, [_I, _I, _I]),
     "fdl_confidence_unmask": (_I, [_I, _I, _I, _I, _P, Strides, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "fdl_dcu_select_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "fdl_block_score_topc_ex": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
+                                     _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "fdl_sparse_attention_ex_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "fdl_sparse_attention_ex": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
+                                     Strides, _P, Strides, _P, _I, _P, _I, _I, _I, _F, _P, Strides, _P, _P, _SZ,
+                                     _P]),
     "fdl_dcu_select": (_I, [_I, _I, _I, _I, _I, _P, Strides, _P, Strides, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
     "fdl_block_score_topc_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
@@ -320,11 +328,13 @@ def block_means_refresh(k, P: int, bs: int, rows, kbar, *, n_rows=None, stream=N
 
 def block_score_topc(q, k, P: int, bs: int, C: int, *, q_idx=None, n_q=None, nq_max=None,
                      scale: float = 0.0, out=None, want_R=False, want_kbar=False, kbar=None, L=None,
-                     workspace=None, stream=None):
-    """Top-C prompt blocks by relevance to the active queries (fdl_block_score_topc).
+                     per_head=False, aggregator="sum", workspace=None, stream=None):
+    """Top-C prompt blocks by relevance to the active queries (fdl_block_score_topc, or
+    fdl_block_score_topc_ex for per_head / aggregator "max").
 
     k None: kbar must hold the block means (block_means) and L the sequence length.
-    Returns (block_idx [B, C] int32, R [B, nb] fp64 or None, kbar [B, Hkv, nb, d] fp32 or None).
+    Returns (block_idx [B, C] int32 ([B, Hkv, C] per head), R [B, nb] ([B, Hkv, nb]) fp64 or
+    None, kbar [B, Hkv, nb, d] fp32 or None).
     """
     B, Hq, _, d = q.shape
     if k is not None:
@@ -333,32 +343,36 @@ def block_score_topc(q, k, P: int, bs: int, C: int, *, q_idx=None, n_q=None, nq_
         if kbar is None or L is None:
             raise FdlError(1, "block_score_topc without keys needs kbar and L")
         Hkv = kbar.shape[1]
+    if aggregator not in ("sum", "max"):
+        raise FdlError(2, f"unknown relevance aggregator {aggregator!r}")
+    mode = (FDL_SCORE_PER_HEAD if per_head else 0) | (FDL_SCORE_MAX if aggregator == "max" else 0)
     qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
     dt = _dtype_code(q)
     nb = -(-P // bs)
+    lead = (B, Hkv) if per_head else (B,)
     if out is None:
-        out = torch.empty((B, max(C, 1)), dtype=torch.int32, device=q.device)
-    R = torch.empty((B, nb), dtype=torch.float64, device=q.device) if want_R else None
+        out = torch.empty(lead + (max(C, 1),), dtype=torch.int32, device=q.device)
+    R = torch.empty(lead + (nb,), dtype=torch.float64, device=q.device) if want_R else None
     if kbar is None and want_kbar:
         kbar = torch.empty((B, Hkv, nb, d), dtype=torch.float32, device=q.device)
     nbytes = int(lib().fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs, nq_max))
     ws, ws_n = _ws(workspace, q.device).get(nbytes)
     ks = _strides4(k) if k is not None else Strides(0, 0, d)
-    st = lib().fdl_block_score_topc(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
-                                    _ptr(k), ks, float(scale), int(bs), int(C), _ptr(out),
-                                    _ptr(R), _ptr(kbar), ws, ws_n, _stream(stream))
-    _check(st, "fdl_block_score_topc")
-    return out[:, :C], R, kbar
+    st = lib().fdl_block_score_topc_ex(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
+                                       _ptr(k), ks, float(scale), int(bs), int(C), mode, _ptr(out),
+                                       _ptr(R), _ptr(kbar), ws, ws_n, _stream(stream))
+    _check(st, "fdl_block_score_topc_ex")
+    return out[..., :C], R, kbar
 
 
 def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, vt=None, q_idx=None, n_q=None,
                      nq_max=None, scale: float = 0.0, out=None, lse=None, want_lse=False,
                      workspace=None, stream=None):
-    """Attention of the active queries over I_p only (fdl_sparse_attention).
+    """Attention of the active queries over I_p only (fdl_sparse_attention_ex).
 
     sink_idx [B, n_sinks] and block_idx [B, C] int32 or None: each read as the set of its
-    valid entries (any order, repeats count once, -1 and out-of-range entries ignored);
-    vt None or transpose_v(v).
+    valid entries (any order, repeats count once, -1 and out-of-range entries ignored); a
+    [B, Hkv, C] block_idx gives every KV head its own blocks.  vt None or transpose_v(v).
     Returns (o [B, Hq, nq_max, d], lse or None).
     """
     B, Hq, _, d = q.shape
@@ -366,24 +380,28 @@ def sparse_attention(q, k, v, P: int, sink_idx, block_idx, bs: int, *, vt=None, 
     qi, nqp, nq_max = _rows(q, q_idx, n_q, nq_max)
     dt = _dtype_code(q)
     n_sinks = 0 if sink_idx is None else sink_idx.shape[1]
-    C = 0 if block_idx is None else block_idx.shape[1]
-    if sink_idx is not None and sink_idx.stride(1) != 1 or (block_idx is not None and block_idx.stride(1) != 1):
+    per_head = block_idx is not None and block_idx.dim() == 3
+    if per_head and tuple(block_idx.shape[:2]) != (B, Hkv):
+        raise FdlError(2, "per-head block_idx must be [B, Hkv, C]")
+    C = 0 if block_idx is None else block_idx.shape[-1]
+    if sink_idx is not None and sink_idx.stride(1) != 1 or (block_idx is not None and block_idx.stride(-1) != 1):
         raise FdlError(2, "index tensors must be contiguous along their last axis")
     if sink_idx is not None and n_sinks and sink_idx.stride(0) != n_sinks:
         sink_idx = sink_idx.contiguous()
-    if block_idx is not None and C and block_idx.stride(0) != C:
+    if block_idx is not None and C and not block_idx.is_contiguous():
         block_idx = block_idx.contiguous()
     if out is None:
         out = torch.empty((B, Hq, nq_max, d), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, nq_max), dtype=torch.float32, device=q.device)
-    nbytes = int(lib().fdl_sparse_attention_workspace_bytes(dt, B, Hq, Hkv, L, P, d, nq_max, n_sinks, C, bs))
+    nbytes = int(lib().fdl_sparse_attention_ex_workspace_bytes(dt, B, Hq, Hkv, L, P, d, nq_max, n_sinks, C, bs,
+                                                                int(per_head)))
     ws, ws_n = _ws(workspace, q.device).get(nbytes)
-    st = lib().fdl_sparse_attention(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
-                                    _ptr(k), _strides4(k), _ptr(v), _strides4(v), *_vt(vt, v), _ptr(sink_idx), n_sinks,
-                                    _ptr(block_idx), C, int(bs), float(scale), _ptr(out), _strides4(out),
-                                    _ptr(lse), ws, ws_n, _stream(stream))
-    _check(st, "fdl_sparse_attention")
+    st = lib().fdl_sparse_attention_ex(dt, B, Hq, Hkv, L, P, d, _ptr(q), _strides4(q), qi, nqp, nq_max,
+                                       _ptr(k), _strides4(k), _ptr(v), _strides4(v), *_vt(vt, v), _ptr(sink_idx),
+                                       n_sinks, _ptr(block_idx), C, int(per_head), int(bs), float(scale), _ptr(out),
+                                       _strides4(out), _ptr(lse), ws, ws_n, _stream(stream))
+    _check(st, "fdl_sparse_attention_ex")
     return out, lse
 
 

@@ -14,6 +14,11 @@ second stream, one event per layer, while the layers before it attend on the
 caller's stream, and each layer's scoring waits for its own means.  Without it,
 each layer computes its means right before scoring them.
 
+Variants (Summary, "Independent weaknesses" and "Reproducibility"): dense_tail keeps the
+last layers of the stack dense on the active rows (Dream-like models need their last 4
+layers kept); per_head gives every KV head its own top-C blocks; aggregator "max" scores
+a block by its strongest query instead of the summed relevance.
+
 cached_step is the same step over an approximate KV cache ("Prerequisites",
 approximate KV cache): every layer first writes the recomputed keys and values
 of U(t) = I_active into its cache, then recomputes only the block means those
@@ -29,10 +34,11 @@ from . import fdl as F
 
 class StepRunner:
     def __init__(self, *, B, L, P, Hq, Hkv, d, dtype, n_t, rho, w, bs, C, n_sinks, layers, l_dense,
-                 scale=0.0, device="cuda", overlap_means=True):
+                 scale=0.0, device="cuda", overlap_means=True, dense_tail=0, per_head=False, aggregator="sum"):
         self.B, self.L, self.P, self.Hq, self.Hkv, self.d = B, L, P, Hq, Hkv, d
         self.n_t, self.rho, self.w, self.bs, self.C, self.n_sinks = n_t, rho, w, bs, C, n_sinks
         self.layers, self.l_dense, self.scale = layers, l_dense, scale
+        self.dense_tail, self.per_head, self.aggregator = dense_tail, per_head, aggregator
         self.k = F.focus_count(n_t, rho)
         self.nq_max = max(min(self.k * w, L), 1)
         dev = torch.device(device)
@@ -42,9 +48,10 @@ class StepRunner:
         self.active = torch.empty((B, self.nq_max), **i32)
         self.n_active = torch.empty((B,), **i32)
         self.sinks = torch.empty((B, max(n_sinks, 1)), **i32)
-        self.blocks = [torch.empty((B, max(C, 1)), **i32) for _ in range(layers)]
+        lead = (B, Hkv) if per_head else (B,)
+        self.blocks = [torch.empty(lead + (max(C, 1),), **i32) for _ in range(layers)]
         self.nb = -(-P // bs)
-        sparse_layers = range(l_dense, layers) if C else range(0)
+        sparse_layers = range(l_dense, layers - dense_tail) if C else range(0)
         self.kbar = {l: torch.empty((B, Hkv, self.nb, d), dtype=torch.float32, device=dev) for l in sparse_layers}
         self.overlap_means = overlap_means
         self.side = torch.cuda.Stream(device=dev) if dev.type == "cuda" and overlap_means else None
@@ -59,13 +66,18 @@ class StepRunner:
             lib.fdl_dense_attention_workspace_bytes(dt, B, Hq, Hkv, L, d, self.nq_max),
             lib.fdl_sink_identify_workspace_bytes(dt, B, Hq, Hkv, L, d, self.nq_max),
             lib.fdl_block_score_topc_workspace_bytes(dt, B, Hq, Hkv, P, d, bs, self.nq_max),
-            lib.fdl_sparse_attention_workspace_bytes(dt, B, Hq, Hkv, L, P, d, self.nq_max, n_sinks, C, bs),
+            lib.fdl_sparse_attention_ex_workspace_bytes(dt, B, Hq, Hkv, L, P, d, self.nq_max, n_sinks, C, bs,
+                                                        int(per_head)),
         )
         self.workspace.get(need)
 
     def _rows(self):
         return dict(q_idx=self.active, n_q=self.n_active, nq_max=self.nq_max, scale=self.scale,
                     workspace=self.workspace)
+
+    def is_dense(self, l):
+        """Layers 1..l_dense and the dense tail attend densely on the active rows."""
+        return l < self.l_dense or l >= self.layers - self.dense_tail
 
     def pcgi(self, conf, mask):
         F.pcgi_select(conf, mask, self.n_t, self.rho, self.w, k_cap=self.focus.shape[1], nq_max=self.nq_max,
@@ -81,12 +93,12 @@ class StepRunner:
     def score_blocks(self, l, q):
         """Block top-C of one sparse layer from its block means (already in self.kbar[l])."""
         F.block_score_topc(q, None, self.P, self.bs, self.C, kbar=self.kbar[l], L=self.L, out=self.blocks[l],
-                           **self._rows())
+                           per_head=self.per_head, aggregator=self.aggregator, **self._rows())
 
     def attend(self, l, q, k, v, vt=None):
         """Sparse attention of one layer over the step's sinks and the layer's selected blocks."""
         sinks = self.sinks[:, : self.n_sinks] if self.n_sinks else None
-        blocks = self.blocks[l][:, : self.C] if self.C else None
+        blocks = self.blocks[l][..., : self.C] if self.C else None
         F.sparse_attention(q, k, v, self.P, sinks, blocks, self.bs, vt=vt, out=self.out[l], **self._rows())
 
     def sparse_step(self, conf, mask, qs, ks, vs, hooks=None, vts=None):
@@ -116,7 +128,7 @@ class StepRunner:
         for l in range(self.layers):
             q, k, v = qs[l], ks[l], vs[l]
             vt = vts[l] if vts is not None else None
-            if l < self.l_dense:
+            if self.is_dense(l):
                 run("dense", lambda: self.dense_layer(l, q, k, v, vt))
                 if l == self.l_dense - 1:
                     run("sinks", lambda: self.sinks_at(q, k))
@@ -161,10 +173,10 @@ class StepRunner:
 
             def refresh():
                 F.kv_refresh(self.active, k_new[l], v_new[l], k, v, n_rows=self.n_active, vt=vt)
-                if l >= self.l_dense and self.C:
+                if l in self.kbar:
                     F.block_means_refresh(k, self.P, self.bs, self.active, self.kbar[l], n_rows=self.n_active)
             run("refresh", refresh)
-            if l < self.l_dense:
+            if self.is_dense(l):
                 run("dense", lambda: self.dense_layer(l, q, k, v, vt))
                 if l == self.l_dense - 1:
                     run("sinks", lambda: self.sinks_at(q, k))

@@ -288,3 +288,25 @@ def test_dcu_validation():
     assert call(xp=NULL) == 1 and call(out=NULL) == 1 and call(keys=NULL) == 1
     assert call(xn=MISALIGNED) == 4 and call(sp=S(0, 0, 4100)) == 4
     assert call(ws=NULL) == 5 and call(n=ws_n - 8) == 5
+
+
+def test_variant_entry_points_validation():
+    lib = F.lib()
+    st = S(32 * 32768 * 128, 32768 * 128, 128)
+    # a mode outside FDL_SCORE_PER_HEAD | FDL_SCORE_MAX, and blocks_per_head outside {0, 1}
+    ws = lib.fdl_block_score_topc_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32256, 128, 128, 1024)
+    for mode, status in ((4, 2), (-1, 2)):
+        assert lib.fdl_block_score_topc_ex(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128, FAKE, st, FAKE, FAKE, 1024,
+                                           FAKE, st, 0.0, 128, 64, mode, FAKE, NULL, NULL, FAKE, ws, None) == status
+    assert lib.fdl_sparse_attention_ex_workspace_bytes(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128, 1024, 16, 64,
+                                                       128, 2) == 0
+    z = S(0, 0, 0)
+    assert lib.fdl_sparse_attention_ex(F.FDL_BF16, 1, 32, 32, 32768, 32256, 128, FAKE, st, FAKE, FAKE, 1024,
+                                       FAKE, st, FAKE, st, NULL, z, FAKE, 16, FAKE, 64, 2, 128, 0.0, FAKE, st,
+                                       NULL, FAKE, 1 << 30, None) == 2
+    # per-head key lists: one list per (sequence, KV head) where the list path is taken
+    shared = lib.fdl_sparse_attention_ex_workspace_bytes(F.FDL_F32, 2, 8, 4, 4096, 4000, 64, 256, 8, 16, 64, 0)
+    ph = lib.fdl_sparse_attention_ex_workspace_bytes(F.FDL_F32, 2, 8, 4, 4096, 4000, 64, 256, 8, 16, 64, 1)
+    assert ph > shared
+    assert lib.fdl_sparse_attention_ex_workspace_bytes(F.FDL_F32, 2, 8, 4, 4096, 4000, 64, 256, 8, 16, 64, 0) == \
+        lib.fdl_sparse_attention_workspace_bytes(F.FDL_F32, 2, 8, 4, 4096, 4000, 64, 256, 8, 16, 64)

@@ -93,5 +93,15 @@ CTX32K_GQA_B4 = Workload(
     layers=28, l_dense=2, conf="beta25", steps=8,
     notes="batch of 4; one block-entry dense refresh then 7 sparse steps")
 
+# The pages' own hyper-parameters (Summary, "Reproducibility": rho = 4, w = 8, l_dense = 6,
+# blocks of 64, sparsity ratio alpha = 0.5, N_sinks = 0.01 M) on the 32K LLaDA-shaped stack:
+# nb = 504 blocks, of which alpha = 0.5 prunes 252 (C = 252), and N_sinks = floor(0.01 L) = 327.
+CTX32K_PAPER = Workload(
+    name="ctx32k_mha32_d128_bf16_paper_defaults", tag=6, dtype="bf16", B=1, P=32256, G=512,
+    masked=256, Hq=32, Hkv=32, d=128, n_t=16, rho=4.0, w=8, bs=64, C=252, n_sinks=327,
+    layers=32, l_dense=6, conf="beta25",
+    notes="the pages' default hyper-parameters at 32K, with all 327 sink positions injected")
+
 ALL = (TINY_2K_F32, CTX8K_MHA, CTX16K_GQA, CTX32K_STACK, CTX32K_GQA_B4)
-BY_NAME = {w.name: w for w in ALL}
+PRESETS = (CTX32K_PAPER,)
+BY_NAME = {w.name: w for w in ALL + PRESETS}
