@@ -51,6 +51,11 @@ def parse():
     ap.add_argument("--refresh-reps", type=int, default=3)
     ap.add_argument("--no-dcu", action="store_true", help="skip the dynamic cache update scoring measurement")
     ap.add_argument("--dcu-reps", type=int, default=20)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (8K, 16K, the 32K batch of 4, the pages' defaults)")
+    ap.add_argument("--config-reps", type=int, default=10)
+    ap.add_argument("--conf-only", action="store_true",
+                    help="only the confidence / unmask measurement (the run profiled for it)")
     ap.add_argument("--dcu-only", action="store_true",
                     help="only the dynamic cache update scoring measurement (the run profiled for it)")
     ap.add_argument("--serial-means", action="store_true",
@@ -67,44 +72,81 @@ def parse():
 
 # ------------------------------------------------------------------ accounting
 
-def step_accounting(wl, n_active, sinks, blocks_per_layer):
-    """Algorithmic HBM bytes and flops of every stage of one step (realised sets)."""
-    E = 2  # bf16
+def step_accounting(wl, n_active, sinks, blocks_per_layer, dense_tail=0, per_head=False):
+    """Algorithmic HBM bytes and flops of every stage of one step (realised sets).
+
+    `bytes` is what the method must move: every input read once and every output written
+    once.  The block means and the relevance parts are intermediates between two entry
+    points, and the queries that scoring reads are read again by the attention: those
+    extra bytes are counted in `io_bytes` only.  n_active, sinks and blocks_per_layer hold
+    one entry per sequence (blocks_per_layer[l][b], per KV head when per_head)."""
+    E = 2 if wl.dtype == "bf16" else 4
     d, Hq, Hkv, L, P = wl.d, wl.Hq, wl.Hkv, wl.L, wl.P
-    na = int(n_active)
-    q_rows = Hq * na * d * E
-    acc = {}
-    acc["pcgi"] = dict(bytes=L * 5 + na * 4, flops=0, calls=1)
-    kv_all = 2 * Hkv * L * d * E
-    acc["dense"] = dict(bytes=wl.l_dense * (kv_all + 2 * q_rows + Hq * na * 4),
-                        flops=wl.l_dense * 4 * na * L * d * Hq, calls=wl.l_dense)
-    acc["sinks"] = dict(bytes=Hkv * L * d * E + q_rows + Hq * na * 4 + L * 4,
-                        flops=2 * na * L * d * Hq, calls=1)
-    n_sparse = wl.layers - wl.l_dense
     nb = -(-P // wl.bs)
+    n_sparse = len(blocks_per_layer)
+    n_dense = wl.layers - n_sparse
+    acc = {k: dict(bytes=0, io_bytes=0, flops=0, calls=0) for k in ("pcgi", "dense", "sinks", "means", "blocks",
+                                                                      "sparse")}
+    acc["pcgi"]["calls"] = 1
+    acc["dense"]["calls"] = n_dense
+    acc["sinks"]["calls"] = 1
+    acc["means"]["calls"] = acc["blocks"]["calls"] = acc["sparse"]["calls"] = n_sparse
+    kv_all = 2 * Hkv * L * d * E
     scan = Hkv * P * d * E
-    # block means of every sparse layer: one read of the prompt keys, the means written
-    acc["means"] = dict(bytes=n_sparse * (scan + Hkv * nb * d * 4), flops=0, calls=n_sparse)
-    sb, sf, kb, kf = 0, 0, 0, 0
-    snk = set(int(s) for s in sinks if s >= 0)
-    for blocks in blocks_per_layer:
-        sel = [int(b) for b in blocks if b >= 0]
-        blk_keys = sum(min(wl.bs, P - b * wl.bs) for b in sel)
-        covered = set(b for b in sel)
-        extra = sum(1 for s in snk if s < P and s // wl.bs not in covered)
-        n_keys = blk_keys + (L - P) + extra
-        kb += Hkv * nb * d * 4 + q_rows + len(sel) * 4       # scoring reads the means and the queries
-        kf += 2 * Hq * na * d + 2 * Hkv * nb * d
-        sb += 2 * Hkv * n_keys * d * E + 2 * q_rows
-        sf += 4 * na * n_keys * d * Hq
-    acc["blocks"] = dict(bytes=kb, flops=kf, calls=n_sparse)
-    acc["sparse"] = dict(bytes=sb, flops=sf, calls=n_sparse)
+    for b in range(wl.B):
+        na = int(n_active[b])
+        q_rows = Hq * na * d * E
+        acc["pcgi"]["bytes"] += L * 5 + na * 4
+        acc["dense"]["bytes"] += n_dense * (kv_all + 2 * q_rows + Hq * na * 4)
+        acc["dense"]["flops"] += n_dense * 4 * na * L * d * Hq
+        acc["sinks"]["bytes"] += Hkv * L * d * E + q_rows + Hq * na * 4 + L * 4
+        acc["sinks"]["flops"] += 2 * na * L * d * Hq
+        acc["means"]["bytes"] += n_sparse * scan
+        acc["means"]["io_bytes"] += n_sparse * (scan + Hkv * nb * d * 4)
+        snk = set(int(x) for x in sinks[b] if x >= 0)
+        for layer_blocks in blocks_per_layer:
+            lists = layer_blocks[b] if per_head else [layer_blocks[b]] * Hkv
+            n_sel = 0
+            for g in range(Hkv):
+                sel = [int(x) for x in lists[g] if x >= 0]
+                n_sel += len(sel)
+                blk_keys = sum(min(wl.bs, P - x * wl.bs) for x in sel)
+                covered = set(sel)
+                extra = sum(1 for x in snk if x < P and x // wl.bs not in covered)
+                n_keys = blk_keys + (L - P) + extra
+                acc["sparse"]["bytes"] += 2 * n_keys * d * E
+                acc["sparse"]["flops"] += 4 * na * n_keys * d * (Hq // Hkv)
+            acc["sparse"]["bytes"] += 2 * q_rows                          # Q rows read, O rows written
+            acc["blocks"]["io_bytes"] += Hkv * nb * d * 4 + q_rows + n_sel * 4
+            acc["blocks"]["flops"] += 2 * Hq * na * d + 2 * Hkv * nb * d
+    for a in acc.values():
+        a["io_bytes"] = max(a["io_bytes"], a["bytes"])
+    acc["sparse"]["io_bytes"] = acc["sparse"]["bytes"]
     return acc
+
+
+def percentiles(samples):
+    import numpy as np
+    x = np.asarray(samples, dtype=np.float64)
+    return {"median": round(float(np.median(x)), 4), "p10": round(float(np.percentile(x, 10)), 4),
+            "p90": round(float(np.percentile(x, 90)), 4), "n": int(x.size)}
+
+
+def timed_replays(graph, stream, reps):
+    """Per-replay durations (ms) of a captured graph: one event between consecutive replays."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        graph.replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
 
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=0.25):
+def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=1.0, n_sparse_sample=16):
     """The fp64 oracle on a bounded sample of the step, timed on the host cores."""
     import numpy as np
     from oracle import focus_oracle as O
@@ -130,7 +172,9 @@ def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=0.25):
     t["sinks"] = (time.perf_counter() - t0) * scale_rows
     sinks = synth_sinks = None
     sparse_times = []
-    for l in (wl.l_dense, wl.layers - 1):
+    sample_layers = sorted(set(int(round(x)) for x in
+                               __import__("numpy").linspace(wl.l_dense, wl.layers - 1, n_sparse_sample)))
+    for l in sample_layers:
         Q, K, V = layer_host(l)
         t0 = time.perf_counter()
         R = O.block_relevance(Q[:, active], O.block_means(K, wl.P, wl.bs), wl.scale)
@@ -143,6 +187,30 @@ def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=0.25):
         O.sparse_attention(Q[:, active], K, V, I_p, wl.scale)
         sparse_times.append(time.perf_counter() - t0)
     t["sparse_layer"] = float(np.mean(sparse_times))
+    # the same stages on one thread (BLAS limited to one), on a smaller row sample
+    t1 = {}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            sub1 = active[: max(1, na // 16)]
+            s1 = na / len(sub1)
+            Q, K, V = layer_host(wl.l_dense - 1)
+            t0 = time.perf_counter()
+            _, lse1 = O.dense_attention(Q[:, sub1], K, V, wl.scale)
+            t1["dense_layer"] = (time.perf_counter() - t0) * s1
+            t0 = time.perf_counter()
+            O.sink_scores(Q[:, sub1], K, lse1, wl.scale)
+            t1["sinks"] = (time.perf_counter() - t0) * s1
+            Q, K, V = layer_host(wl.l_dense)
+            t0 = time.perf_counter()
+            R = O.block_relevance(Q[:, sub1], O.block_means(K, wl.P, wl.bs), wl.scale)
+            I_p = O.key_set(sinks, O.top_blocks(R, wl.C), wl.bs, wl.P, wl.L)
+            t_score = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            O.sparse_attention(Q[:, sub1], K, V, I_p, wl.scale)
+            t1["sparse_layer"] = t_score + (time.perf_counter() - t0) * s1
+    except ImportError:  # threadpoolctl missing: no single-thread figures
+        t1 = {}
     step_s = (t["pcgi"] + wl.l_dense * t["dense_layer"] + t["sinks"] +
               (wl.layers - wl.l_dense) * t["sparse_layer"])
     measured = t["pcgi"] + t["dense_layer"] / scale_rows + t["sinks"] / scale_rows + sum(sparse_times)
@@ -154,11 +222,14 @@ def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=0.25):
         "step_s_extrapolated": step_s,
         "measured_s": measured,
         "sample": (f"fp64 NumPy oracle on host: PCGI; layer {wl.l_dense} dense attention and sink scores "
-                   f"on {len(sub)} of {na} active rows (scaled x{scale_rows:.2f}); block top-C + sparse "
-                   f"attention of layers {wl.l_dense + 1} and {wl.layers} on all rows (mean x "
+                   f"on {len(sub)} of {na} active rows (scaled x{scale_rows:.2f}); block means, top-C and "
+                   f"sparse attention of layers {[l + 1 for l in sample_layers]} on all rows (mean x "
                    f"{wl.layers - wl.l_dense}); dense layers x{wl.l_dense}; sinks taken as the injected "
                    f"positions; extrapolated to one full step"),
         "stage_s": {k: round(v, 4) for k, v in t.items()},
+        "stage_s_one_thread": {k: round(v, 4) for k, v in t1.items()},
+        "one_thread_sample": "BLAS limited to one thread; 1/16 of the active rows, scaled (the block "
+                             "scoring of the sparse layer on those rows, unscaled)",
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
@@ -237,6 +308,9 @@ def main():
     F.fdl.lib()
     if args.dcu_only:
         print(json.dumps({"dcu": dcu_measurement(F, dev, torch.cuda.current_stream(), args)}), flush=True)
+        return
+    if args.conf_only:
+        print(json.dumps({"confidence_unmask": confidence_measurement(F, dev, args)}), flush=True)
         return
     t_setup = time.time()
     conf_np, mask_np = synth.step_inputs(wl)
@@ -374,8 +448,8 @@ def main():
     stage_ms = {k: [a.elapsed_time(b) / nsteps for a, b in v] for k, v in stage_events.items()}
     n_active = int(run.n_active[0])
     sinks = run.sinks[0, : wl.n_sinks].cpu().numpy()
-    blocks = [run.blocks[l][0, : wl.C].cpu().numpy() for l in range(wl.l_dense, wl.layers)]
-    acc = step_accounting(wl, n_active, sinks, blocks)
+    blocks = [[run.blocks[l][0, : wl.C].cpu().numpy()] for l in range(wl.l_dense, wl.layers)]
+    acc = step_accounting(wl, [n_active], [sinks], blocks)
     step_bytes = sum(a["bytes"] for a in acc.values())
     step_flops = sum(a["flops"] for a in acc.values())
     breakdown = {}
@@ -386,7 +460,7 @@ def main():
         breakdown[name] = {
             "calls": calls, "ms_total": round(tot, 4),
             "us_per_call": round(1000 * tot / max(calls, 1), 2),
-            "GBps": round(a["bytes"] / (tot / 1000) / 1e9, 1) if tot else None,
+            "GBps": round(a["io_bytes"] / (tot / 1000) / 1e9, 1) if tot else None,
             "TFLOPps": round(a["flops"] / (tot / 1000) / 1e12, 1) if tot and a["flops"] else None,
         }
     # the dominant entry point (largest share of the step) is sparse attention; its launches
@@ -398,6 +472,9 @@ def main():
     dom = "sparse"
     a = acc[dom]
     us_launch, n_launch = launch_timing(args.kernel_reps)
+    # the per-step spread: the step's replays again, one event between consecutive ones (after
+    # the launch timing, which earlier bench runs took right after the timed steps)
+    spread = percentiles(timed_replays(graph, stream, args.steps)) if mode == "graph" else None
     per_call_s = us_launch / 1e6
     bytes_call = a["bytes"] / a["calls"]
     flops_call = a["flops"] / a["calls"]
@@ -435,6 +512,7 @@ def main():
                    "l_dense": wl.l_dense, "k": run.k, "w": wl.w, "block": wl.bs, "top_c": wl.C,
                    "n_sinks": wl.n_sinks, "parallelism": "single GPU"},
         "step_us": round(ms * 1000, 1),
+        "ms_per_step_spread": spread,
         "pct_hbm_peak": round(100 * step_bytes / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 2),
         "timing": mode,
         "eager_ms_per_step_with_call_events": round(eager_ms, 4),
@@ -510,9 +588,212 @@ def main():
             "algorithmic_bytes": int(cbytes), "refreshed_rows": na, "prompt_blocks_touched": touched,
             "note": "each layer refreshes the active rows of its KV cache and the block means they touch "
                     "right before attending, instead of the full per-layer means scan; not the headline workload"}
+    del qs, ks, vs, vts, run
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = other_configs(F, dev, args)
+        result["peaks_measured"] = achievable_peaks(dev)
+        result["confidence_unmask"] = confidence_measurement(F, dev, args)
     if not args.no_dcu:
         result["dcu"] = dcu_measurement(F, dev, stream, args)
     print(json.dumps(result), flush=True)
+
+
+def roof(bytes_, flops, seconds):
+    """The bound of a launch (larger of bytes / HBM peak and flops / bf16 peak) and the
+    fraction of it reached in `seconds`."""
+    if flops / (BF16_PEAK_TFLOPS * 1e12) > bytes_ / (HBM_PEAK_GBS * 1e9):
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4)}
+    ach = bytes_ / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
+def measure_config(F, dev, wl, args, *, step=0, refresh=False):
+    """One sparse step of workload `wl` as bench.py times the headline: inputs resident, the
+    step captured in a HIP graph and replayed; then the sparse layers' attention alone, and
+    optionally one layer's block-entry dense refresh.  A one-layer workload runs its layer
+    both ways (dense with the sinks, then scored and attended sparsely)."""
+    import numpy as np
+    import torch
+    from long_context_diffusion_amd.step import StepRunner
+    from workloads import synth
+    t0 = time.time()
+    if step == 0:
+        conf_np, mask_np = synth.step_inputs(wl)
+    else:
+        states = [synth.scenario(wl, b)[step] for b in range(wl.B)]
+        conf_np = np.stack([c for _, c in states])
+        mask_np = np.stack([m.astype(np.uint8) for m, _ in states])
+    conf = torch.from_numpy(np.ascontiguousarray(conf_np)).to(dev)
+    mask = torch.from_numpy(np.ascontiguousarray(mask_np)).to(dev)
+    one = wl.layers == wl.l_dense == 1
+    n_layers = 2 if one else wl.layers
+    qs, ks, vs = [], [], []
+    for l in range(wl.layers):
+        k, v = synth.make_kv(wl, l, dev)
+        ks.append(k)
+        vs.append(v)
+        qs.append(synth.make_q(wl, l, step, dev))
+    if one:
+        qs, ks, vs = qs * 2, ks * 2, vs * 2
+    vts = [F.transpose_v(v) for v in vs[: wl.layers]]
+    if one:
+        vts = vts * 2
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    run = StepRunner(B=wl.B, L=wl.L, P=wl.P, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, dtype=dt, n_t=wl.n_t, rho=wl.rho,
+                     w=wl.w, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks, layers=n_layers, l_dense=wl.l_dense,
+                     scale=wl.scale, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        run.sparse_step(conf, mask, qs, ks, vs, vts=vts)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.sparse_step(conf, mask, qs, ks, vs, vts=vts)
+    g.replay()
+    torch.cuda.synchronize()
+    samples = timed_replays(g, stream, args.config_reps)
+    ms = float(np.mean(samples))
+    sparse_layers = list(range(wl.l_dense, n_layers))
+    n_active = run.n_active.cpu().numpy()
+    sinks = run.sinks[:, : wl.n_sinks].cpu().numpy()
+    blocks = [run.blocks[l][:, : wl.C].cpu().numpy() for l in sparse_layers]
+    acc = step_accounting(dataclass_layers(wl, n_layers), n_active, sinks, blocks)
+    step_bytes = sum(a["bytes"] for a in acc.values())
+    step_flops = sum(a["flops"] for a in acc.values())
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        for l in sparse_layers:
+            run.attend(l, qs[l], ks[l], vs[l], vts[l])
+    ga.replay()
+    torch.cuda.synchronize()
+    a_samples = timed_replays(ga, stream, args.config_reps)
+    us_call = 1000.0 * float(np.median(a_samples)) / len(sparse_layers)
+    sp = acc["sparse"]
+    res = {
+        "workload": wl.name, "batch": wl.B, "seq_len": wl.L, "heads_q_kv": [wl.Hq, wl.Hkv], "head_dim": wl.d,
+        "dtype": wl.dtype, "layers": wl.layers, "l_dense": wl.l_dense, "k": run.k, "w": wl.w, "block": wl.bs,
+        "top_c": wl.C, "n_sinks": wl.n_sinks, "step": step, "n_active": [int(x) for x in n_active],
+        "ms_per_step": round(ms, 4), "ms_per_step_spread": percentiles(samples),
+        "step_algorithmic_bytes": int(step_bytes), "step_algorithmic_flops": int(step_flops),
+        "GBps": round(step_bytes / (ms / 1000) / 1e9, 1),
+        "pct_hbm_peak": round(100 * step_bytes / (ms / 1000) / 1e9 / HBM_PEAK_GBS, 2),
+        "TFLOPps": round(step_flops / (ms / 1000) / 1e12, 1),
+        "sparse_attention": dict(roof(sp["bytes"] / sp["calls"], sp["flops"] / sp["calls"], us_call / 1e6),
+                                 us_per_call=round(us_call, 2), calls_per_replay=len(sparse_layers),
+                                 replays=len(a_samples)),
+    }
+    if one:
+        res["note"] = "one layer, run both ways: dense on the active rows with the sinks, then scored and sparse"
+    if refresh:
+        out = torch.empty_like(qs[0])
+        F.dense_attention(qs[0], ks[0], vs[0], vt=vts[0], out=out, want_lse=False, scale=wl.scale)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        F.dense_attention(qs[0], ks[0], vs[0], vt=vts[0], out=out, want_lse=False, scale=wl.scale)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1)
+        rflops = 4.0 * wl.B * wl.L * wl.L * wl.d * wl.Hq
+        res["dense_refresh"] = {"ms_per_layer": round(rms, 3), "TFLOPps": round(rflops / (rms / 1000) / 1e12, 1),
+                                "frac_bf16_peak": round(rflops / (rms / 1000) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                "flops_per_layer": rflops}
+        del out
+    res["setup_and_timing_s"] = round(time.time() - t0, 1)
+    del qs, ks, vs, vts, run, g, ga
+    torch.cuda.empty_cache()
+    return res
+
+
+def dataclass_layers(wl, layers):
+    import dataclasses
+    return dataclasses.replace(wl, layers=layers)
+
+
+def other_configs(F, dev, args):
+    """The 8K and 16K one-layer workloads, the 32K Dream-shaped batch of 4 (a sparse step
+    after the block entry, and one layer of its dense refresh) and the pages' default
+    hyper-parameters on the 32K stack."""
+    import torch
+    from workloads import configs
+    out = {}
+    for wl, kw in ((configs.CTX8K_MHA, {}), (configs.CTX16K_GQA, {}),
+                   (configs.CTX32K_GQA_B4, dict(step=1, refresh=True)), (configs.CTX32K_PAPER, {})):
+        print(f"# config {wl.name}", file=sys.stderr, flush=True)
+        out[wl.name] = measure_config(F, dev, wl, args, **kw)
+        torch.cuda.empty_cache()
+    return out
+
+
+def achievable_peaks(dev):
+    """Rates that library kernels reach on this GPU: a streaming read (torch's sum of 4 GiB of
+    bf16) and a bf16 GEMM (torch.mm, 8192^3, hipBLASLt)."""
+    import torch
+    x = torch.empty(1 << 31, dtype=torch.bfloat16, device=dev).normal_()
+    x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = x.numel() * 2 / (e0.elapsed_time(e1) / reps / 1000) / 1e9
+    del x
+    n = 8192
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    tf = 2.0 * n ** 3 / (e0.elapsed_time(e1) / reps / 1000) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"stream_read_GBps": round(read_gbs, 1), "stream_read_frac_of_8000": round(read_gbs / HBM_PEAK_GBS, 4),
+            "bf16_gemm_TFLOPps": round(tf, 1), "bf16_gemm_frac_of_2500": round(tf / BF16_PEAK_TFLOPS, 4),
+            "kernels": "torch.sum over 4 GiB bf16; torch.mm bf16 8192 x 8192 x 8192"}
+
+
+def confidence_measurement(F, dev, args):
+    """fdl_confidence_unmask on the 32K step's masked rows: 256 rows of logits over a
+    126464-token vocabulary (LLaDA-8B's), bf16, n(t) = 16.  Algorithmic bytes: the logits
+    read once."""
+    import torch
+    from workloads import synth
+    B, M, V, L = 1, 256, 126464, 32768
+    logits = synth.make_logits(B, M, V, seed=5, device=dev)
+    pos = torch.arange(L - M, L, dtype=torch.int32, device=dev).reshape(1, M)
+    mask = torch.ones((B, L), dtype=torch.uint8, device=dev)
+    conf = torch.zeros((B, L), dtype=torch.float32, device=dev)
+    ws = F.Workspace(dev)
+    stream = torch.cuda.current_stream()
+    F.confidence_unmask(logits, pos, mask, conf, 16, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    reps = 20
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream)
+    for i in range(reps):
+        mask.fill_(1)
+        F.confidence_unmask(logits, pos, mask, conf, 16, workspace=ws, stream=stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    # each interval holds one small fill kernel besides the call
+    us = [1000.0 * evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    import numpy as np
+    med = float(np.median(us))
+    nbytes = B * M * V * 2
+    return {"workload": f"{M} masked rows x {V} vocabulary, bf16, n(t) = 16", "us_per_call_median": round(med, 2),
+            "us_spread": percentiles(us), "algorithmic_bytes": nbytes,
+            "roofline": roof(nbytes, 0, med / 1e6), "note": "each timed interval also holds a mask fill kernel"}
 
 
 def dcu_measurement(F, dev, stream, args):

@@ -28,7 +28,6 @@ struct AttnArgs {
     int n_sinks;
     const int32_t* block_idx;  // [B, C], or [B, Hkv, C] with blk_per_head
     int C, bs, nb;
-    int blk_per_head;      // 1: one block list (and key set) per KV head
     uint32_t bs_magic;     // ceil(2^32 / bs) for bs >= 2: division by bs as a multiply-high
     int n_splits;          // key-range splits (upper bound when dyn); > 1: partials combined by attn_merge
     int tiles_per_split;   // key tiles per split (static plans)
@@ -41,6 +40,7 @@ struct AttnArgs {
     int32_t* n_keys;       // [lists] |I_p| (sparse)
     float* part_o;         // [B*Hq*nq_max][n_splits][d] unnormalised fp32 outputs
     float* part_ml;        // [B*Hq*nq_max][n_splits][2] running max (log2 domain) and sum
+    int blk_per_head;      // 1: one block list (and key set) per KV head
 };
 
 // The key set of (sequence b, KV head g): one per sequence, or one per KV head of each

@@ -39,7 +39,8 @@ namespace fdl {
 
 namespace {
 
-template <int MODE>
+// PER_HEAD (kSparseLds only): every KV head maps its own block list
+template <int MODE, bool PER_HEAD = false>
 __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
     constexpr int NQC = 8;   // 16-wide d chunks of Q . K
     constexpr int NDB = 4;   // 32-wide d blocks of the output
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         int n_keys = a.L, n_blk = 0, sink0 = a.L;
         const int32_t* klist = nullptr;
         if (MODE == kSparseLds) {
-            build_key_map<512>(a, b, g, s_blk, s_unc, s_tmp, s_tmp64, reinterpret_cast<int*>(s_raw), n_blk, sink0, n_keys);
+            build_key_map<512, PER_HEAD>(a, b, g, s_blk, s_unc, s_tmp, s_tmp64, reinterpret_cast<int*>(s_raw), n_blk, sink0, n_keys);
             // the Q rows have landed in this wave's staging area: fragments to registers, then
             // every wave is done with the staging areas before tile loads overwrite them
             __builtin_amdgcn_s_waitcnt(0);
@@ -601,6 +602,8 @@ hipError_t launch_attn_bf16_d128(const AttnArgs& args, hipStream_t stream) {
         if (!ok) a.vt = nullptr;
     }
     if (!a.sparse) hipLaunchKernelGGL(attn_d128_kernel<kDense>, grid, dim3(512), 0, stream, a);
+    else if (sparse_map_in_lds(a) && a.blk_per_head)
+        hipLaunchKernelGGL((attn_d128_kernel<kSparseLds, true>), grid, dim3(512), 0, stream, a);
     else if (sparse_map_in_lds(a)) hipLaunchKernelGGL(attn_d128_kernel<kSparseLds>, grid, dim3(512), 0, stream, a);
     else hipLaunchKernelGGL(attn_d128_kernel<kSparseList>, grid, dim3(512), 0, stream, a);
     return hipGetLastError();

@@ -92,13 +92,14 @@ __device__ __forceinline__ float xhalf(float x) {
 // ascending, then padding) are recognised with one reduction and mapped as they stand; any
 // other list is brought to canonical form (canonical_ids: sorted and de-duplicated in LDS,
 // with `scratch`, at least 1024 ints of LDS, as the sort's scratch).  Every thread of the
-// block calls it, THREADS of them; C and n_sinks are at most 1024.
-template <int THREADS>
+// block calls it, THREADS of them; C and n_sinks are at most 1024.  PER_HEAD: the block list
+// of KV head g (a.blk_per_head), else the sequence's one list.
+template <int THREADS, bool PER_HEAD>
 __device__ inline void build_key_map(const AttnArgs& a, int b, int g, int* s_blk, int* s_unc, int* s_tmp,
                                      uint64_t* s_tmp64, int* scratch, int& n_blk, int& sink0, int& n_keys) {
     constexpr int EPT = 1024 / THREADS;   // entries of each list per thread
     const int tid = threadIdx.x;
-    const int32_t* blk_g = a.block_idx + static_cast<int64_t>(list_of(a, b, g)) * a.C;
+    const int32_t* blk_g = a.block_idx + static_cast<int64_t>(PER_HEAD ? b * a.Hkv + g : b) * a.C;
     const int32_t* snk_g = a.sink_idx + static_cast<int64_t>(b) * a.n_sinks;
     int sv[EPT];
     uint64_t packed = 0;   // bad entries << 40 | valid block ids << 20 | valid sinks

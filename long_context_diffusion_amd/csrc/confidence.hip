@@ -25,6 +25,7 @@ namespace {
 constexpr int kChunk = 8192;          // logits per partial workgroup
 constexpr int kPartThreads = 256;
 constexpr int kSelThreadsU = 1024;
+constexpr int kFoldBatch = 8;         // chunk parts loaded together per row
 constexpr float kLog2eU = 1.44269504088896340736f;
 
 struct Part {   // one chunk of one row
@@ -157,22 +158,37 @@ __global__ __launch_bounds__(kSelThreadsU) void conf_select_kernel(const Part* p
     uint8_t* mb = mask + static_cast<int64_t>(b) * L;
     // combine the chunks of each row in chunk order; s_pos = -1 marks rows that are not
     // candidates (position outside [0, L) or no longer masked)
+    int n_cand_local = 0;
     for (int r = tid; r < n; r += kSelThreadsU) {
         const Part* pr = parts + (static_cast<int64_t>(b) * m_max + r) * n_chunks;
-        Part q = pr[0];
-        float M = q.m, S = q.s;
-        int A = q.arg;
-        for (int c = 1; c < n_chunks; ++c) {
-            q = pr[c];
-            fold(M, S, A, q.m, q.s, q.arg);
+        float M = -INFINITY, S = 0.0f;
+        int A = 0x7fffffff;
+        // the chunks' parts in batches of independent loads, folded in chunk order
+        for (int c0 = 0; c0 < n_chunks; c0 += kFoldBatch) {
+            Part q[kFoldBatch];
+#pragma unroll
+            for (int u = 0; u < kFoldBatch; ++u) q[u] = pr[min(c0 + u, n_chunks - 1)];
+#pragma unroll
+            for (int u = 0; u < kFoldBatch; ++u) {
+                if (c0 + u >= n_chunks) break;
+                if (c0 + u == 0) {
+                    M = q[u].m;
+                    S = q[u].s;
+                    A = q[u].arg;
+                } else {
+                    fold(M, S, A, q[u].m, q[u].s, q[u].arg);
+                }
+            }
         }
         const int p = pb[r];
         const bool cand = p >= 0 && p < L && mb[p] != 0;
         s_c[r] = 1.0f / S;
         s_tok[r] = A;
         s_pos[r] = cand ? p : -1;
+        n_cand_local += cand ? 1 : 0;
     }
-    __syncthreads();
+    int n_cand;
+    block_exclusive_sum(n_cand_local, sm.tmp, &n_cand);   // also orders the row writes
     // the n(t) most confident candidates; rows are ranked by (c, lower position) through
     // distinct 64-bit keys and written in row order
     auto key_of = [&](int j, uint64_t* key) -> bool {
@@ -181,7 +197,18 @@ __global__ __launch_bounds__(kSelThreadsU) void conf_select_kernel(const Part* p
         return p >= 0;
     };
     const int cap = min(max(n_t, 0), kMaxConfRows);
-    const int nsel = block_emit_topk<uint64_t>(n, cap, key_of, [](int j) { return j; }, s_sel, cap, &sm);
+    int nsel;
+    if (n <= kSelThreadsU) {
+        // up to one row per thread: rank by the distinct keys; rows that are not candidates
+        // get key 0, below every candidate's, and at most n_cand rows are taken
+        auto key_rank = [&](int j) -> uint64_t {
+            uint64_t k;
+            return key_of(j, &k) ? k : 0ull;
+        };
+        nsel = block_topk_distinct(n, min(cap, n_cand), key_rank, [](int j) { return j; }, s_sel, cap, &sm);
+    } else {
+        nsel = block_emit_topk<uint64_t>(n, cap, key_of, [](int j) { return j; }, s_sel, cap, &sm);
+    }
     __syncthreads();
     for (int i = tid; i < nsel; i += kSelThreadsU) s_tok[s_sel[i]] |= static_cast<int>(0x80000000u);   // selected flag
     __syncthreads();
