@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cached-means", action="store_true",
                     help="skip the step variant that refreshes the KV cache and its touched block means")
     ap.add_argument("--refresh-reps", type=int, default=3)
+    ap.add_argument("--means-ahead", type=int, default=0,
+                    help="side-stream block means run this many sparse layers ahead (0: all at the step start)")
     ap.add_argument("--no-dcu", action="store_true", help="skip the dynamic cache update scoring measurement")
     ap.add_argument("--dcu-reps", type=int, default=20)
     ap.add_argument("--no-configs", action="store_true",
@@ -331,7 +333,8 @@ def main():
     run = StepRunner(B=wl.B, L=wl.L, P=wl.P, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d, dtype=torch.bfloat16,
                      n_t=wl.n_t, rho=wl.rho, w=wl.w, bs=wl.bs, C=wl.C, n_sinks=wl.n_sinks,
                      layers=wl.layers, l_dense=wl.l_dense, scale=wl.scale, device=dev,
-                     overlap_means=not args.serial_means)
+                     overlap_means=not args.serial_means,
+                     means_ahead=args.means_ahead if args.means_ahead > 0 else None)
     stream = torch.cuda.current_stream()
 
     def step(hooks=None):

@@ -169,7 +169,7 @@ fdl_status fdl_sink_identify(fdl_dtype dtype, int B, int Hq, int Hkv, int L, int
  * caller may compute them for every layer ahead of the layers that score them.
  *   k, ks   [B, Hkv, L, d] with strides ks (rows 0..P-1 are read)
  *   P, bs   prompt length (1 <= P <= L), block size (>= 1)
- *   kbar    [B, Hkv, nb, d] fp32 out, dense; each mean is summed in fp64 and rounded
+ *   kbar    [B, Hkv, nb, d] fp32 out, dense, 16-byte aligned (FDL_ERR_ALIGN); each mean is summed in fp64 and rounded
  *           once.  The sum is exact, hence the mean correctly rounded, while the binary
  *           exponents of a block's nonzero keys span at most 29 - log2(bs) (fp32) or
  *           45 - log2(bs) (bf16)
@@ -194,7 +194,8 @@ fdl_status fdl_block_means(fdl_dtype dtype, int B, int Hkv, int L, int P, int d,
  *   P, bs, C   prompt length (P <= L), block size (>= 1), blocks kept (>= 0)
  *   block_idx  [B, C] out, ascending, -1 padded when C > nb
  *   R          [B, nb] fp64 out, or NULL
- *   kbar       [B, Hkv, nb, d] fp32 block means: out (k given) or in (k NULL), or NULL
+ *   kbar       [B, Hkv, nb, d] fp32 block means: out (k given) or in (k NULL), or NULL;
+ *              16-byte aligned when given (FDL_ERR_ALIGN)
  * The workspace holds each KV head's part of R, R, and the block means when k is
  * given and kbar is NULL; its size does not depend on nq_max.
  */

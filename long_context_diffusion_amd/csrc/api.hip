@@ -216,6 +216,7 @@ fdl_status fdl_block_means(fdl_dtype dt, int B, int Hkv, int L, int P, int d, co
     if (st != FDL_OK) return st;
     if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
     if (!kbar) return FDL_ERR_NULL;
+    if (!aligned16(kbar)) return FDL_ERR_ALIGN;
     if (P < 1 || P > L || bs < 1) return FDL_ERR_SHAPE;
     BlockArgs a{};
     a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
@@ -244,6 +245,7 @@ fdl_status fdl_block_score_topc_ex(fdl_dtype dt, int B, int Hq, int Hkv, int L, 
     if (k && (st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
     if (!k && !kbar) return FDL_ERR_NULL;
     if (!block_idx) return FDL_ERR_NULL;
+    if (kbar && !aligned16(kbar)) return FDL_ERR_ALIGN;
     if (P < 1 || P > L || bs < 1 || C < 0) return FDL_ERR_SHAPE;
     if (mode < 0 || mode > (FDL_SCORE_PER_HEAD | FDL_SCORE_MAX)) return FDL_ERR_SHAPE;
     if ((st = check_ws(ws, ws_bytes, block_workspace_bytes(B, Hq, Hkv, P, d, bs, nq_max))) != FDL_OK) return st;
@@ -364,6 +366,7 @@ fdl_status fdl_block_means_refresh(fdl_dtype dt, int B, int Hkv, int L, int P, i
     if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
     if (P < 1 || P > L || bs < 1 || n_max < 0) return FDL_ERR_SHAPE;
     if (!kbar) return FDL_ERR_NULL;
+    if (!aligned16(kbar)) return FDL_ERR_ALIGN;
     if (n_max == 0) return FDL_OK;
     if (!rows) return FDL_ERR_NULL;
     CacheArgs a{};

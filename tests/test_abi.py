@@ -310,3 +310,11 @@ def test_variant_entry_points_validation():
     assert ph > shared
     assert lib.fdl_sparse_attention_ex_workspace_bytes(F.FDL_F32, 2, 8, 4, 4096, 4000, 64, 256, 8, 16, 64, 0) == \
         lib.fdl_sparse_attention_workspace_bytes(F.FDL_F32, 2, 8, 4, 4096, 4000, 64, 256, 8, 16, 64)
+
+
+def test_block_means_alignment():
+    lib = F.lib()
+    st = S(32 * 32768 * 128, 32768 * 128, 128)
+    assert lib.fdl_block_means(F.FDL_BF16, 1, 32, 32768, 32256, 128, FAKE, st, 128, MISALIGNED, None) == 4
+    assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 32, 32768, 32256, 128, FAKE, st, 128, FAKE, NULL, 8,
+                                       MISALIGNED, None) == 4
