@@ -389,7 +389,9 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 }
                 raw_next = !vt2;
                 const int valid_here = n_keys - t * 64;
-                if (valid_here < 64) {
+                // only the last tile of a key range is short: a real, rare branch (if-converted,
+                // its 32 compares and selects ran on every tile)
+                if (__builtin_expect(valid_here < 64, 0)) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
