@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (8K, 16K, the 32K batch of 4, the pages' defaults)")
     ap.add_argument("--config-reps", type=int, default=10)
+    ap.add_argument("--refresh-only", action="store_true",
+                    help="only the block-entry dense refresh of one layer (the run profiled for MFMA counters)")
     ap.add_argument("--conf-only", action="store_true",
                     help="only the confidence / unmask measurement (the run profiled for it)")
     ap.add_argument("--dcu-only", action="store_true",
@@ -242,7 +244,7 @@ def cpu_baseline(wl, conf, mask, layer_host, step_bytes, rows_frac=1.0, n_sparse
 # HBM bytes per sparse-attention launch, measured with hardware counters and kept
 # as text beside the profiles; it only applies to the kernel sources it was taken on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attention_ctx32k_traffic.md")
-KERNEL_SOURCES = ("attention_d128.hip", "attention.hip", "attention.cuh", "common.cuh")
+KERNEL_SOURCES = ("attention_d128.hip", "attention_tiles.cuh", "attention.hip", "attention.cuh", "common.cuh")
 
 
 def kernel_sources_sha256():
@@ -313,6 +315,25 @@ def main():
         return
     if args.conf_only:
         print(json.dumps({"confidence_unmask": confidence_measurement(F, dev, args)}), flush=True)
+        return
+    if args.refresh_only:
+        q = synth.make_q(wl, 0, 0, dev)
+        k, v = synth.make_kv(wl, 0, dev)
+        vt = F.transpose_v(v)
+        out = torch.empty_like(q)
+        F.dense_attention(q, k, v, vt=vt, out=out, want_lse=False, scale=wl.scale)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.refresh_reps):
+            F.dense_attention(q, k, v, vt=vt, out=out, want_lse=False, scale=wl.scale)
+        e1.record()
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / args.refresh_reps
+        rflops = 4.0 * wl.L * wl.L * wl.d * wl.Hq
+        print(json.dumps({"dense_refresh": {"ms_per_layer": round(rms, 3),
+                                            "TFLOPps": round(rflops / (rms / 1000) / 1e12, 1),
+                                            "reps": args.refresh_reps}}), flush=True)
         return
     t_setup = time.time()
     conf_np, mask_np = synth.step_inputs(wl)

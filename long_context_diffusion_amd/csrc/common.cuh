@@ -266,6 +266,40 @@ __device__ __forceinline__ void wave_count(int* hist, int digit, bool on) {
     if ((pending >> lane) & 1ull) atomicAdd(&hist[digit], 1);
 }
 
+// One digit of a radix select: with every wave's histogram of the current digit in
+// sm->hist (complete: the caller synchronised), finds the digit of the *remaining-th largest
+// key and the rank left within it (*remaining updated), in every thread.  Three barriers;
+// the histograms are free again on return.
+__device__ inline int radix_pick_digit(SelectSmem* sm, int* remaining) {
+    const int nw = blockDim.x / kWave;
+    if (threadIdx.x < kWave) {
+        // lane l owns bins 4l..4l+3; find the bin holding the remaining-th largest
+        const int l = threadIdx.x;
+        int h[4] = {0, 0, 0, 0};
+        for (int w = 0; w < nw; ++w)
+            for (int q = 0; q < 4; ++q) h[q] += sm->hist[w][4 * l + q];
+        const int mine = h[0] + h[1] + h[2] + h[3];
+        int suffix = mine;  // sum over lanes >= l
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_down(suffix, off, kWave);
+            if (l + off < kWave) suffix += y;
+        }
+        int above = suffix - mine;
+        for (int q = 3; q >= 0; --q) {
+            if (above < *remaining && *remaining <= above + h[q]) {
+                sm->digit = 4 * l + q;
+                sm->remaining = *remaining - above;
+            }
+            above += h[q];
+        }
+    }
+    __syncthreads();
+    const int dgt = sm->digit;
+    *remaining = sm->remaining;
+    __syncthreads();
+    return dgt;
+}
+
 // Radix select: the k-th largest ordered key among the valid entries of [0, n)
 // (1 <= k <= number of valid entries).  Every thread of the block must call it.
 template <typename U, typename KeyFn>
@@ -284,33 +318,9 @@ __device__ U block_kth_largest(int n, int k, KeyFn key_of, SelectSmem* sm) {
             wave_count(sm->hist[wv], static_cast<int>((kj >> shift) & 0xff), (kj & prefix_mask) == prefix);
         });
         __syncthreads();
-        if (threadIdx.x < kWave) {
-            // lane l owns bins 4l..4l+3; find the bin holding the remaining-th largest
-            const int l = threadIdx.x;
-            int h[4] = {0, 0, 0, 0};
-            for (int w = 0; w < nw; ++w)
-                for (int q = 0; q < 4; ++q) h[q] += sm->hist[w][4 * l + q];
-            const int mine = h[0] + h[1] + h[2] + h[3];
-            int suffix = mine;  // sum over lanes >= l
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int y = __shfl_down(suffix, off, kWave);
-                if (l + off < kWave) suffix += y;
-            }
-            int above = suffix - mine;
-            for (int q = 3; q >= 0; --q) {
-                if (above < remaining && remaining <= above + h[q]) {
-                    sm->digit = 4 * l + q;
-                    sm->remaining = remaining - above;
-                }
-                above += h[q];
-            }
-        }
-        __syncthreads();
-        const int dgt = sm->digit;
-        remaining = sm->remaining;
+        const int dgt = radix_pick_digit(sm, &remaining);
         prefix |= static_cast<U>(dgt) << shift;
         prefix_mask |= static_cast<U>(0xff) << shift;
-        __syncthreads();
     }
     return prefix;
 }

@@ -165,6 +165,134 @@ __device__ __forceinline__ double block_sum_f64(double x, double* s_tmp) {
 
 __device__ __forceinline__ bool bit_set(const uint32_t* bits, int j) { return (bits[j >> 5] >> (j & 31)) & 1u; }
 
+constexpr int kRegKeys = 32;   // positions per thread held in registers (L up to 32768)
+
+// Takes the mandatory positions of [lo, hi) and the `budget` other positions of largest key
+// (the lower position first among equal keys; all of them when there are fewer), and
+// writes them ascending to out; *count gets their number.  `key(e)` and `mand(e)` describe
+// position lo + e; every thread of the block calls it.  The radix select runs over
+// `for_each(body)`, which calls body(key, valid) for every position of the thread.
+template <typename ForEach, typename Emit>
+__device__ inline void budget_select(ForEach for_each, Emit emit, int n_mand_local, int span, int L, int budget,
+                                     int32_t* out, int32_t* count, SelectSmem* sm) {
+    int n_mand;
+    block_exclusive_sum(n_mand_local, sm->tmp, &n_mand);
+    const int n_other = L - n_mand;
+    const bool take_all = budget >= n_other;
+    const int nsel = take_all ? n_other : max(budget, 0);
+    uint32_t thr = 0;
+    const int wv = threadIdx.x / kWave;
+    if (!take_all && nsel > 0) {
+        // radix select of the nsel-th largest key among the valid positions, 8 bits a pass
+        uint32_t prefix = 0, prefix_mask = 0;
+        int remaining = nsel;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = threadIdx.x; i < kMaxWaves * 256; i += blockDim.x) sm->hist[i / 256][i % 256] = 0;
+            __syncthreads();
+            for_each([&](uint32_t kj, bool ok) {
+                wave_count(sm->hist[wv], static_cast<int>((kj >> shift) & 0xff), ok && (kj & prefix_mask) == prefix);
+            });
+            __syncthreads();
+            const int dgt = radix_pick_digit(sm, &remaining);
+            prefix |= static_cast<uint32_t>(dgt) << shift;
+            prefix_mask |= 0xffu << shift;
+        }
+        thr = prefix;
+    }
+    int gt = 0, eq = 0;
+    if (nsel > 0 && !take_all) {
+        for_each([&](uint32_t kj, bool ok) {
+            gt += ok && kj > thr ? 1 : 0;
+            eq += ok && kj == thr ? 1 : 0;
+        });
+    }
+    int gt_total, eq_total;
+    block_exclusive_sum(gt, sm->tmp, &gt_total);
+    const int eq_before = block_exclusive_sum(eq, sm->tmp, &eq_total);
+    const int ties_taken = nsel - gt_total;   // ties go to the lower positions
+    const int my_ties = take_all || nsel == 0 ? 0 : min(max(ties_taken - eq_before, 0), eq);
+    const int my_other = take_all ? (span - n_mand_local) : (nsel == 0 ? 0 : gt + my_ties);
+    int n_total;
+    const int pos = block_exclusive_sum(n_mand_local + my_other, sm->tmp, &n_total);
+    emit(pos, take_all, nsel, thr, eq_before, ties_taken, out);
+    if (threadIdx.x == 0) *count = n_total;
+}
+
+// Positions with their keys and mandatory bits in registers (at most kRegKeys per thread).
+__device__ inline void select_from_registers(const float* dl, const uint32_t* s_mand, int lo, int hi, int L,
+                                             int budget, int32_t* out, int32_t* count, SelectSmem* sm) {
+    uint32_t key[kRegKeys];
+    uint32_t mand = 0, live = 0;   // bit e: position lo + e is mandatory / exists
+    const int span = hi - lo;
+    if (span == kRegKeys && (lo & 31) == 0 && (reinterpret_cast<uintptr_t>(dl + lo) & 15) == 0) {
+        // a whole 32-bit word of the bitmask, 16-byte loads
+        const f32x4* src = reinterpret_cast<const f32x4*>(dl + lo);
+#pragma unroll
+        for (int v = 0; v < kRegKeys / 4; ++v) {
+            const f32x4 x = src[v];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) key[4 * v + i] = __float_as_uint(x[i]);
+        }
+        mand = s_mand[lo >> 5];
+        live = 0xffffffffu;
+    } else {
+#pragma unroll
+        for (int e = 0; e < kRegKeys; ++e) {
+            const bool in = e < span;
+            key[e] = in ? __float_as_uint(dl[lo + e]) : 0u;
+            mand |= (in && bit_set(s_mand, lo + e)) ? (1u << e) : 0u;
+            live |= in ? (1u << e) : 0u;
+        }
+    }
+    const uint32_t other = live & ~mand;
+    auto for_each = [&](auto body) {
+#pragma unroll
+        for (int e = 0; e < kRegKeys; ++e) body(key[e], ((other >> e) & 1u) != 0);
+    };
+    auto emit = [&](int pos, bool take_all, int nsel, uint32_t thr, int tie_seen, int ties_taken, int32_t* dst) {
+#pragma unroll
+        for (int e = 0; e < kRegKeys; ++e) {
+            bool take = (mand >> e) & 1u;
+            if (!take && ((other >> e) & 1u) && nsel > 0) {
+                if (take_all || key[e] > thr) {
+                    take = true;
+                } else if (key[e] == thr) {
+                    take = tie_seen < ties_taken;
+                    ++tie_seen;
+                }
+            }
+            if (take) dst[pos++] = lo + e;
+        }
+    };
+    budget_select(for_each, emit, __popc(mand), span, L, budget, out, count, sm);
+}
+
+// Positions read from the distances in memory (L2) on every pass.
+__device__ inline void select_from_memory(const float* dl, const uint32_t* s_mand, int lo, int hi, int L,
+                                          int budget, int32_t* out, int32_t* count, SelectSmem* sm) {
+    int n_mand_local = 0;
+    for (int j = lo; j < hi; ++j) n_mand_local += bit_set(s_mand, j) ? 1 : 0;
+    auto for_each = [&](auto body) {
+        for (int j = lo; j < hi; ++j) body(__float_as_uint(dl[j]), !bit_set(s_mand, j));
+    };
+    auto emit = [&](int pos, bool take_all, int nsel, uint32_t thr, int tie_seen, int ties_taken, int32_t* dst) {
+        for (int j = lo; j < hi; ++j) {
+            bool take = bit_set(s_mand, j);
+            if (!take && nsel > 0) {
+                const uint32_t kj = __float_as_uint(dl[j]);
+                if (take_all || kj > thr) {
+                    take = true;
+                } else if (kj == thr) {
+                    take = tie_seen < ties_taken;
+                    ++tie_seen;
+                }
+            }
+            if (take) dst[pos++] = j;
+        }
+    };
+    budget_select(for_each, emit, n_mand_local, hi - lo, L, budget, out, count, sm);
+}
+
 __global__ __launch_bounds__(kSelThreads) void dcu_select_kernel(const float* dist, const double* activity, int NL,
                                                                  int L, const int32_t* keys, int n_keys, int w_m,
                                                                  int total, int32_t* budgets, int32_t* upd_idx,
@@ -220,58 +348,15 @@ __global__ __launch_bounds__(kSelThreads) void dcu_select_kernel(const float* di
     const int budget = s_budget;
 
     // -- the budget over the other tokens: keys are the distances' bits (d >= +0, so the bit
-    //    patterns order like the values)
+    //    patterns order like the values).  Every thread owns the contiguous positions
+    //    [lo, hi); up to kRegKeys of them are held in registers for the whole selection.
     const float* dl = dist + static_cast<int64_t>(bl) * L;
-    auto key_of = [&](int j, uint32_t* key) -> bool {
-        *key = __float_as_uint(dl[j]);
-        return !bit_set(s_mand, j);
-    };
     int lo, hi;
     thread_chunk(L, &lo, &hi);
-    int n_mand_local = 0;
-    for (int j = lo; j < hi; ++j) n_mand_local += bit_set(s_mand, j) ? 1 : 0;
-    int n_mand;
-    block_exclusive_sum(n_mand_local, sm.tmp, &n_mand);
-    const int n_other = L - n_mand;
-    const bool take_all = budget >= n_other;
-    const int nsel = take_all ? n_other : max(budget, 0);
-    uint32_t thr = 0;
-    if (!take_all && nsel > 0) thr = block_kth_largest<uint32_t>(L, nsel, key_of, &sm);
-    int gt = 0, eq = 0;
-    if (nsel > 0 && !take_all) {
-        for_each_key<uint32_t>(lo, hi, key_of, [&](int, uint32_t kj) {
-            gt += kj > thr ? 1 : 0;
-            eq += kj == thr ? 1 : 0;
-        });
-    }
-    int gt_total, eq_total;
-    block_exclusive_sum(gt, sm.tmp, &gt_total);
-    const int eq_before = block_exclusive_sum(eq, sm.tmp, &eq_total);
-    const int ties_taken = nsel - gt_total;   // ties go to the lower positions
-    const int my_ties = take_all || nsel == 0 ? 0 : min(max(ties_taken - eq_before, 0), eq);
-    const int my_other = take_all ? (hi - lo - n_mand_local) : (nsel == 0 ? 0 : gt + my_ties);
-    int n_total;
-    int out = block_exclusive_sum(n_mand_local + my_other, sm.tmp, &n_total);
-    int32_t* ub = upd_idx + static_cast<int64_t>(bl) * L;
-    int tie_seen = eq_before;
-    for (int j = lo; j < hi; ++j) {
-        bool take = bit_set(s_mand, j);
-        if (!take && nsel > 0) {
-            if (take_all) {
-                take = true;
-            } else {
-                const uint32_t kj = __float_as_uint(dl[j]);
-                if (kj > thr) {
-                    take = true;
-                } else if (kj == thr) {
-                    take = tie_seen < ties_taken;
-                    ++tie_seen;
-                }
-            }
-        }
-        if (take) ub[out++] = j;
-    }
-    if (tid == 0) n_upd[bl] = n_total;
+    if ((L + kSelThreads - 1) / kSelThreads <= kRegKeys)
+        select_from_registers(dl, s_mand, lo, hi, L, budget, upd_idx + static_cast<int64_t>(bl) * L, &n_upd[bl], &sm);
+    else
+        select_from_memory(dl, s_mand, lo, hi, L, budget, upd_idx + static_cast<int64_t>(bl) * L, &n_upd[bl], &sm);
 }
 
 }  // namespace
