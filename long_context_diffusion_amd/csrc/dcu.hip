@@ -19,7 +19,8 @@
 //                 the other tokens, and the ascending update list.
 //
 // The distance is computed as d = (|x - y|^2 - (|x| - |y|)^2) / (2 |x| |y|) with
-// |x| - |y| = (x - y).(x + y) / (|x| + |y|): every sum is of exact differences, so d stays
+// |x| - |y| = (x - y).(x + y) / (|x| + |y|): the sums are of the elementwise differences
+// (exact for bf16 inputs, rounded once for fp32 ones) rather than of the inputs, so d stays
 // accurate relative to |x - y|^2 / (2 |x| |y|) when the two inputs are close, where
 // 1 - x.y / (|x| |y|) would lose all its digits to cancellation.
 
