@@ -378,8 +378,19 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                 keys_fetch(t + 3, kr);
                 issue_k(kn, kdma);
                 const bool raw1 = raw_next;   // V(t+1) sits row-major in s_raw
+                // Over I_p the transpose is split around the softmax (the LDS round trip hides
+                // behind it; in key-list mode every tile is staged).  Over a dense range a
+                // tile is staged only when no V^T is given: there the transpose is one block,
+                // so the other tiles carry no registers for it (the compiler set them to zero
+                // on every tile, 8 VALU moves) -- the sparse kernels have no registers to spare
+                // for the block's address arithmetic.
+                constexpr bool kSplitTranspose = MODE != kDense;
                 u32x4 ra, rb;
-                if (raw1) transpose_load(s_raw, ra, rb);
+                if (kSplitTranspose) {
+                    if (raw1) transpose_load(s_raw, ra, rb);
+                } else if (__builtin_expect(raw1, 0)) {
+                    transpose_v(s_raw, tnext);
+                }
                 if (vt2) {
                     issue_vt(k02, tdma);
                 } else {
@@ -424,17 +435,17 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                     m_run = m_new;
                 }
                 const float mneg = -m_run;
-                float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                float ps[4];
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const float pv = fast_exp2(fmaf(st[kc >> 1][8 * (kc & 1) + j], a.sl2, mneg));
-                        ps[kc] += pv;
+                        ps[kc] = j == 0 ? pv : ps[kc] + pv;   // (0 + pv would be one more add)
                         pf[kc][j] = static_cast<__bf16>(pv);
                     }
                 l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                if (raw1) transpose_store(ra, rb, tnext);
+                if (kSplitTranspose && raw1) transpose_store(ra, rb, tnext);
                 if (MODE != kDense) __builtin_amdgcn_s_setprio(0);
                 barrier_keep<4>();   // the loads of tile t+2 may stay in flight
             };
