@@ -9,12 +9,13 @@
 // The n(t) rows of highest confidence whose position is still masked are unmasked.
 //
 // Two kernels, a single read of the logits (the work is bound by HBM bandwidth):
-//   conf_partial  one workgroup per (sequence, row, chunk of kChunk logits): the
-//                 chunk's max, its argmax and sum of exp(z - max), 16 bytes per lane,
-//                 folded across the workgroup.
-//   conf_select   one workgroup per sequence: combines the chunks of every row (in
-//                 chunk order), ranks the still-masked rows by (confidence, position)
-//                 and writes the mask, the tokens, c_t and the unmasked positions.
+//   conf_partial  one workgroup of 1024 threads per (sequence, row): the row's max, its
+//                 argmax and sum of exp(z - max), streamed in rounds of 16-byte loads per
+//                 lane (the next round's loads in flight while one is folded into each
+//                 thread's running state), then folded across the workgroup once.
+//   conf_select   one workgroup per sequence: ranks the still-masked rows by
+//                 (confidence, position) and writes the mask, the tokens, c_t and the
+//                 unmasked positions.
 
 #include "ops.cuh"
 
@@ -22,13 +23,12 @@ namespace fdl {
 
 namespace {
 
-constexpr int kChunk = 8192;          // logits per partial workgroup
-constexpr int kPartThreads = 256;
+constexpr int kRowThreads = 1024;     // threads of a row's workgroup
+constexpr int kRowLoads = 2;          // 16-byte loads per thread and round
 constexpr int kSelThreadsU = 1024;
-constexpr int kFoldBatch = 8;         // chunk parts loaded together per row
 constexpr float kLog2eU = 1.44269504088896340736f;
 
-struct Part {   // one chunk of one row
+struct Part {   // one row: max, sum of exp(z - max), argmax
     float m, s;
     int arg, pad;
 };
@@ -46,63 +46,89 @@ __device__ __forceinline__ void fold(float& m, float& s, int& arg, float m2, flo
     }
 }
 
+// Folds the N values x (x[i] at index idx(i), increasing) into one thread's running
+// (max m, sum s of exp(z - m), argmax).  The values' max is a max tree; only when it
+// exceeds the running max (rare once a row's first values are in) are its first position
+// found and s brought to the new max; then every value adds exp(z - m).
+template <int N, typename Idx>
+__device__ __forceinline__ void fold_values(const float (&x)[N], Idx idx, float& m, float& s, int& arg) {
+    float rm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) rm = fmaxf(rm, x[i]);
+    if (rm > m) {
+        int ra = idx(N - 1);
+#pragma unroll
+        for (int i = N - 2; i >= 0; --i) ra = x[i] == rm ? idx(i) : ra;   // the first one equal to rm
+        s = m == -INFINITY ? 0.0f : s * fast_exp2((m - rm) * kLog2eU);
+        m = rm;
+        arg = ra;
+    }
+    if (m == -INFINITY) return;   // nothing but -inf so far
+    const float mb = m * kLog2eU;
+#pragma unroll
+    for (int i = 0; i < N; ++i) s += fast_exp2(fmaf(x[i], kLog2eU, -mb));
+}
+
 template <typename T>
-__global__ __launch_bounds__(kPartThreads) void conf_partial_kernel(const T* logits, int64_t lsb, int64_t lsr,
-                                                                    const int32_t* n_rows, int m_max, int V,
-                                                                    int n_chunks, Part* parts) {
-    constexpr int EPV = 16 / sizeof(T);                 // elements per 16-byte load
-    constexpr int VPT = kChunk / EPV / kPartThreads;    // loads per thread
-    __shared__ float s_m[kPartThreads / kWave], s_s[kPartThreads / kWave];
-    __shared__ int s_a[kPartThreads / kWave];
-    const int ch = blockIdx.x % n_chunks;
-    const int row = (blockIdx.x / n_chunks) % m_max;
-    const int b = blockIdx.x / (n_chunks * m_max);
+__global__ __launch_bounds__(kRowThreads) void conf_partial_kernel(const T* logits, int64_t lsb, int64_t lsr,
+                                                                  const int32_t* n_rows, int m_max, int V,
+                                                                  Part* parts) {
+    constexpr int EPV = 16 / sizeof(T);                  // elements per 16-byte load
+    constexpr int kRound = kRowThreads * kRowLoads * EPV;   // logits per round
+    __shared__ float s_m[kRowThreads / kWave], s_s[kRowThreads / kWave];
+    __shared__ int s_a[kRowThreads / kWave];
+    const int row = blockIdx.x % m_max;
+    const int b = blockIdx.x / m_max;
     const int nr = n_rows ? n_rows[b] : m_max;
     if (row >= nr) return;
     const T* z = logits + b * lsb + static_cast<int64_t>(row) * lsr;
-    const int lo = ch * kChunk, hi = min(V, lo + kChunk);
     const int tid = threadIdx.x;
-    // element e = lo + EPV (tid + kPartThreads u) + j: all loads first, then the folds
-    float x[VPT][EPV];
+    const int n_rounds = (V + kRound - 1) / kRound;
+    // round r, load u of this thread: elements r kRound + EPV (tid + kRowThreads u) + 0 .. EPV-1,
+    // read as one 16-byte load when all of them exist; the loads of round r + 1 go out
+    // before round r is folded
+    auto load_round = [&](int r, u32x4 (&w)[kRowLoads]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int e0 = lo + EPV * (tid + kPartThreads * u);
-        if (e0 + EPV <= hi) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(z + e0);
-            if (sizeof(T) == 2) {
+        for (int u = 0; u < kRowLoads; ++u) {
+            const int e0 = r * kRound + EPV * (tid + kRowThreads * u);
+            w[u] = e0 + EPV <= V ? *reinterpret_cast<const u32x4*>(z + e0) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    float m = -INFINITY, s = 0.0f;
+    int arg = 0x7fffffff;
+    u32x4 cur[kRowLoads], nxt[kRowLoads];
+    load_round(0, cur);
+    for (int r = 0; r < n_rounds; ++r) {
+        if (r + 1 < n_rounds) load_round(r + 1, nxt);
+        float x[kRowLoads * EPV];
+        const int base = r * kRound + EPV * tid;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[u][2 * i] = bf16lo(w[i]);
-                    x[u][2 * i + 1] = bf16hi(w[i]);
+        for (int u = 0; u < kRowLoads; ++u) {
+            const int e0 = base + kRowThreads * EPV * u;
+            if (e0 + EPV <= V) {
+                if (sizeof(T) == 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[EPV * u + 2 * i] = bf16lo(cur[u][i]);
+                        x[EPV * u + 2 * i + 1] = bf16hi(cur[u][i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[EPV * u + i] = __uint_as_float(cur[u][i]);
                 }
             } else {
+                // the row's last, partial vector (or past the row): element by element
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[u][i] = __uint_as_float(w[i]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) x[u][j] = e0 + j < hi ? Elem<T>::load(z + e0 + j) : -INFINITY;
-        }
-    }
-    float m = -INFINITY;
-    int arg = 0x7fffffff;
-#pragma unroll
-    for (int u = 0; u < VPT; ++u)
-#pragma unroll
-        for (int j = 0; j < EPV; ++j) {
-            const int e = lo + EPV * (tid + kPartThreads * u) + j;
-            if (x[u][j] > m) {   // elements visit in increasing index: the first max is kept
-                m = x[u][j];
-                arg = e;
+                for (int j = 0; j < EPV; ++j) x[EPV * u + j] = e0 + j < V ? Elem<T>::load(z + e0 + j) : -INFINITY;
             }
         }
-    float s = 0.0f;
-    if (m > -INFINITY) {
-        const float mb = m * kLog2eU;
+        // the thread's values of this round in increasing index: value EPV u + j is element
+        // base + kRowThreads EPV u + j
+        fold_values(x, [&](int i) { return base + kRowThreads * EPV * (i / EPV) + i % EPV; }, m, s, arg);
+        if (r + 1 < n_rounds) {
 #pragma unroll
-        for (int u = 0; u < VPT; ++u)
-#pragma unroll
-            for (int j = 0; j < EPV; ++j) s += fast_exp2(fmaf(x[u][j], kLog2eU, -mb));
+            for (int u = 0; u < kRowLoads; ++u) cur[u] = nxt[u];
+        }
     }
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -128,7 +154,7 @@ __global__ __launch_bounds__(kPartThreads) void conf_partial_kernel(const T* log
     if (tid == 0) {
         float M = s_m[0], S = s_s[0];
         int A = s_a[0];
-        for (int w = 1; w < kPartThreads / kWave; ++w) {
+        for (int w = 1; w < kRowThreads / kWave; ++w) {
             if (s_m[w] == -INFINITY) continue;
             if (M == -INFINITY) {
                 M = s_m[w];
@@ -138,11 +164,11 @@ __global__ __launch_bounds__(kPartThreads) void conf_partial_kernel(const T* log
                 fold(M, S, A, s_m[w], s_s[w], s_a[w]);
             }
         }
-        parts[(static_cast<int64_t>(b) * m_max + row) * n_chunks + ch] = Part{M, S, A, 0};
+        parts[static_cast<int64_t>(b) * m_max + row] = Part{M, S, A, 0};
     }
 }
 
-__global__ __launch_bounds__(kSelThreadsU) void conf_select_kernel(const Part* parts, int n_chunks, const int32_t* pos,
+__global__ __launch_bounds__(kSelThreadsU) void conf_select_kernel(const Part* parts, const int32_t* pos,
                                                                    const int32_t* n_rows, int m_max, int L, int n_t,
                                                                    uint8_t* mask, float* conf, int32_t* tokens,
                                                                    int32_t* unmasked) {
@@ -156,30 +182,13 @@ __global__ __launch_bounds__(kSelThreadsU) void conf_select_kernel(const Part* p
     const int n = min(n_rows ? n_rows[b] : m_max, m_max);
     const int32_t* pb = pos + static_cast<int64_t>(b) * m_max;
     uint8_t* mb = mask + static_cast<int64_t>(b) * L;
-    // combine the chunks of each row in chunk order; s_pos = -1 marks rows that are not
-    // candidates (position outside [0, L) or no longer masked)
+    // each row's (max, sum, argmax); s_pos = -1 marks rows that are not candidates
+    // (position outside [0, L) or no longer masked)
     int n_cand_local = 0;
     for (int r = tid; r < n; r += kSelThreadsU) {
-        const Part* pr = parts + (static_cast<int64_t>(b) * m_max + r) * n_chunks;
-        float M = -INFINITY, S = 0.0f;
-        int A = 0x7fffffff;
-        // the chunks' parts in batches of independent loads, folded in chunk order
-        for (int c0 = 0; c0 < n_chunks; c0 += kFoldBatch) {
-            Part q[kFoldBatch];
-#pragma unroll
-            for (int u = 0; u < kFoldBatch; ++u) q[u] = pr[min(c0 + u, n_chunks - 1)];
-#pragma unroll
-            for (int u = 0; u < kFoldBatch; ++u) {
-                if (c0 + u >= n_chunks) break;
-                if (c0 + u == 0) {
-                    M = q[u].m;
-                    S = q[u].s;
-                    A = q[u].arg;
-                } else {
-                    fold(M, S, A, q[u].m, q[u].s, q[u].arg);
-                }
-            }
-        }
+        const Part q = parts[static_cast<int64_t>(b) * m_max + r];
+        const float S = q.s;
+        const int A = q.arg;
         const int p = pb[r];
         const bool cand = p >= 0 && p < L && mb[p] != 0;
         s_c[r] = 1.0f / S;
@@ -230,28 +239,26 @@ __global__ __launch_bounds__(kSelThreadsU) void conf_select_kernel(const Part* p
 
 }  // namespace
 
-int conf_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
 size_t confidence_workspace_bytes(int B, int V, int m_max) {
-    return static_cast<size_t>(B) * m_max * conf_chunks(V) * sizeof(Part);
+    return V > 0 ? static_cast<size_t>(B) * m_max * sizeof(Part) : 0;   // one part per row
 }
 
 hipError_t launch_confidence_unmask(fdl_dtype dtype, int B, int L, int V, const void* logits, int64_t lsb,
                                     int64_t lsr, const int32_t* pos, const int32_t* n_rows, int m_max, int n_t,
                                     uint8_t* mask, float* conf, int32_t* tokens, int32_t* unmasked, void* ws,
                                     hipStream_t stream) {
-    const int nc = conf_chunks(V);
     Part* parts = static_cast<Part*>(ws);
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * m_max * nc));
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * m_max));
     if (dtype == FDL_BF16)
-        hipLaunchKernelGGL(conf_partial_kernel<uint16_t>, grid, dim3(kPartThreads), 0, stream,
-                           static_cast<const uint16_t*>(logits), lsb, lsr, n_rows, m_max, V, nc, parts);
+        hipLaunchKernelGGL(conf_partial_kernel<uint16_t>, grid, dim3(kRowThreads), 0, stream,
+                           static_cast<const uint16_t*>(logits), lsb, lsr, n_rows, m_max, V, parts);
     else
-        hipLaunchKernelGGL(conf_partial_kernel<float>, grid, dim3(kPartThreads), 0, stream,
-                           static_cast<const float*>(logits), lsb, lsr, n_rows, m_max, V, nc, parts);
+        hipLaunchKernelGGL(conf_partial_kernel<float>, grid, dim3(kRowThreads), 0, stream,
+                           static_cast<const float*>(logits), lsb, lsr, n_rows, m_max, V, parts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(conf_select_kernel, dim3(B), dim3(kSelThreadsU), 0, stream, parts, nc, pos, n_rows, m_max, L,
+    hipLaunchKernelGGL(conf_select_kernel, dim3(B), dim3(kSelThreadsU), 0, stream, parts, pos, n_rows, m_max, L,
                        n_t, mask, conf, tokens, unmasked);
     return hipGetLastError();
 }

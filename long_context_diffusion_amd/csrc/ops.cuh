@@ -98,7 +98,6 @@ hipError_t launch_dcu_select(fdl_dtype dtype, const DcuArgs& a, hipStream_t stre
 
 // token confidence and unmasking (confidence.hip)
 constexpr int kMaxConfRows = 4096;   // listed rows per sequence
-int conf_chunks(int V);
 size_t confidence_workspace_bytes(int B, int V, int m_max);
 hipError_t launch_confidence_unmask(fdl_dtype dtype, int B, int L, int V, const void* logits, int64_t lsb,
                                     int64_t lsr, const int32_t* pos, const int32_t* n_rows, int m_max, int n_t,
