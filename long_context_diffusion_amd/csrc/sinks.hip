@@ -14,7 +14,8 @@
 //                 probabilities of all query rows (of every query head sharing
 //                 the KV head) in a fixed order.  Q rows stream through LDS in
 //                 blocks of 32.
-//   sink_reduce   adds the per-KV-head partials in head order (deterministic).
+//   sink_reduce   adds the per-KV-head partials in a fixed order (deterministic):
+//                 four runs of consecutive heads, then the four run sums.
 //   sink_select   top-n over the L scores of each sequence, ascending output: a
 //                 threshold from the per-thread maxima, then an exact rank of the
 //                 few scores above it (a radix select when there are many).
@@ -178,24 +179,41 @@ __global__ __launch_bounds__(256) void sink_colsum_f32_kernel(const SinkArgs a) 
     if (key < a.L) a.part[(static_cast<int64_t>(b) * a.Hkv + g) * a.L + key] = acc;
 }
 
-// scores[b][j] = sum over KV heads of the partial column sums, in head order.
-__global__ __launch_bounds__(256) void sink_reduce_kernel(const SinkArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= static_cast<int64_t>(a.B) * a.L) return;
-    const int b = static_cast<int>(i / a.L);
-    const int j = static_cast<int>(i % a.L);
+// score[b][j] = sum over KV heads of part[b][g][j]: a workgroup takes kRedKeys keys, its
+// kRedGroups thread groups each add a contiguous run of heads for every key, and the
+// group sums are added in group order (a fixed order: repeated runs are bit-identical).
+constexpr int kRedKeys = 64;
+constexpr int kRedGroups = 4;
+__global__ __launch_bounds__(kRedKeys * kRedGroups) void sink_reduce_kernel(const SinkArgs a) {
+    __shared__ float s_g[kRedGroups][kRedKeys];
+    const int kt = threadIdx.x % kRedKeys, grp = threadIdx.x / kRedKeys;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kRedKeys + kt;   // b * L + j
+    const bool ok = i < static_cast<int64_t>(a.B) * a.L;
+    const int b = ok ? static_cast<int>(i / a.L) : 0;
+    const int j = ok ? static_cast<int>(i % a.L) : 0;
+    const int per = (a.Hkv + kRedGroups - 1) / kRedGroups;
+    const int g0 = grp * per, g1 = min(a.Hkv, g0 + per);
     const float* p = a.part + static_cast<int64_t>(b) * a.Hkv * a.L + j;
     float s = 0.0f;
-    int g = 0;
-    for (; g + 8 <= a.Hkv; g += 8) {
-        float x[8];
+    if (ok) {
+        int g = g0;
+        for (; g + 8 <= g1; g += 8) {
+            float x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = p[static_cast<int64_t>(g + u) * a.L];
+            for (int u = 0; u < 8; ++u) x[u] = p[static_cast<int64_t>(g + u) * a.L];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += x[u];
+            for (int u = 0; u < 8; ++u) s += x[u];
+        }
+        for (; g < g1; ++g) s += p[static_cast<int64_t>(g) * a.L];
     }
-    for (; g < a.Hkv; ++g) s += p[static_cast<int64_t>(g) * a.L];
-    a.scores[i] = s;
+    s_g[grp][kt] = s;
+    __syncthreads();
+    if (grp == 0 && ok) {
+        float t = s_g[0][kt];
+#pragma unroll
+        for (int q = 1; q < kRedGroups; ++q) t += s_g[q][kt];
+        a.scores[i] = t;
+    }
 }
 
 constexpr int kSelThreads = 1024;
@@ -353,7 +371,8 @@ hipError_t launch_sink_identify(fdl_dtype dtype, int d, SinkArgs a, int n_sinks,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t n = static_cast<int64_t>(a.B) * a.L;
-    hipLaunchKernelGGL(sink_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sink_reduce_kernel, dim3(static_cast<unsigned>((n + kRedKeys - 1) / kRedKeys)),
+                       dim3(kRedKeys * kRedGroups), 0, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(sink_select_kernel, dim3(a.B), dim3(kSelThreads), 0, stream, a.scores, a.L, n_sinks, sink_idx);
