@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int j = min(lo[c] + j0 + u * RG, max(hi[c] - 1, lo[c]));
-                x[c][u] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * a.ksr);
+                x[c][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * a.ksr));
             }
 #pragma unroll
         for (int c = 0; c < kMeansBlocks; ++c)

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kRowThreads) void conf_partial_kernel(const T* logi
 #pragma unroll
         for (int u = 0; u < kRowLoads; ++u) {
             const int e0 = r * kRound + EPV * (tid + kRowThreads * u);
-            w[u] = e0 + EPV <= V ? *reinterpret_cast<const u32x4*>(z + e0) : u32x4{0u, 0u, 0u, 0u};
+            w[u] = e0 + EPV <= V ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(z + e0))
+                                  : u32x4{0u, 0u, 0u, 0u};
         }
     };
     float m = -INFINITY, s = 0.0f;

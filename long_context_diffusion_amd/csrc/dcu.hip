@@ -77,8 +77,8 @@ __device__ __forceinline__ float token_distance(const T* x, const T* y, int H, i
         for (int u = 0; u < kLoadsPerLane; ++u) {
             const int v = v0 + lane + kWave * u;
             if (v < nvec) {
-                a[u] = xv[v];
-                c[u] = yv[v];
+                a[u] = __builtin_nontemporal_load(xv + v);
+                c[u] = __builtin_nontemporal_load(yv + v);
             } else {
                 a[u] = u32x4{0u, 0u, 0u, 0u};
                 c[u] = u32x4{0u, 0u, 0u, 0u};
