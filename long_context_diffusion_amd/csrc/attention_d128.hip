@@ -195,7 +195,9 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                     const int kb = min(max(kr[3 * i] * a.bs + kr[3 * i + 2], 0), a.L - 1);
                     k = q < n_blk ? kb : (q < sink0 ? a.P + (q - n_blk) : kr[3 * i + 1]);
                 }
-                key[i] = ok ? k : 0;
+                // over a dense range a position past the keys (or a tile past the split) reads
+                // the last key's row: its scores are masked, and a clamp is cheaper than a select
+                key[i] = MODE == kDense ? min(q, n_keys - 1) : (ok ? k : 0);
             }
         };
         // Tiles of 64 consecutive keys (every tile of a dense range; in I_p the tiles
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
         // d = 16wv + 8i .. +7, lane l chunk l % 8 of row d, i.e. keys
         // k0 + 8 ((l % 8) ^ vt_swz(d)) .. +7 (16 contiguous bytes).  Chunks at or past
         // n_keys (only in the last tile of a dense key range; n_keys is a multiple of 8)
-        // read chunk 0 of the row instead, whose probabilities are zero.
+        // read the row's last chunk instead: their probabilities are zero.
         const uint16_t* vtbase = static_cast<const uint16_t*>(a.vt) + b * a.vtsb + g * a.vtsh;
         const int vtsd = a.vtsd;
         auto issue_vt = [&](int k0, uint8_t* dst) __attribute__((always_inline)) {
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
             for (int i = 0; i < 2; ++i) {
                 const int d = 16 * wv + 8 * i + (lane >> 3);
                 int kk = k0 + 8 * ((lane & 7) ^ vt_swz(d));
-                if (MODE == kDense) kk = kk < n_keys ? kk : 0;
+                if (MODE == kDense) kk = min(kk, n_keys - 8);
                 const uint16_t* src = vtbase + d * vtsd + kk;
                 __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + 1024 * (2 * wv + i)), 16, 0, 0);
             }
