@@ -480,6 +480,17 @@ __global__ __launch_bounds__(512) void attn_d128_kernel(const AttnArgs a) {
                         st[c >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[c & 7], st[c >> 3], 0, 0, 0);
                     }
                 }
+                if (MODE != kDense) {
+                    // over I_p the scheduler otherwise places each fragment read right before
+                    // its MFMA, which then waits for the LDS round trip: keep 4 reads ahead
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 4 LDS reads
+#pragma unroll
+                    for (int j = 0; j < 28; ++j) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // the last 4 MFMAs
+                }
                 barrier_keep<0>();   // this wave's loads of the next tile have landed
             };
             // tile t0 + j: K in s_k[j % 4], V^T in s_t[j % 4]
