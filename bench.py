@@ -64,6 +64,8 @@ def parse():
                     help="only the dynamic cache update scoring measurement (the run profiled for it)")
     ap.add_argument("--serial-means", action="store_true",
                     help="block means right before each layer's scoring instead of on a second stream")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only the achievable read / MFMA rates of the library's measurement kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--kernel-reps", type=int, default=3,
@@ -282,6 +284,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.peaks_only:
+        print(json.dumps({"peaks_measured": achievable_peaks("cuda")}), flush=True)
+        return
     if args.calibrate_copy:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -754,37 +759,54 @@ def other_configs(F, dev, args):
 
 
 def achievable_peaks(dev):
-    """Rates that library kernels reach on this GPU: a streaming read (torch's sum of 4 GiB of
-    bf16) and a bf16 GEMM (torch.mm, 8192^3, hipBLASLt)."""
+    """What plain kernels sustain on this GPU, beside the published peaks: the library's own
+    streaming read (fdl_calibrate_read: 4 GiB once with non-temporal 16-byte loads, best of
+    three grid sizes) and MFMA loop (fdl_calibrate_mfma: one wave per SIMD issuing
+    v_mfma_f32_32x32x16_bf16 back to back for about 20 ms); then library rates for context
+    (torch's sum over the same 4 GiB, torch.mm bf16 8192^3 through hipBLASLt)."""
     import torch
-    x = torch.empty(1 << 31, dtype=torch.bfloat16, device=dev).normal_()
-    x.sum()
-    torch.cuda.synchronize()
+    import long_context_diffusion_amd as F
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
-    e0.record()
-    for _ in range(reps):
-        x.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    read_gbs = x.numel() * 2 / (e0.elapsed_time(e1) / reps / 1000) / 1e9
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1000
+
+    x = torch.empty(1 << 31, dtype=torch.bfloat16, device=dev).normal_()
+    nbytes = x.numel() * 2
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    read = {}
+    for per_cu in (4, 8, 16):
+        sink = torch.empty((cus * per_cu,), dtype=torch.int32, device=dev)
+        read[per_cu] = nbytes / timed(lambda: F.calibrate_read(x, cus * per_cu, sink=sink)) / 1e9
+    best_wg = max(read, key=read.get)
+    torch_read = nbytes / timed(lambda: x.sum()) / 1e9
     del x
+    iters = 200000
+    sink = torch.empty((cus * 4, 2), dtype=torch.float32, device=dev)
+    t = timed(lambda: F.calibrate_mfma(cus, iters, 1.0, 0.5, sink=sink))
+    ok = bool((sink[:, 0] == 16.0 * 0.5 * iters).all() and (sink[:, 1] == 0).all())
+    mfma_tf = cus * 4 * iters * F.fdl.CALIBRATE_MFMA_FLOPS_PER_WAVE_ROUND / t / 1e12
     n = 8192
     a = torch.randn((n, n), device=dev).to(torch.bfloat16)
     b = torch.randn((n, n), device=dev).to(torch.bfloat16)
-    torch.mm(a, b)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        torch.mm(a, b)
-    e1.record()
-    torch.cuda.synchronize()
-    tf = 2.0 * n ** 3 / (e0.elapsed_time(e1) / reps / 1000) / 1e12
+    tf = 2.0 * n ** 3 / timed(lambda: torch.mm(a, b)) / 1e12
     del a, b
     torch.cuda.empty_cache()
-    return {"stream_read_GBps": round(read_gbs, 1), "stream_read_frac_of_8000": round(read_gbs / HBM_PEAK_GBS, 4),
-            "bf16_gemm_TFLOPps": round(tf, 1), "bf16_gemm_frac_of_2500": round(tf / BF16_PEAK_TFLOPS, 4),
-            "kernels": "torch.sum over 4 GiB bf16; torch.mm bf16 8192 x 8192 x 8192"}
+    return {"read_GBps": round(read[best_wg], 1), "read_frac_of_8000": round(read[best_wg] / HBM_PEAK_GBS, 4),
+            "read_GBps_by_workgroups_per_cu": {k: round(v, 1) for k, v in read.items()},
+            "mfma_bf16_TFLOPps": round(mfma_tf, 1), "mfma_frac_of_2500": round(mfma_tf / BF16_PEAK_TFLOPS, 4),
+            "mfma_ms": round(t * 1e3, 3), "mfma_result_exact": ok,
+            "kernels": "fdl_calibrate_read over 4 GiB; fdl_calibrate_mfma, one wave per SIMD, 8 chains",
+            "library": {"torch_sum_read_GBps": round(torch_read, 1), "torch_mm_bf16_TFLOPps": round(tf, 1),
+                        "kernels": "torch.sum over 4 GiB bf16; torch.mm bf16 8192 x 8192 x 8192"}}
 
 
 def confidence_measurement(F, dev, args):

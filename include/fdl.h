@@ -18,6 +18,7 @@
  *   fdl_block_means_refresh  (4) the means of the blocks a refresh touched
  *   fdl_confidence_unmask    confidence of the masked positions, unmasking of n(t) of them
  *   fdl_dcu_select           per-layer cache update sets of the dynamic cache update (DCU)
+ *   fdl_calibrate_read, fdl_calibrate_mfma   achievable read and MFMA rates (measurement)
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
@@ -402,6 +403,26 @@ fdl_status fdl_dcu_select(fdl_dtype dtype, int B, int NL, int L, int H, const vo
                           const void* x_prev, fdl_strides xps, const int32_t* key_tokens, int n_keys, int w_m,
                           int total, float* dist, double* activity, int32_t* budgets, int32_t* upd_idx,
                           int32_t* n_upd, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Measurement helpers (not steps of the method): what plain kernels reach on this GPU,
+ * so that a kernel's share of the published peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16
+ * MFMA on MI355X) can be read beside its share of what the part sustains.
+ *
+ * fdl_calibrate_read streams `bytes` (a positive multiple of 16) from the device buffer
+ *   `src` once with non-temporal 16-byte loads, `workgroups` (>= 1) workgroups of 256
+ *   threads each taking 64 KB a round.  sink [workgroups] uint32 receives the XOR of the
+ *   32-bit words each workgroup read; the XOR of all entries is the XOR of the buffer.
+ *   src must be 16-byte aligned (FDL_ERR_ALIGN).
+ * fdl_calibrate_mfma runs `workgroups` (>= 1) workgroups of 4 waves; every wave issues
+ *   iters (>= 1) rounds of 8 independent v_mfma_f32_32x32x16_bf16 on operands held in
+ *   registers (every element a_val resp. b_val, rounded to bf16): 262144 flop per wave
+ *   and round.  sink [workgroups * 4 * 2] fp32: per wave an accumulator element, which is
+ *   16 * a * b * iters (a, b the bf16 operands; exact while that stays below 2^24), and the
+ *   largest deviation of any of its elements from it.
+ */
+fdl_status fdl_calibrate_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+fdl_status fdl_calibrate_mfma(int workgroups, int iters, float a_val, float b_val, float* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -437,4 +437,17 @@ fdl_status fdl_dcu_select(fdl_dtype dt, int B, int NL, int L, int H, const void*
     return hip_status(launch_dcu_select(dt, a, stream));
 }
 
+fdl_status fdl_calibrate_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream) {
+    if (bytes == 0 || bytes % 16 || workgroups < 1) return FDL_ERR_SHAPE;
+    if (!src || !sink) return FDL_ERR_NULL;
+    if (!aligned16(src)) return FDL_ERR_ALIGN;
+    return hip_status(launch_calib_read(src, bytes, sink, workgroups, stream));
+}
+
+fdl_status fdl_calibrate_mfma(int workgroups, int iters, float a_val, float b_val, float* sink, hipStream_t stream) {
+    if (workgroups < 1 || iters < 1) return FDL_ERR_SHAPE;
+    if (!sink) return FDL_ERR_NULL;
+    return hip_status(launch_calib_mfma(workgroups, iters, a_val, b_val, sink, stream));
+}
+
 }  // extern "C"

@@ -104,4 +104,8 @@ hipError_t launch_confidence_unmask(fdl_dtype dtype, int B, int L, int V, const 
                                     uint8_t* mask, float* conf, int32_t* tokens, int32_t* unmasked, void* ws,
                                     hipStream_t stream);
 
+// calibrate.hip
+hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+hipError_t launch_calib_mfma(int workgroups, int iters, float a_val, float b_val, float* sink, hipStream_t stream);
+
 }  // namespace fdl

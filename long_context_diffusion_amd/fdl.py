@@ -35,6 +35,7 @@ EXPORTS = (
     "fdl_confidence_unmask_workspace_bytes", "fdl_confidence_unmask",
     "fdl_dcu_select_workspace_bytes", "fdl_dcu_select",
     "fdl_block_score_topc_ex", "fdl_sparse_attention_ex_workspace_bytes", "fdl_sparse_attention_ex",
+    "fdl_calibrate_read", "fdl_calibrate_mfma",
 )
 FDL_SCORE_PER_HEAD, FDL_SCORE_MAX = 1, 2
 
@@ -85,6 +86,8 @@ _SIGS = {
                                      _P]),
     "fdl_dcu_select": (_I, [_I, _I, _I, _I, _I, _P, Strides, _P, Strides, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
+    "fdl_calibrate_read": (_I, [_P, _SZ, _P, _I, _P]),
+    "fdl_calibrate_mfma": (_I, [_I, _I, _F, _F, _P, _P]),
     "fdl_block_score_topc_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
                                           _I, _I, _P, _P, _P, _P]),
     "fdl_sparse_attention": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _P,
@@ -469,3 +472,31 @@ def dcu_select(x_now, x_prev, key_tokens, w_m: int, total: int, *, out=None, wor
                               _ptr(budgets), _ptr(upd_idx), _ptr(n_upd), ws, ws_n, _stream(stream))
     _check(st, "fdl_dcu_select")
     return dist, activity, budgets, upd_idx, n_upd
+
+
+def calibrate_read(x: torch.Tensor, workgroups: int, *, sink=None, stream=None):
+    """Streams the bytes of the contiguous device tensor x once (fdl_calibrate_read) and
+    returns the [workgroups] int32 tensor of per-workgroup XORs of its 32-bit words."""
+    if not x.is_contiguous() or (x.numel() * x.element_size()) % 16:
+        raise FdlError(2, "x must be contiguous with a size that is a multiple of 16 bytes")
+    if sink is None:
+        sink = torch.empty((workgroups,), dtype=torch.int32, device=x.device)
+    st = lib().fdl_calibrate_read(_ptr(x), x.numel() * x.element_size(), _ptr(sink), int(workgroups),
+                                  _stream(stream))
+    _check(st, "fdl_calibrate_read")
+    return sink
+
+
+def calibrate_mfma(workgroups: int, iters: int, a_val: float, b_val: float, *, device="cuda", sink=None,
+                   stream=None):
+    """Back-to-back bf16 MFMAs on register operands (fdl_calibrate_mfma); returns the
+    [workgroups * 4, 2] fp32 tensor of per-wave (accumulator element, largest deviation)."""
+    if sink is None:
+        sink = torch.empty((workgroups * 4, 2), dtype=torch.float32, device=device)
+    st = lib().fdl_calibrate_mfma(int(workgroups), int(iters), float(a_val), float(b_val), _ptr(sink),
+                                  _stream(stream))
+    _check(st, "fdl_calibrate_mfma")
+    return sink
+
+
+CALIBRATE_MFMA_FLOPS_PER_WAVE_ROUND = 8 * 2 * 32 * 32 * 16

@@ -318,3 +318,17 @@ def test_block_means_alignment():
     assert lib.fdl_block_means(F.FDL_BF16, 1, 32, 32768, 32256, 128, FAKE, st, 128, MISALIGNED, None) == 4
     assert lib.fdl_block_means_refresh(F.FDL_BF16, 1, 32, 32768, 32256, 128, FAKE, st, 128, FAKE, NULL, 8,
                                        MISALIGNED, None) == 4
+
+
+def test_calibrate_validation():
+    lib = F.lib()
+    out = ctypes.c_void_p(0x20000)
+    assert lib.fdl_calibrate_read(FAKE, 0, out, 8, NULL) == 2
+    assert lib.fdl_calibrate_read(FAKE, 24, out, 8, NULL) == 2
+    assert lib.fdl_calibrate_read(FAKE, 4096, out, 0, NULL) == 2
+    assert lib.fdl_calibrate_read(NULL, 4096, out, 8, NULL) == 1
+    assert lib.fdl_calibrate_read(FAKE, 4096, NULL, 8, NULL) == 1
+    assert lib.fdl_calibrate_read(MISALIGNED, 4096, out, 8, NULL) == 4
+    assert lib.fdl_calibrate_mfma(0, 10, 1.0, 1.0, out, NULL) == 2
+    assert lib.fdl_calibrate_mfma(4, 0, 1.0, 1.0, out, NULL) == 2
+    assert lib.fdl_calibrate_mfma(4, 10, 1.0, 1.0, NULL, NULL) == 1
