@@ -67,7 +67,7 @@ __device__ __forceinline__ void unpack16<float>(const u32x4& x, float* out) {
 // A workgroup takes kMeansBlocks consecutive blocks and keeps the loads of all of them
 // in flight together.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a) {
+__global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a, int wg0) {
     constexpr int EPP = 16 / sizeof(T);     // elements per 16-byte piece
     constexpr int NP = D / EPP;             // pieces per key row
     constexpr int RG = kThreads / NP;       // rows read together by the workgroup
@@ -77,8 +77,9 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const BlockArgs a
     __shared__ double s_sum[kMeansBlocks][kWaves][EPP][NP];
     const int tid = threadIdx.x;
     const int chunks = (a.nb + kMeansBlocks - 1) / kMeansBlocks;
-    const int chunk = blockIdx.x % chunks;
-    const int bg = blockIdx.x / chunks;
+    const int wg = wg0 + static_cast<int>(blockIdx.x);   // launches of one wave each: see launch_block_means
+    const int chunk = wg % chunks;
+    const int bg = wg / chunks;
     const int g = bg % a.Hkv, b = bg / a.Hkv;
     const int piece = tid % NP, rg = tid / NP;
     const T* kbase = static_cast<const T*>(a.k) + b * a.ksb + g * a.ksh + piece * EPP;
@@ -437,13 +438,53 @@ size_t block_workspace_bytes(int B, int Hq, int Hkv, int P, int d, int bs, int n
            static_cast<size_t>(B) * Hkv * nb * d * sizeof(float);                       // block means
 }
 
+// Workgroups of block_means_kernel<T, D> the whole device holds at once (CUs x resident
+// workgroups per CU), queried once per device; 0 when the query fails.
+template <typename T, int D>
+int64_t means_wave() {
+    static int64_t cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, block_means_kernel<T, D>, kThreads, 0) != hipSuccess ||
+            per_cu <= 0)
+            cached[dev] = -1;
+        else
+            cached[dev] = static_cast<int64_t>(cus) * per_cu;
+    }
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+// The grid goes out as launches of at most one wave of resident workgroups each.  The means
+// usually run on a second stream beside the layers' own kernels; between two launches the
+// other stream's kernels are dispatched, instead of waiting behind the tail of a grid of
+// several waves.  On the 32K step (4032 workgroups a layer, 1024 resident) one-wave launches
+// took the replayed step from 5.15-5.17 to 4.94-5.01 ms (alternating runs on one box);
+// splitting each layer's grid in two launches changed nothing and in eight (half a wave
+// each) made the step slower.
+template <typename T, int D>
+void launch_means_waves(const BlockArgs& a, int64_t total, hipStream_t stream) {
+    const int64_t wave = means_wave<T, D>();
+    const int64_t step = wave > 0 ? wave : total;
+    for (int64_t w0 = 0; w0 < total; w0 += step) {
+        const int64_t n = total - w0 < step ? total - w0 : step;
+        hipLaunchKernelGGL((block_means_kernel<T, D>), dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, stream, a,
+                           static_cast<int>(w0));
+    }
+}
+
 hipError_t launch_block_means(fdl_dtype dtype, int d, const BlockArgs& a, hipStream_t stream) {
     const int chunks = (a.nb + kMeansBlocks - 1) / kMeansBlocks;
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * chunks));
-#define FDL_MEANS(T, DD) hipLaunchKernelGGL((block_means_kernel<T, DD>), grid, dim3(kThreads), 0, stream, a)
-    if (dtype == FDL_BF16) { if (d == 128) FDL_MEANS(uint16_t, 128); else FDL_MEANS(uint16_t, 64); }
-    else { if (d == 128) FDL_MEANS(float, 128); else FDL_MEANS(float, 64); }
-#undef FDL_MEANS
+    const int64_t total = static_cast<int64_t>(a.B) * a.Hkv * chunks;
+    if (dtype == FDL_BF16) {
+        if (d == 128) launch_means_waves<uint16_t, 128>(a, total, stream);
+        else launch_means_waves<uint16_t, 64>(a, total, stream);
+    } else {
+        if (d == 128) launch_means_waves<float, 128>(a, total, stream);
+        else launch_means_waves<float, 64>(a, total, stream);
+    }
     return hipGetLastError();
 }
 
