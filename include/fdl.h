@@ -16,6 +16,7 @@
  *                         max-over-queries relevance
  *   fdl_kv_refresh        approximate KV cache: the rows of U(t) take new K/V (Prerequisites)
  *   fdl_block_means_refresh  (4) the means of the blocks a refresh touched
+ *   fdl_kv_refresh_means     both in one launch
  *   fdl_confidence_unmask    confidence of the masked positions, unmasking of n(t) of them
  *   fdl_dcu_select           per-layer cache update sets of the dynamic cache update (DCU)
  *   fdl_calibrate_read, fdl_calibrate_mfma   achievable read and MFMA rates (measurement)
@@ -338,6 +339,21 @@ fdl_status fdl_block_means_refresh(fdl_dtype dtype, int B, int Hkv, int L, int P
                                    const void* k, fdl_strides ks, int bs, const int32_t* rows,
                                    const int32_t* n_rows, int n_max, float* kbar,
                                    hipStream_t stream);
+
+/*
+ * fdl_kv_refresh_means - fdl_kv_refresh and fdl_block_means_refresh of the same rows in
+ * one launch, with the same results (Summary page, "Prerequisites" (approximate KV cache)
+ * and "Method steps" (4)).  The touched blocks' means take their refreshed rows from
+ * k_new and the other rows from k, so they need not wait for the scatter.
+ *   arguments as in fdl_kv_refresh, plus P, bs and kbar as in fdl_block_means_refresh;
+ *   rows distinct within a sequence (as the means read one new row per position).
+ * bs above 2048 is FDL_ERR_UNSUPPORTED; other errors as the two calls it replaces.
+ */
+fdl_status fdl_kv_refresh_means(fdl_dtype dtype, int B, int Hkv, int L, int P, int d, int bs,
+                                const int32_t* rows, const int32_t* n_rows, int n_max, const void* k_new,
+                                fdl_strides kns, const void* v_new, fdl_strides vns, void* k, fdl_strides ks,
+                                void* v, fdl_strides vs, void* vt, fdl_strides vts, float* kbar,
+                                hipStream_t stream);
 
 /*
  * fdl_confidence_unmask - the confidence of the masked positions and the unmasking of

@@ -8,5 +8,5 @@ from .fdl import (  # noqa: F401
     FdlError, Workspace, block_means, block_means_refresh, block_score_topc, calibrate_mfma, calibrate_read,
     confidence_unmask, dcu_select,
     dense_attention, focus_count, pcgi_select,
-    kv_refresh, sink_identify, sparse_attention, transpose_v,
+    kv_refresh, kv_refresh_means, sink_identify, sparse_attention, transpose_v,
 )

@@ -378,6 +378,37 @@ fdl_status fdl_block_means_refresh(fdl_dtype dt, int B, int Hkv, int L, int P, i
     return hip_status(launch_block_means_refresh(dt, a, stream));
 }
 
+fdl_status fdl_kv_refresh_means(fdl_dtype dt, int B, int Hkv, int L, int P, int d, int bs, const int32_t* rows,
+                                const int32_t* n_rows, int n_max, const void* k_new, fdl_strides kns,
+                                const void* v_new, fdl_strides vns, void* k, fdl_strides ks, void* v,
+                                fdl_strides vs, void* vt, fdl_strides vts, float* kbar, hipStream_t stream) {
+    fdl_status st = check_dtype_dims(dt, B, Hkv, Hkv, L, d);
+    if (st != FDL_OK) return st;
+    if (n_max < 0 || P < 1 || P > L || bs < 1) return FDL_ERR_SHAPE;
+    if (bs > kFusedMaxBs) return FDL_ERR_UNSUPPORTED;
+    if ((st = check_tensor(k, ks, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(v, vs, dt, d)) != FDL_OK) return st;
+    if ((st = check_vt(vt, vts, dt, d, L)) != FDL_OK) return st;
+    if (vt && (vts.r < L || vts.r >= (1ll << 31))) return FDL_ERR_SHAPE;
+    if (!kbar) return FDL_ERR_NULL;
+    if (!aligned16(kbar)) return FDL_ERR_ALIGN;
+    if (n_max == 0) return FDL_OK;
+    if (!rows) return FDL_ERR_NULL;
+    if ((st = check_tensor(k_new, kns, dt, d)) != FDL_OK) return st;
+    if ((st = check_tensor(v_new, vns, dt, d)) != FDL_OK) return st;
+    CacheArgs a{};
+    a.B = B; a.Hkv = Hkv; a.L = L; a.P = P; a.d = d; a.bs = bs; a.n_max = n_max;
+    a.nb = static_cast<int>((static_cast<int64_t>(P) + bs - 1) / bs);
+    a.rows = rows; a.n_rows = n_rows;
+    a.k_new = k_new; a.knb = kns.b; a.knh = kns.h; a.knr = kns.r;
+    a.v_new = v_new; a.vnb = vns.b; a.vnh = vns.h; a.vnr = vns.r;
+    a.k = k; a.ksb = ks.b; a.ksh = ks.h; a.ksr = ks.r;
+    a.v = v; a.vsb = vs.b; a.vsh = vs.h; a.vsr = vs.r;
+    a.vt = vt; a.vtsb = vts.b; a.vtsh = vts.h; a.vtsd = vts.r;
+    a.kbar = kbar;
+    return hip_status(launch_kv_refresh_means(dt, a, stream));
+}
+
 size_t fdl_confidence_unmask_workspace_bytes(int B, int V, int m_max) {
     if (B < 1 || V < 1 || m_max < 0 || m_max > kMaxConfRows) return 0;
     return confidence_workspace_bytes(B, V, m_max);

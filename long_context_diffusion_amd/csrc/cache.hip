@@ -33,15 +33,15 @@ constexpr int kScatterRows = 64;
 constexpr int kScatterThreads = 256;
 
 template <typename T>
-__global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const CacheArgs a) {
+__device__ __forceinline__ void kv_scatter_body(const CacheArgs& a, int chunk, int bg) {
     constexpr int kMaxPieces = kScatterRows * 128 * 4 / 16 / kScatterThreads;   // d <= 128, 4-byte T
     // staged V rows, row stride d + pad elements: the transposing reads (one d, 64 rows) then
     // fall on different banks (d = 128 bf16 rows, 256 bytes apart, would all hit one bank)
     constexpr int kPad = sizeof(T) == 2 ? 4 : 1;
     __shared__ __attribute__((aligned(16))) uint8_t tile[kScatterRows * (128 + kPad) * sizeof(T)];
     __shared__ int s_row[kScatterRows];
-    const int i0 = blockIdx.x * kScatterRows;
-    const int b = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
+    const int i0 = chunk * kScatterRows;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int n = min(a.n_rows ? a.n_rows[b] : a.n_max, a.n_max);
     if (i0 >= n) return;
     const int32_t* rows = a.rows + static_cast<int64_t>(b) * a.n_max;
@@ -124,8 +124,11 @@ __device__ __forceinline__ void unpack_piece<float>(const u32x4& x, float* out) 
 // loads, all of a thread's loads of the block in flight together (lane l takes piece l % NP
 // of rows l / NP, l / NP + RG, ...), summed in fp64, folded over the row groups with
 // shuffles and over the waves through LDS, and its mean rounded once.
-template <typename T, int D>
-__global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(const CacheArgs a) {
+// FROM_NEW: the refreshed rows of a block are read from k_new (the list entry that holds
+// them) and the other rows from the cache, so the means need not wait for the scatter
+// (the fused refresh runs both in one launch); otherwise every row comes from the cache.
+template <typename T, int D, bool FROM_NEW>
+__device__ __forceinline__ void means_refresh_body(const CacheArgs& a, int chunk, int bg) {
     constexpr int EPP = 16 / sizeof(T);          // elements per 16-byte piece
     constexpr int NP = D / EPP;                  // pieces per row
     constexpr int RG = kRefreshThreads / NP;     // rows read together by the workgroup
@@ -133,8 +136,8 @@ __global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(co
     constexpr int kWaves = kRefreshThreads / kWave;
     __shared__ double s_sum[kWaves][EPP][NP];
     __shared__ int s_blk[64];
-    const int i0 = blockIdx.x * 64;
-    const int b = blockIdx.y / a.Hkv, g = blockIdx.y % a.Hkv;
+    const int i0 = chunk * 64;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int n = min(a.n_rows ? a.n_rows[b] : a.n_max, a.n_max);
     if (i0 >= n) return;
     const int32_t* rows = a.rows + static_cast<int64_t>(b) * a.n_max;
@@ -159,10 +162,21 @@ __global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(co
     __syncthreads();
     const int piece = tid % NP, rg = tid / NP, wv = tid / kWave;
     const T* kbase = static_cast<const T*>(a.k) + b * a.ksb + g * a.ksh + piece * EPP;
+    const T* knbase = static_cast<const T*>(a.k_new) + b * a.knb + g * a.knh + piece * EPP;
+    __shared__ int s_src[FROM_NEW ? kFusedMaxBs : 1];   // row lo + j: list entry, or -1
     for (int e = 0; e < 64; ++e) {
         const int blk = s_blk[e];
         if (blk < 0) continue;   // the same for every thread
         const int lo = blk * a.bs, hi = min(lo + a.bs, a.P);
+        if constexpr (FROM_NEW) {
+            for (int j = tid; j < hi - lo; j += kRefreshThreads) s_src[j] = -1;
+            __syncthreads();
+            for (int i = tid; i < n; i += kRefreshThreads) {
+                const int r = rows[i];
+                if (r >= lo && r < hi) s_src[r - lo] = i;
+            }
+            __syncthreads();
+        }
         double acc[EPP];
 #pragma unroll
         for (int q = 0; q < EPP; ++q) acc[q] = 0.0;
@@ -171,7 +185,12 @@ __global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(co
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int j = min(j0 + u * RG, hi - 1);
-                x[u] = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(j) * a.ksr);
+                const T* src = kbase + static_cast<int64_t>(j) * a.ksr;
+                if constexpr (FROM_NEW) {
+                    const int si = s_src[j - lo];
+                    if (si >= 0) src = knbase + static_cast<int64_t>(si) * a.knr;
+                }
+                x[u] = *reinterpret_cast<const u32x4*>(src);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
@@ -205,7 +224,38 @@ __global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(co
     }
 }
 
+template <typename T>
+__global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const CacheArgs a) {
+    kv_scatter_body<T>(a, blockIdx.x, blockIdx.y);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kRefreshThreads) void block_means_refresh_kernel(const CacheArgs a) {
+    means_refresh_body<T, D, false>(a, blockIdx.x, blockIdx.y);
+}
+
+// Both in one launch: the first workgroups of each (sequence, KV head) scatter, the others
+// recompute the touched means from the cache and the new rows.
+template <typename T, int D>
+__global__ __launch_bounds__(kRefreshThreads) void kv_refresh_means_kernel(const CacheArgs a) {
+    static_assert(kScatterThreads == kRefreshThreads, "one workgroup size");
+    const int n_scatter = (a.n_max + kScatterRows - 1) / kScatterRows;
+    if (static_cast<int>(blockIdx.x) < n_scatter) kv_scatter_body<T>(a, blockIdx.x, blockIdx.y);
+    else means_refresh_body<T, D, true>(a, blockIdx.x - n_scatter, blockIdx.y);
+}
+
 }  // namespace
+
+hipError_t launch_kv_refresh_means(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream) {
+    if (a.n_max == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>((a.n_max + kScatterRows - 1) / kScatterRows + (a.n_max + 63) / 64),
+                    static_cast<unsigned>(a.B * a.Hkv));
+#define FDL_FUSED(T, DD) hipLaunchKernelGGL((kv_refresh_means_kernel<T, DD>), grid, dim3(kRefreshThreads), 0, stream, a)
+    if (dtype == FDL_BF16) { if (a.d == 128) FDL_FUSED(uint16_t, 128); else FDL_FUSED(uint16_t, 64); }
+    else { if (a.d == 128) FDL_FUSED(float, 128); else FDL_FUSED(float, 64); }
+#undef FDL_FUSED
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_scatter(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream) {
     if (a.n_max == 0) return hipSuccess;

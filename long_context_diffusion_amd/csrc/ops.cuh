@@ -70,6 +70,8 @@ struct CacheArgs {
     float* kbar;             // [B, Hkv, nb, d]
 };
 hipError_t launch_kv_scatter(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream);
+constexpr int kFusedMaxBs = 2048;   // largest block size of the fused refresh (LDS row map)
+hipError_t launch_kv_refresh_means(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream);
 hipError_t launch_block_means_refresh(fdl_dtype dtype, const CacheArgs& a, hipStream_t stream);
 hipError_t launch_block_score_topc(fdl_dtype dtype, int d, BlockArgs a, int C, int32_t* block_idx,
                                    double* R_out, void* ws, hipStream_t stream);

@@ -35,7 +35,7 @@ EXPORTS = (
     "fdl_confidence_unmask_workspace_bytes", "fdl_confidence_unmask",
     "fdl_dcu_select_workspace_bytes", "fdl_dcu_select",
     "fdl_block_score_topc_ex", "fdl_sparse_attention_ex_workspace_bytes", "fdl_sparse_attention_ex",
-    "fdl_calibrate_read", "fdl_calibrate_mfma",
+    "fdl_calibrate_read", "fdl_calibrate_mfma", "fdl_kv_refresh_means",
 )
 FDL_SCORE_PER_HEAD, FDL_SCORE_MAX = 1, 2
 
@@ -87,6 +87,8 @@ _SIGS = {
     "fdl_dcu_select": (_I, [_I, _I, _I, _I, _I, _P, Strides, _P, Strides, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
     "fdl_calibrate_read": (_I, [_P, _SZ, _P, _I, _P]),
+    "fdl_kv_refresh_means": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, Strides, _P, Strides, _P, Strides,
+                                  _P, Strides, _P, Strides, _P, _P]),
     "fdl_calibrate_mfma": (_I, [_I, _I, _F, _F, _P, _P]),
     "fdl_block_score_topc_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, Strides, _P, _P, _I, _P, Strides, _F,
                                           _I, _I, _P, _P, _P, _P]),
@@ -313,6 +315,25 @@ def kv_refresh(rows, k_new, v_new, k, v, *, n_rows=None, vt=None, stream=None):
                               _strides4(k_new), _ptr(v_new), _strides4(v_new), _ptr(k), _strides4(k), _ptr(v),
                               _strides4(v), vtp, vts, _stream(stream))
     _check(st, "fdl_kv_refresh")
+
+
+def kv_refresh_means(rows, k_new, v_new, k, v, P: int, bs: int, kbar, *, n_rows=None, vt=None, stream=None):
+    """kv_refresh and block_means_refresh of the same rows in one launch (fdl_kv_refresh_means)."""
+    B, Hkv, L, d = k.shape
+    n_max = rows.shape[1]
+    nb = -(-P // bs)
+    if rows.dtype != torch.int32 or not rows.is_contiguous():
+        raise FdlError(2, "rows must be a contiguous int32 [B, n_max] tensor")
+    if tuple(k_new.shape) != (B, Hkv, n_max, d) or tuple(v_new.shape) != (B, Hkv, n_max, d):
+        raise FdlError(2, "k_new, v_new must be [B, Hkv, n_max, d]")
+    if tuple(kbar.shape) != (B, Hkv, nb, d) or kbar.dtype != torch.float32 or not kbar.is_contiguous():
+        raise FdlError(2, "block means: expected a contiguous [B, Hkv, nb, d] fp32 kbar")
+    vtp, vts = _vt(vt, v)
+    st = lib().fdl_kv_refresh_means(_dtype_code(k), B, Hkv, L, P, d, int(bs), _ptr(rows), _ptr(n_rows), n_max,
+                                    _ptr(k_new), _strides4(k_new), _ptr(v_new), _strides4(v_new), _ptr(k),
+                                    _strides4(k), _ptr(v), _strides4(v), vtp, vts, _ptr(kbar), _stream(stream))
+    _check(st, "fdl_kv_refresh_means")
+    return kbar
 
 
 def block_means_refresh(k, P: int, bs: int, rows, kbar, *, n_rows=None, stream=None):

@@ -199,9 +199,12 @@ class StepRunner:
             vt = vts[l] if vts is not None else None
 
             def refresh():
-                F.kv_refresh(self.active, k_new[l], v_new[l], k, v, n_rows=self.n_active, vt=vt)
+                # a sparse layer refreshes its cache rows and its touched means in one launch
                 if l in self.kbar:
-                    F.block_means_refresh(k, self.P, self.bs, self.active, self.kbar[l], n_rows=self.n_active)
+                    F.kv_refresh_means(self.active, k_new[l], v_new[l], k, v, self.P, self.bs, self.kbar[l],
+                                       n_rows=self.n_active, vt=vt)
+                else:
+                    F.kv_refresh(self.active, k_new[l], v_new[l], k, v, n_rows=self.n_active, vt=vt)
             run("refresh", refresh)
             if self.is_dense(l):
                 run("dense", lambda: self.dense_layer(l, q, k, v, vt))

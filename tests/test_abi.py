@@ -332,3 +332,17 @@ def test_calibrate_validation():
     assert lib.fdl_calibrate_mfma(0, 10, 1.0, 1.0, out, NULL) == 2
     assert lib.fdl_calibrate_mfma(4, 0, 1.0, 1.0, out, NULL) == 2
     assert lib.fdl_calibrate_mfma(4, 10, 1.0, 1.0, NULL, NULL) == 1
+
+
+def test_kv_refresh_means_validation():
+    lib = F.lib()
+    st = S(32 * 4096 * 128, 4096 * 128, 128)
+    ns = S(32 * 64 * 128, 64 * 128, 128)
+    kb = ctypes.c_void_p(0x40000)
+    args = lambda P, bs, kbar: (F.FDL_BF16, 1, 32, 4096, P, 128, bs, FAKE, NULL, 64, FAKE, ns, FAKE, ns,
+                                FAKE, st, FAKE, st, NULL, S(0, 0, 0), kbar, NULL)
+    assert lib.fdl_kv_refresh_means(*args(4000, 4096, kb)) == 7     # block size above the fused bound
+    assert lib.fdl_kv_refresh_means(*args(4097, 64, kb)) == 2
+    assert lib.fdl_kv_refresh_means(*args(4000, 0, kb)) == 2
+    assert lib.fdl_kv_refresh_means(*args(4000, 64, NULL)) == 1
+    assert lib.fdl_kv_refresh_means(*args(4000, 64, MISALIGNED)) == 4

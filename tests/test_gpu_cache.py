@@ -197,3 +197,36 @@ def test_cached_step_graph_replays():
 
 def synth_f64(t):
     return f64(t)
+
+
+@pytest.mark.parametrize("dtype,d,with_vt,bs", [(torch.float32, 64, False, 16), (torch.bfloat16, 64, False, 100),
+                                                (torch.bfloat16, 128, True, 64), (torch.float32, 128, True, 128)])
+def test_fused_refresh_equals_two_calls(dtype, d, with_vt, bs):
+    """fdl_kv_refresh_means gives bit for bit the caches, V^T and means of fdl_kv_refresh
+    followed by fdl_block_means_refresh, for ascending and unordered row lists with -1
+    entries, rows inside and past the prompt, and ragged counts."""
+    print(f"fused refresh dtype={dtype} d={d} vt={with_vt} bs={bs}", flush=True)
+    B, Hkv, L, P = 2, 3, 520, 400
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7 * d + bs)
+    k, v = _rand(g, (B, Hkv, L, d), dtype), _rand(g, (B, Hkv, L, d), dtype)
+    rows = torch.tensor([[3, 4, 40, 47, 48, 199, 245, 399, 400, 519, 7, 8, 150, 151],
+                         [250, 0, 15, -1, 100, 303, 16, 17, 450, 9, 399, 398, 1, 2]], dtype=torch.int32, device=DEV)
+    n_rows = torch.tensor([10, 14], dtype=torch.int32, device=DEV)
+    n_max = rows.shape[1]
+    k_new, v_new = _rand(g, (B, Hkv, n_max, d), dtype), _rand(g, (B, Hkv, n_max, d), dtype)
+    kbar0 = F().block_means(k, P, bs)
+    k1, v1, kb1 = k.clone(), v.clone(), kbar0.clone()
+    vt1 = F().transpose_v(v1) if with_vt else None
+    F().kv_refresh(rows, k_new, v_new, k1, v1, n_rows=n_rows, vt=vt1)
+    F().block_means_refresh(k1, P, bs, rows, kb1, n_rows=n_rows)
+    k2, v2, kb2 = k.clone(), v.clone(), kbar0.clone()
+    vt2 = F().transpose_v(v2) if with_vt else None
+    F().kv_refresh_means(rows, k_new, v_new, k2, v2, P, bs, kb2, n_rows=n_rows, vt=vt2)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert torch.equal(kb1, kb2), "means"
+    if with_vt:
+        assert torch.equal(vt1, vt2)
+    # and both equal a full pass over the refreshed keys
+    assert torch.equal(kb2, F().block_means(k2, P, bs))
